@@ -1,0 +1,150 @@
+/*
+ * rlk_linear.h — C ABI of the fused, batch-invariant linear log-prob for
+ * MI355X (gfx950).
+ *
+ * The operator. Per token t, with hidden h_t (bf16, H values), the LM-head
+ * weight W (bf16, V_total rows of H) and a target id y_t, the logits are
+ * z_t = W h_t and the op returns
+ *     logp_t    = z_{t,y_t} - log sum_v exp(z_{t,v})
+ *     entropy_t = -sum_v p_{t,v} log p_{t,v},   p_t = softmax(z_t)   (nats)
+ * and, in the backward pass, the gradients of sum_t (dlogp_t logp_t +
+ * dentropy_t entropy_t) with respect to the hidden states and W. It is the
+ * linear-logp provider that stands in for VIME's
+ * calculate_log_probs_and_entropy (page "VIME Qwen3-8B TP4/CP2 200-round
+ * consistency experiment", section "User-facing operator matrix"), whose
+ * train-side and rollout-side log-probs must agree bit for bit (page
+ * "RL-Kernel evidence h100-cp-gradient.json",
+ * validation.train_rollout_logprob: require_exact, 0 bitwise mismatches).
+ *
+ * Bitwise contract. For a fixed build, every output row (logp, entropy,
+ * stats, and each row of dhidden) depends only on that row's hidden vector,
+ * its target, its upstream gradients and W: not on T, on the other rows, on
+ * the row's position in the batch, or on the repeat. dweight is a sum over
+ * rows and is only repeat-deterministic. Nothing uses atomics; every
+ * reduction runs in a fixed order set by V alone.
+ *
+ * Memory. All tensor pointers are device pointers owned by the caller,
+ * row-major, 16-byte aligned; inputs and outputs must not alias. The library
+ * allocates nothing: scratch memory is the caller's `workspace` (size from the
+ * *_workspace_bytes queries). It keeps no pointer after a call returns.
+ *
+ * Streams. `stream` is a hipStream_t (NULL = the null stream). Calls enqueue
+ * kernels and return without synchronising; device faults surface at the
+ * caller's next synchronisation.
+ *
+ * Errors. Every argument error is reported before anything is launched, by a
+ * status code (nothing is thrown across the ABI, nothing aborts). There is no
+ * fallback path of any kind: the op either runs the gfx950 kernels or returns
+ * an error.
+ *
+ * Vocabulary slices. A call may cover rows [vocab_start, vocab_start + V) of
+ * a vocabulary of vocab_total rows (one GPU's share of a tensor-parallel LM
+ * head; the pages' actor runs at TP=4). `weight` then points at the slice's
+ * first row. The forward returns the slice's partial statistics, which
+ * rlk_linear_logp_combine_host merges across slices; the backward takes the
+ * merged (whole-vocabulary) statistics.
+ */
+#ifndef RLK_LINEAR_H
+#define RLK_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLK_API __attribute__((visibility("default")))
+
+typedef enum rlk_status {
+  RLK_OK = 0,
+  RLK_ERR_INVALID_ARG = 1,         /* null/misaligned pointer, negative size, bad range, bad flag */
+  RLK_ERR_UNSUPPORTED_SHAPE = 2,   /* H not a positive multiple of 64, or a size beyond the limits */
+  RLK_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the matching *_workspace_bytes() */
+  RLK_ERR_UNSUPPORTED_DEVICE = 4,  /* the current device is not gfx950 */
+  RLK_ERR_HIP = 5                  /* a HIP runtime call failed (no device, launch failure) */
+} rlk_status;
+
+/* Per-row statistics record, 4 floats per row (row-major [T][4]):
+ *   m  = max_v z_{t,v} over the covered vocabulary,
+ *   R  = sum over the covered vocabulary, without one arg-max entry, of exp(z - m),
+ *   B  = sum over the covered vocabulary of exp(z - m) (z - m)   (<= 0),
+ *   zy = z_{t,y_t} if y_t is covered, else -inf.
+ * Over the whole vocabulary: logp = (zy - m) - log1p(R) and
+ * entropy = log1p(R) - B / (1 + R). */
+#define RLK_STATS_WIDTH 4
+
+/* bwd flags */
+#define RLK_DH_F32 1u /* dhidden is fp32 [T,H] (e.g. one slice's partial); default bf16 */
+
+/* Limits checked by every entry point. */
+#define RLK_MAX_T (1LL << 24)
+#define RLK_MAX_H 65536
+#define RLK_MAX_VOCAB ((1LL << 31) - 1)
+
+/* Bytes of device workspace the forward needs for (T, H, V). 0 when T == 0. */
+RLK_API size_t rlk_linear_logp_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V);
+
+/* Bytes of device workspace the backward needs for (T, H, V, flags, whether
+ * dhidden is requested). 0 when T == 0. */
+RLK_API size_t rlk_linear_logp_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V,
+                                                   uint32_t flags, int want_dhidden);
+
+/* Forward.
+ *   hidden   bf16 [T,H]
+ *   weight   bf16 [V,H], rows vocab_start .. vocab_start+V-1 of the LM head
+ *   targets  int32 [T], global ids; 0 <= y < vocab_total is a precondition
+ *            (a row that breaks it gets logp = NaN)
+ *   logp, entropy  fp32 [T] or NULL; must be NULL unless the call covers the
+ *            whole vocabulary (vocab_start == 0 and V == vocab_total)
+ *   stats    fp32 [T,4] or NULL: the record above for the covered vocabulary
+ *   workspace, workspace_bytes: >= rlk_linear_logp_fwd_workspace_bytes(T,H,V)
+ * T == 0 is a no-op. At least one of logp, entropy, stats must be non-NULL. */
+RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
+                                       const int32_t* targets, int64_t T, int64_t H, int64_t V,
+                                       int64_t vocab_start, int64_t vocab_total, float* logp,
+                                       float* entropy, float* stats, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Backward.
+ *   hidden, weight, targets, T, H, V, vocab_start, vocab_total: as in the forward
+ *   stats    fp32 [T,4] whole-vocabulary record (the forward's `stats` for a
+ *            full call, or the combined record for slices)
+ *   dlogp    fp32 [T] or NULL (= 0)
+ *   dentropy fp32 [T] or NULL (= 0)
+ *   dhidden  [T,H] bf16 (fp32 with RLK_DH_F32), or NULL to skip. For a slice it
+ *            is that slice's contribution sum_{v in slice} G[t,v] W[v,:].
+ *   dweight  fp32 [V,H], overwritten, or NULL to skip
+ *   flags    0 or RLK_DH_F32
+ *   workspace, workspace_bytes: >= rlk_linear_logp_bwd_workspace_bytes(
+ *            T, H, V, flags, dhidden != NULL)
+ * G[t,v] = dlogp_t ([v == y_t] - p_{t,v}) - dentropy_t p_{t,v} (log p_{t,v} + entropy_t).
+ * T == 0 with dweight != NULL writes zeros to dweight. */
+RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
+                                       const int32_t* targets, int64_t T, int64_t H, int64_t V,
+                                       int64_t vocab_start, int64_t vocab_total,
+                                       const float* stats, const float* dlogp,
+                                       const float* dentropy, void* dhidden, float* dweight,
+                                       uint32_t flags, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* Host-side merge of S slice records in the fixed order s = 0, 1, ..., S-1.
+ *   partials  host fp32 [S][T][4] (slice s's forward `stats`)
+ *   logp, entropy  host fp32 [T] or NULL
+ *   stats     host fp32 [T,4] or NULL: the merged whole-vocabulary record
+ * Runs on the CPU, touches no device. */
+RLK_API rlk_status rlk_linear_logp_combine_host(const float* partials, int64_t S, int64_t T,
+                                                float* logp, float* entropy, float* stats);
+
+/* Provenance. */
+RLK_API const char* rlk_status_string(int status);
+RLK_API const char* rlk_backend_id(void);
+/* Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host. */
+RLK_API uint64_t rlk_call_count(int which);
+RLK_API int rlk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_LINEAR_H */

@@ -1,0 +1,238 @@
+"""Python binding of the gfx950 fused, batch-invariant linear log-prob.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``librlk_linear.so`` behind the C ABI declared in
+``include/rlk_linear.h``. PyTorch supplies device memory and the stream.
+There is no fallback: if the library is missing or the device is not gfx950,
+calls raise.
+
+    logp, entropy = linear_logp(hidden, weight, targets)           # autograd-aware
+    out = fwd(hidden, weight, targets)                              # dict: logp, entropy, stats
+    dH, dW = bwd(hidden, weight, targets, out["stats"], dlogp)      # gradients
+    parts = fwd(hidden, W_slice, targets, vocab_start=a, vocab_total=V)["stats"]
+    logp, entropy, stats = combine_host([parts_0, parts_1, ...])    # fixed-order merge
+
+The operator is the linear-logp provider of the pages on RL-Kernel (page
+"VIME Qwen3-8B TP4/CP2 200-round consistency experiment", section
+"User-facing operator matrix": it stands in for VIME's
+calculate_log_probs_and_entropy): logp of the target token and entropy of the
+softmax of hidden @ W^T, with every row bitwise independent of the batch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librlk_linear.so")
+
+RLK_OK = 0
+RLK_DH_F32 = 1
+STATUS_NAMES = {0: "RLK_OK", 1: "RLK_ERR_INVALID_ARG", 2: "RLK_ERR_UNSUPPORTED_SHAPE",
+                3: "RLK_ERR_WORKSPACE_TOO_SMALL", 4: "RLK_ERR_UNSUPPORTED_DEVICE",
+                5: "RLK_ERR_HIP"}
+
+_lib = None
+
+
+class RlkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load_library(path: str | None = None):
+    """Load librlk_linear.so (built in-tree by ``_build.py``); raise if absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m rollout_rlk_linear_amd._build` "
+                           "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(p)
+    vp, i64, sz, f32p, i32p, u32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32)
+    lib.rlk_linear_logp_fwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.rlk_linear_logp_fwd_workspace_bytes.restype = sz
+    lib.rlk_linear_logp_bwd_workspace_bytes.argtypes = [i64, i64, i64, u32, ctypes.c_int]
+    lib.rlk_linear_logp_bwd_workspace_bytes.restype = sz
+    lib.rlk_linear_logp_fwd.argtypes = [vp, vp, i32p, i64, i64, i64, i64, i64, f32p, f32p, f32p,
+                                        vp, sz, vp]
+    lib.rlk_linear_logp_fwd.restype = ctypes.c_int
+    lib.rlk_linear_logp_bwd.argtypes = [vp, vp, i32p, i64, i64, i64, i64, i64, f32p, f32p, f32p,
+                                        vp, f32p, u32, vp, sz, vp]
+    lib.rlk_linear_logp_bwd.restype = ctypes.c_int
+    lib.rlk_linear_logp_combine_host.argtypes = [f32p, i64, i64, f32p, f32p, f32p]
+    lib.rlk_linear_logp_combine_host.restype = ctypes.c_int
+    lib.rlk_status_string.argtypes = [ctypes.c_int]
+    lib.rlk_status_string.restype = ctypes.c_char_p
+    lib.rlk_backend_id.argtypes = []
+    lib.rlk_backend_id.restype = ctypes.c_char_p
+    lib.rlk_call_count.argtypes = [ctypes.c_int]
+    lib.rlk_call_count.restype = ctypes.c_uint64
+    lib.rlk_abi_version.argtypes = []
+    lib.rlk_abi_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != RLK_OK:
+        lib = load_library()
+        raise RlkError(status, lib.rlk_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def backend_id() -> str:
+    return load_library().rlk_backend_id().decode()
+
+
+def call_count(which: int) -> int:
+    return int(load_library().rlk_call_count(which))
+
+
+def fwd_workspace_bytes(T: int, H: int, V: int) -> int:
+    return int(load_library().rlk_linear_logp_fwd_workspace_bytes(T, H, V))
+
+
+def bwd_workspace_bytes(T: int, H: int, V: int, flags: int = 0, want_dhidden: bool = True) -> int:
+    return int(load_library().rlk_linear_logp_bwd_workspace_bytes(T, H, V, flags, int(want_dhidden)))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _check_inputs(hidden, weight, targets):
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if targets.dtype != torch.int32:
+        raise TypeError("targets must be int32")
+    for name, t in (("hidden", hidden), ("weight", weight), ("targets", targets)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def fwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, *,
+        vocab_start: int = 0, vocab_total: int | None = None, want_logp: bool = True,
+        want_entropy: bool = True, want_stats: bool = True, out: dict | None = None):
+    """Forward through ``rlk_linear_logp_fwd``. Returns dict(logp, entropy, stats).
+
+    For a vocabulary slice (``vocab_start``/``vocab_total``) only ``stats`` is
+    produced: the slice's (m, R, B, zy) record per row, fp32 [T, 4].
+    """
+    lib = load_library()
+    _check_inputs(hidden, weight, targets)
+    T, H = hidden.shape
+    V = weight.shape[0]
+    vt = V if vocab_total is None else vocab_total
+    full = vocab_start == 0 and V == vt
+    dev = hidden.device
+    out = {} if out is None else out
+    logp = out.get("logp") if full and want_logp else None
+    ent = out.get("entropy") if full and want_entropy else None
+    stats = out.get("stats") if want_stats or not full else None
+    if full and want_logp and logp is None:
+        logp = torch.empty(T, dtype=torch.float32, device=dev)
+    if full and want_entropy and ent is None:
+        ent = torch.empty(T, dtype=torch.float32, device=dev)
+    if (want_stats or not full) and stats is None:
+        stats = torch.empty(T, 4, dtype=torch.float32, device=dev)
+    nws = lib.rlk_linear_logp_fwd_workspace_bytes(T, H, V)
+    ws = out.get("_ws_fwd")
+    if ws is None or ws.numel() < nws:
+        ws = _workspace(nws, dev)
+    _check(lib.rlk_linear_logp_fwd(_ptr(hidden), _ptr(weight), _ptr(targets), T, H, V,
+                                   vocab_start, vt, _ptr(logp), _ptr(ent), _ptr(stats),
+                                   _ptr(ws), ws.numel(), _stream(dev)))
+    return {"logp": logp, "entropy": ent, "stats": stats}
+
+
+def bwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor,
+        dlogp: torch.Tensor | None, dentropy: torch.Tensor | None = None, *,
+        vocab_start: int = 0, vocab_total: int | None = None, want_dhidden: bool = True,
+        want_dweight: bool = True, dhidden_f32: bool = False, out: dict | None = None):
+    """Backward through ``rlk_linear_logp_bwd``. Returns (dhidden, dweight).
+
+    ``stats`` is the whole-vocabulary record (fwd's ``stats`` or the combined
+    one for slices). dhidden is bf16 [T,H] (fp32 with ``dhidden_f32``),
+    dweight fp32 [V,H].
+    """
+    lib = load_library()
+    _check_inputs(hidden, weight, targets)
+    T, H = hidden.shape
+    V = weight.shape[0]
+    vt = V if vocab_total is None else vocab_total
+    dev = hidden.device
+    out = {} if out is None else out
+    for name, t in (("stats", stats), ("dlogp", dlogp), ("dentropy", dentropy)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor")
+    flags = RLK_DH_F32 if dhidden_f32 else 0
+    dh = out.get("dhidden") if want_dhidden else None
+    dw = out.get("dweight") if want_dweight else None
+    if want_dhidden and dh is None:
+        dh = torch.empty(T, H, dtype=torch.float32 if dhidden_f32 else torch.bfloat16, device=dev)
+    if want_dweight and dw is None:
+        dw = torch.empty(V, H, dtype=torch.float32, device=dev)
+    nws = lib.rlk_linear_logp_bwd_workspace_bytes(T, H, V, flags, int(want_dhidden))
+    ws = out.get("_ws_bwd")
+    if ws is None or ws.numel() < nws:
+        ws = _workspace(nws, dev)
+    _check(lib.rlk_linear_logp_bwd(_ptr(hidden), _ptr(weight), _ptr(targets), T, H, V,
+                                   vocab_start, vt, _ptr(stats), _ptr(dlogp), _ptr(dentropy),
+                                   _ptr(dh), _ptr(dw), flags, _ptr(ws), ws.numel(), _stream(dev)))
+    return dh, dw
+
+
+def combine_host(partials):
+    """Merge per-slice stats (list of [T,4] fp32, CPU or device) in list order.
+
+    Runs ``rlk_linear_logp_combine_host`` on the CPU. Returns (logp, entropy,
+    stats) as CPU fp32 tensors.
+    """
+    lib = load_library()
+    parts = torch.stack([p.detach().to("cpu", torch.float32) for p in partials]).contiguous()
+    S, T = parts.shape[0], parts.shape[1]
+    logp = torch.empty(T, dtype=torch.float32)
+    ent = torch.empty(T, dtype=torch.float32)
+    stats = torch.empty(T, 4, dtype=torch.float32)
+    _check(lib.rlk_linear_logp_combine_host(_ptr(parts), S, T, _ptr(logp), _ptr(ent), _ptr(stats)))
+    return logp, ent, stats
+
+
+class LinearLogp(torch.autograd.Function):
+    """Autograd wrapper: forward (logp, entropy); backward (dhidden, dweight)."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, targets):
+        o = fwd(hidden, weight, targets)
+        ctx.save_for_backward(hidden, weight, targets, o["stats"])
+        ctx.mark_non_differentiable(o["stats"])
+        return o["logp"], o["entropy"]
+
+    @staticmethod
+    def backward(ctx, dlogp, dentropy):
+        hidden, weight, targets, stats = ctx.saved_tensors
+        dl = None if dlogp is None else dlogp.float().contiguous()
+        de = None if dentropy is None else dentropy.float().contiguous()
+        dh, dw = bwd(hidden, weight, targets, stats, dl, de,
+                     want_dhidden=ctx.needs_input_grad[0], want_dweight=ctx.needs_input_grad[1])
+        return dh, (None if dw is None else dw.to(weight.dtype)), None
+
+
+def linear_logp(hidden, weight, targets):
+    """(logp, entropy) per token; differentiable in hidden and weight."""
+    return LinearLogp.apply(hidden, weight, targets)

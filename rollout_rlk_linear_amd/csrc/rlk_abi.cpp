@@ -1,0 +1,266 @@
+// rlk_abi.cpp — the C ABI of the linear log-prob library: argument checks,
+// workspace planning, device check, launch sequencing, host-side combine and
+// provenance. Every argument error is returned before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "rlk_internal.h"
+#include "../../include/rlk_linear.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+const char kBackendId[] = "rlk.linear_logp.bitwise.gfx950.v1";
+
+std::atomic<uint64_t> g_calls[3];
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by fwd and bwd.
+rlk_status check_shape(int64_t T, int64_t H, int64_t V, int64_t vocab_start, int64_t vocab_total) {
+  if (T < 0 || H <= 0 || V <= 0 || vocab_start < 0 || vocab_total <= 0) return RLK_ERR_INVALID_ARG;
+  if (vocab_total > RLK_MAX_VOCAB || V > vocab_total || vocab_start > vocab_total - V)
+    return RLK_ERR_INVALID_ARG;
+  if (T > RLK_MAX_T || H > RLK_MAX_H || (H % 64) != 0) return RLK_ERR_UNSUPPORTED_SHAPE;
+  return RLK_OK;
+}
+
+// The kernels are built for gfx950 only; refuse anything else.
+rlk_status check_device() {
+  static std::atomic<int> cache[256];  // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return RLK_ERR_HIP;
+  if (dev < 256) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 1) return RLK_OK;
+    if (c == 2) return RLK_ERR_UNSUPPORTED_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return RLK_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 256) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? RLK_OK : RLK_ERR_UNSUPPORTED_DEVICE;
+}
+
+}  // namespace
+
+namespace rlk {
+
+size_t fwd_workspace(int64_t T, int64_t H, int64_t V) {
+  (void)H;
+  if (T <= 0) return 0;
+  const int64_t G = ceil_div(V, 256);
+  return align256(size_t(T) * size_t(G) * 16);
+}
+
+BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh) {
+  BwdPlan p{};
+  const int64_t Vp = round_up(V, 256);
+  int64_t S = V / kSplitCols;
+  if (S < 1) S = 1;
+  if (S > kMaxSplits) S = kMaxSplits;
+  p.split_w = (int)round_up(ceil_div(Vp, S), 256);
+  p.nsplits = (int)ceil_div(Vp, p.split_w);
+  p.Tp = round_up(T > 0 ? T : 1, 64);
+  int64_t spc = kChunkElems / (p.Tp * p.split_w);
+  if (spc < 1) spc = 1;
+  if (spc > p.nsplits) spc = p.nsplits;
+  p.splits_per_chunk = (int)spc;
+  p.nchunks = (int)ceil_div(p.nsplits, spc);
+  p.ldg = spc * p.split_w;
+  p.off_rowc = 0;
+  p.off_gtv = align256(size_t(p.Tp) * 32);
+  p.off_part = align256(p.off_gtv + size_t(p.Tp) * size_t(p.ldg) * 2);
+  p.total = align256(p.off_part + (want_dh ? size_t(p.nsplits) * size_t(T) * size_t(H) * 4 : 0));
+  return p;
+}
+
+}  // namespace rlk
+
+extern "C" {
+
+RLK_API size_t rlk_linear_logp_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V) {
+  if (T <= 0 || H <= 0 || V <= 0) return 0;
+  return rlk::fwd_workspace(T, H, V);
+}
+
+RLK_API size_t rlk_linear_logp_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V,
+                                                   uint32_t flags, int want_dhidden) {
+  (void)flags;
+  if (T <= 0 || H <= 0 || V <= 0) return 0;
+  return rlk::bwd_plan(T, H, V, want_dhidden != 0).total;
+}
+
+RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
+                                       const int32_t* targets, int64_t T, int64_t H, int64_t V,
+                                       int64_t vocab_start, int64_t vocab_total, float* logp,
+                                       float* entropy, float* stats, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  rlk_status s = check_shape(T, H, V, vocab_start, vocab_total);
+  if (s != RLK_OK) return s;
+  const bool full = vocab_start == 0 && V == vocab_total;
+  if (!full && (logp || entropy)) return RLK_ERR_INVALID_ARG;
+  if (!logp && !entropy && !stats) return RLK_ERR_INVALID_ARG;
+  if (!weight || !aligned(weight, 16)) return RLK_ERR_INVALID_ARG;
+  if (T == 0) {
+    g_calls[0].fetch_add(1, std::memory_order_relaxed);
+    return RLK_OK;
+  }
+  if (!hidden || !aligned(hidden, 16) || !targets || !aligned(targets, 4)) return RLK_ERR_INVALID_ARG;
+  if ((logp && !aligned(logp, 4)) || (entropy && !aligned(entropy, 4)) ||
+      (stats && !aligned(stats, 16)))
+    return RLK_ERR_INVALID_ARG;
+  const size_t need = rlk::fwd_workspace(T, H, V);
+  if (workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 16)) return RLK_ERR_INVALID_ARG;
+  s = check_device();
+  if (s != RLK_OK) return s;
+
+  rlk::FwdArgs a{};
+  a.hidden = static_cast<const uint16_t*>(hidden);
+  a.weight = static_cast<const uint16_t*>(weight);
+  a.targets = targets;
+  a.T = (int)T;
+  a.H = (int)H;
+  a.V = (int)V;
+  a.vocab_start = vocab_start;
+  a.vocab_total = vocab_total;
+  a.full = full ? 1 : 0;
+  a.logp = logp;
+  a.entropy = entropy;
+  a.stats = reinterpret_cast<float4*>(stats);
+  a.part = static_cast<float4*>(workspace);
+  if (rlk::launch_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RLK_ERR_HIP;
+  g_calls[0].fetch_add(1, std::memory_order_relaxed);
+  return RLK_OK;
+}
+
+RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
+                                       const int32_t* targets, int64_t T, int64_t H, int64_t V,
+                                       int64_t vocab_start, int64_t vocab_total,
+                                       const float* stats, const float* dlogp,
+                                       const float* dentropy, void* dhidden, float* dweight,
+                                       uint32_t flags, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  rlk_status s = check_shape(T, H, V, vocab_start, vocab_total);
+  if (s != RLK_OK) return s;
+  if (flags & ~uint32_t(RLK_DH_F32)) return RLK_ERR_INVALID_ARG;
+  if (!weight || !aligned(weight, 16)) return RLK_ERR_INVALID_ARG;
+  if (!dhidden && !dweight) return RLK_ERR_INVALID_ARG;
+  if (dweight && !aligned(dweight, 16)) return RLK_ERR_INVALID_ARG;
+  if (T == 0) {
+    if (dweight) {
+      s = check_device();
+      if (s != RLK_OK) return s;
+      if (rlk::launch_fill_zero(dweight, V * H, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return RLK_ERR_HIP;
+    }
+    g_calls[1].fetch_add(1, std::memory_order_relaxed);
+    return RLK_OK;
+  }
+  if (!hidden || !aligned(hidden, 16) || !targets || !aligned(targets, 4)) return RLK_ERR_INVALID_ARG;
+  if (!stats || !aligned(stats, 16)) return RLK_ERR_INVALID_ARG;
+  if ((dlogp && !aligned(dlogp, 4)) || (dentropy && !aligned(dentropy, 4)))
+    return RLK_ERR_INVALID_ARG;
+  if (dhidden && !aligned(dhidden, 16)) return RLK_ERR_INVALID_ARG;
+  const rlk::BwdPlan plan = rlk::bwd_plan(T, H, V, dhidden != nullptr);
+  if (workspace_bytes < plan.total) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 256)) return RLK_ERR_INVALID_ARG;
+  s = check_device();
+  if (s != RLK_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  rlk::BwdArgs a{};
+  a.hidden = static_cast<const uint16_t*>(hidden);
+  a.weight = static_cast<const uint16_t*>(weight);
+  a.targets = targets;
+  a.T = (int)T;
+  a.H = (int)H;
+  a.V = (int)V;
+  a.vocab_start = vocab_start;
+  a.vocab_total = vocab_total;
+  a.stats = reinterpret_cast<const float4*>(stats);
+  a.dlogp = dlogp;
+  a.dentropy = dentropy;
+  a.dhidden = dhidden;
+  a.dh_f32 = (flags & RLK_DH_F32) ? 1 : 0;
+  a.dweight = dweight;
+  a.rowc = reinterpret_cast<float4*>(ws + plan.off_rowc);
+  a.gtv = reinterpret_cast<uint16_t*>(ws + plan.off_gtv);
+  a.part = reinterpret_cast<float*>(ws + plan.off_part);
+  if (rlk::launch_bwd(a, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return RLK_ERR_HIP;
+  g_calls[1].fetch_add(1, std::memory_order_relaxed);
+  return RLK_OK;
+}
+
+// Host merge of slice records, s = 0, 1, ..., S-1 left to right, with the
+// same algebra as the device: the larger max is the base (the left one on a
+// tie), d = m_other - m_base, R = R_b + e^d (1 + R_o),
+// B = B_b + e^d (B_o + (1 + R_o) d), zy = max(zy_1, zy_2).
+RLK_API rlk_status rlk_linear_logp_combine_host(const float* partials, int64_t S, int64_t T,
+                                                float* logp, float* entropy, float* stats) {
+  if (S < 1 || T < 0) return RLK_ERR_INVALID_ARG;
+  if (T > 0 && !partials) return RLK_ERR_INVALID_ARG;
+  for (int64_t t = 0; t < T; ++t) {
+    float m = partials[t * 4 + 0], R = partials[t * 4 + 1], B = partials[t * 4 + 2],
+          zy = partials[t * 4 + 3];
+    for (int64_t s = 1; s < S; ++s) {
+      const float* q = partials + (s * T + t) * 4;
+      const bool left_base = !(q[0] > m);
+      const float mb = left_base ? m : q[0], Rb = left_base ? R : q[1], Bb = left_base ? B : q[2];
+      const float mo = left_base ? q[0] : m, Ro = left_base ? q[1] : R, Bo = left_base ? q[2] : B;
+      zy = std::fmax(zy, q[3]);
+      m = mb;
+      if (mo == -INFINITY) {
+        R = Rb;
+        B = Bb;
+        continue;
+      }
+      const float d = mo - mb;
+      const float e = std::exp(d);
+      const float one_r = 1.f + Ro;
+      R = Rb + e * one_r;
+      B = Bb + e * (Bo + one_r * d);
+    }
+    const float L = std::log1p(R);
+    if (stats) {
+      stats[t * 4 + 0] = m;
+      stats[t * 4 + 1] = R;
+      stats[t * 4 + 2] = B;
+      stats[t * 4 + 3] = zy;
+    }
+    if (logp) logp[t] = (zy - m) - L;
+    if (entropy) entropy[t] = L - B / (1.f + R);
+  }
+  g_calls[2].fetch_add(1, std::memory_order_relaxed);
+  return RLK_OK;
+}
+
+RLK_API const char* rlk_status_string(int status) {
+  switch (status) {
+    case RLK_OK: return "ok";
+    case RLK_ERR_INVALID_ARG: return "invalid argument";
+    case RLK_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (H must be a positive multiple of 64 within the limits)";
+    case RLK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RLK_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case RLK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+RLK_API const char* rlk_backend_id(void) { return kBackendId; }
+
+RLK_API uint64_t rlk_call_count(int which) {
+  if (which < 0 || which > 2) return 0;
+  return g_calls[which].load(std::memory_order_relaxed);
+}
+
+RLK_API int rlk_abi_version(void) { return kAbiVersion; }
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// rlk_internal.h — host-side plan and launcher interface between the C ABI
+// (rlk_abi.cpp) and the kernels (rlk_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rlk {
+
+// Batches of at most this many rows use 32-row tiles, larger ones 256-row
+// tiles. Both instantiate the same per-element arithmetic and reduction
+// order, so a row's bits do not depend on which one ran.
+constexpr int kSmallT = 64;
+
+// dH is reduced over fixed vocabulary splits: at most kMaxSplits of them,
+// about one per kSplitCols columns, each a multiple of 256 columns. They
+// depend on V only.
+constexpr int kMaxSplits = 8;
+constexpr int kSplitCols = 16384;
+// Soft bound on the elements of one bf16 logit-gradient chunk (T x columns).
+constexpr int64_t kChunkElems = int64_t(1) << 27;
+
+struct FwdArgs {
+  const uint16_t* hidden;
+  const uint16_t* weight;
+  const int32_t* targets;
+  int T, H, V;
+  int64_t vocab_start, vocab_total;
+  int full;
+  float* logp;
+  float* entropy;
+  float4* stats;
+  float4* part;  // workspace [T][G]
+};
+
+struct BwdPlan {
+  int nsplits;          // splits of the (call-local) vocabulary
+  int split_w;          // columns per split (multiple of 256)
+  int splits_per_chunk;
+  int nchunks;
+  int64_t ldg;          // row stride of the G chunk buffer (columns)
+  int64_t Tp;           // rows reserved for rowc (T rounded up)
+  size_t off_rowc, off_gtv, off_part, total;
+};
+
+struct BwdArgs {
+  const uint16_t* hidden;
+  const uint16_t* weight;
+  const int32_t* targets;
+  int T, H, V;
+  int64_t vocab_start, vocab_total;
+  const float4* stats;
+  const float* dlogp;
+  const float* dentropy;
+  void* dhidden;
+  int dh_f32;
+  float* dweight;
+  float4* rowc;
+  uint16_t* gtv;
+  float* part;
+};
+
+size_t fwd_workspace(int64_t T, int64_t H, int64_t V);
+BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh);
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+}  // namespace rlk

@@ -1,0 +1,182 @@
+"""The C-ABI library on the host (no GPU needed).
+
+* it loads and exports every symbol that include/rlk_linear.h declares;
+* every argument error is returned as its status code before any HIP call
+  (fake device pointers are never dereferenced on the host);
+* workspace queries follow the documented sizes;
+* the host-side slice combine agrees with the float64 oracle.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import rollout_rlk_linear_amd as rlk
+from oracle import finalize_partials, forward_f64, merge_partials, slice_partials_f64
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlk_linear.h")
+
+OK, INVALID, SHAPE, WS_SMALL, DEVICE, HIPERR = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p(1 << 20)  # aligned fake device pointer, never dereferenced on the host
+NULL = None
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"RLK_API\s+[\w\s\*]+?\b(rlk_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for n in ["rlk_linear_logp_fwd", "rlk_linear_logp_bwd", "rlk_linear_logp_fwd_workspace_bytes",
+              "rlk_linear_logp_bwd_workspace_bytes", "rlk_linear_logp_combine_host",
+              "rlk_status_string", "rlk_backend_id", "rlk_call_count", "rlk_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(rlk.LIB_PATH)
+    for n in declared_symbols():
+        assert hasattr(raw, n), n
+
+
+def test_provenance(lib):
+    assert lib.rlk_backend_id().decode() == "rlk.linear_logp.bitwise.gfx950.v1"
+    assert lib.rlk_abi_version() == 1
+    for s in range(6):
+        assert lib.rlk_status_string(s)
+    assert lib.rlk_status_string(99).decode() == "unknown status"
+    assert lib.rlk_call_count(7) == 0
+
+
+def fwd(lib, hidden=P, weight=P, targets=P, T=4, H=64, V=100, vs=0, vt=None, logp=P, ent=P,
+        stats=P, ws=P, nws=1 << 30):
+    vt = V if vt is None else vt
+    return lib.rlk_linear_logp_fwd(hidden, weight, targets, T, H, V, vs, vt, logp, ent, stats, ws,
+                                   nws, NULL)
+
+
+def bwd(lib, hidden=P, weight=P, targets=P, T=4, H=64, V=100, vs=0, vt=None, stats=P, dl=P,
+        de=NULL, dh=P, dw=P, flags=0, ws=P, nws=1 << 34):
+    vt = V if vt is None else vt
+    return lib.rlk_linear_logp_bwd(hidden, weight, targets, T, H, V, vs, vt, stats, dl, de, dh, dw,
+                                   flags, ws, nws, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(H=0), INVALID), (dict(V=0), INVALID),
+    (dict(H=96), SHAPE), (dict(H=65536 + 64), SHAPE), (dict(T=(1 << 24) + 1), SHAPE),
+    (dict(vs=-1), INVALID), (dict(vt=50), INVALID), (dict(vs=10, vt=105), INVALID),
+    (dict(vt=(1 << 31)), INVALID),
+    (dict(vs=5, vt=200, stats=P), INVALID),              # slice with logp/entropy requested
+    (dict(logp=NULL, ent=NULL, stats=NULL), INVALID),    # nothing requested
+    (dict(weight=NULL), INVALID), (dict(hidden=NULL), INVALID), (dict(targets=NULL), INVALID),
+    (dict(hidden=ctypes.c_void_p((1 << 20) + 2)), INVALID),   # misaligned
+    (dict(stats=ctypes.c_void_p((1 << 20) + 4)), INVALID),
+    (dict(nws=0), WS_SMALL), (dict(ws=NULL), INVALID),
+])
+def test_fwd_argument_errors(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_fwd_slice_without_logp_passes_checks(lib):
+    # a valid slice call gets past every argument check to the device check
+    st = fwd(lib, vs=5, vt=200, logp=NULL, ent=NULL)
+    assert st in (HIPERR, DEVICE) if not torch.cuda.is_available() else True
+
+
+def test_fwd_T0_is_noop(lib):
+    before = lib.rlk_call_count(0)
+    assert fwd(lib, T=0, hidden=NULL, targets=NULL, ws=NULL, nws=0) == OK
+    assert lib.rlk_call_count(0) == before + 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(H=100), SHAPE), (dict(vs=1), INVALID),
+    (dict(flags=2), INVALID), (dict(dh=NULL, dw=NULL), INVALID), (dict(stats=NULL), INVALID),
+    (dict(hidden=NULL), INVALID), (dict(weight=NULL), INVALID),
+    (dict(dh=ctypes.c_void_p((1 << 20) + 8)), INVALID),
+    (dict(dw=ctypes.c_void_p((1 << 20) + 4)), INVALID),
+    (dict(dl=ctypes.c_void_p((1 << 20) + 2)), INVALID),
+    (dict(nws=1024), WS_SMALL), (dict(ws=ctypes.c_void_p((1 << 20) + 16)), INVALID),
+])
+def test_bwd_argument_errors(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check of the no-device path")
+def test_valid_call_without_device_reports_hip_error(lib):
+    assert fwd(lib) in (HIPERR, DEVICE)
+    assert bwd(lib) in (HIPERR, DEVICE)
+
+
+def test_bwd_T0_without_dweight_is_noop(lib):
+    assert bwd(lib, T=0, hidden=NULL, targets=NULL, stats=NULL, dw=NULL, ws=NULL, nws=0) == OK
+
+
+def test_workspace_sizes(lib):
+    f = lib.rlk_linear_logp_fwd_workspace_bytes
+    assert f(0, 4096, 151936) == 0
+    # one 16-byte record per (row, group of 256 columns), rounded to 256 B
+    assert f(512, 4096, 151936) == 512 * 594 * 16
+    assert f(3, 256, 1024) == 256
+    b = lib.rlk_linear_logp_bwd_workspace_bytes
+    sizes = [b(T, 4096, 151936, 0, 1) for T in (1, 4, 64, 512, 5208)]
+    assert all(x < y for x, y in zip(sizes, sizes[1:]))
+    assert b(512, 4096, 151936, 0, 0) < b(512, 4096, 151936, 0, 1)
+    assert b(0, 4096, 151936, 0, 1) == 0
+
+
+# --------------------------------------------------------- host combine
+
+def test_combine_host_matches_oracle():
+    r = np.random.default_rng(5)
+    T, H, V = 40, 16, 300
+    h = r.standard_normal((T, H))
+    W = r.standard_normal((V, H)) * 2.5   # peaky rows: small entropies
+    y = r.integers(0, V, T)
+    bounds = [0, 75, 150, 225, 300]
+    parts = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        m, R, B, zy = slice_partials_f64(h, W[a:b], y, a)
+        parts.append(torch.tensor(np.stack([m, R, B, zy], axis=1), dtype=torch.float32))
+    logp, ent, stats = rlk.combine_host(parts)
+    full = forward_f64(h, W, y)
+    assert np.abs(logp.numpy() - full["logp"]).max() <= 1e-5 * max(1, np.abs(full["logp"]).max())
+    rel = np.abs(ent.numpy() - full["entropy"]) / np.maximum(np.abs(full["entropy"]), 1e-30)
+    assert rel.max() <= 1e-4
+    # the merged record finalises like the oracle's own merge
+    acc = [p.double().numpy().T for p in parts]
+    o = acc[0]
+    for q in acc[1:]:
+        o = merge_partials(o, q)
+    fin = finalize_partials(o)
+    np.testing.assert_allclose(stats.numpy()[:, 0], o[0], rtol=1e-6)
+    np.testing.assert_allclose(logp.numpy(), fin["logp"], rtol=1e-5, atol=1e-5)
+
+
+def test_combine_host_argument_errors(lib):
+    assert lib.rlk_linear_logp_combine_host(P, 0, 4, NULL, NULL, NULL) == INVALID
+    assert lib.rlk_linear_logp_combine_host(NULL, 2, 4, NULL, NULL, NULL) == INVALID
+    assert lib.rlk_linear_logp_combine_host(NULL, 2, 0, NULL, NULL, NULL) == OK
+
+
+def test_combine_host_empty_slice_and_missing_target():
+    # slice 1 holds the target; a slice record with m = -inf (nothing) is neutral
+    p0 = torch.tensor([[2.0, 0.5, -0.3, -math.inf]])
+    p1 = torch.tensor([[3.0, 0.0, 0.0, 3.0]])
+    logp, ent, st = rlk.combine_host([p0, p1])
+    # by hand: base = p1 (larger max), d = -1, R = 0 + e^-1 (1.5), B = 0 + e^-1 (-0.3 + 1.5 * -1)
+    e = math.exp(-1.0)
+    R = e * 1.5
+    B = e * (-0.3 - 1.5)
+    assert math.isclose(st[0, 1].item(), R, rel_tol=1e-6)
+    assert math.isclose(st[0, 2].item(), B, rel_tol=1e-6)
+    assert math.isclose(logp[0].item(), -math.log1p(R), rel_tol=1e-6)
+    assert math.isclose(ent[0].item(), math.log1p(R) - B / (1 + R), rel_tol=1e-6)

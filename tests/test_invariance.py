@@ -1,0 +1,124 @@
+"""GPU bitwise batch invariance (no oracle applies: the GPU against itself).
+
+The pages' acceptance form for the linear-logp route is zero bitwise
+mismatches and max |diff| = 0 between the trainer's large packed batches and
+the rollout engine's CUDA-graph batches of 1 to 4 ("RL-Kernel evidence
+h100-cp-gradient.json", validation.train_rollout_logprob and
+validation.cuda_graph.expected_capture_sizes). Here a fixed pool of 64
+Qwen3-8B-shaped rows (H = 4096, V = 151936) is scored in batches of 1, 2, 3,
+4 and 64, under 3 row permutations, embedded in a batch of 512 other rows,
+and repeated; every row's logp, entropy and statistics record must be
+bit-identical across all of them. The same holds for each row of dhidden.
+"""
+
+import pytest
+import torch
+
+import rollout_rlk_linear_amd as rlk
+import workloads as wl
+from tests._util import bits_equal, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    W = dev(wl.qwen512().weight)
+    pool = wl.pool64()
+    _, _, dlogp = wl.qwen_rows(64, 2)
+    return {"W": W, "h": dev(pool["hidden"]), "y": dev(pool["targets"]), "dlogp": dev(dlogp),
+            "pool": pool}
+
+
+def score(W, h, y):
+    o = rlk.fwd(h, W, y)
+    return torch.stack([o["logp"], o["entropy"]], dim=1), o["stats"]
+
+
+def batched(W, h, y, bs):
+    outs, stats = [], []
+    for r0 in range(0, h.shape[0], bs):
+        a, s = score(W, h[r0:r0 + bs].contiguous(), y[r0:r0 + bs].contiguous())
+        outs.append(a)
+        stats.append(s)
+    return torch.cat(outs), torch.cat(stats)
+
+
+def mismatch(a, b):
+    return int((a.contiguous().view(torch.int32) != b.contiguous().view(torch.int32)).sum())
+
+
+def test_batch_sizes_bitwise(setup):
+    W, h, y = setup["W"], setup["h"], setup["y"]
+    ref, ref_st = score(W, h, y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref).all()
+    for bs in (1, 2, 3, 4, 64):
+        for rep in range(3):
+            got, st = batched(W, h, y, bs)
+            torch.cuda.synchronize()
+            assert mismatch(got, ref) == 0, f"batch {bs} repeat {rep}"
+            assert mismatch(st, ref_st) == 0, f"stats, batch {bs} repeat {rep}"
+            assert float((got - ref).abs().max()) == 0.0
+
+
+def test_permutations_bitwise(setup):
+    W, h, y = setup["W"], setup["h"], setup["y"]
+    ref, ref_st = score(W, h, y)
+    for perm in setup["pool"]["perms"]:
+        p = perm.cuda()
+        got, st = score(W, h[p].contiguous(), y[p].contiguous())
+        inv = torch.argsort(p)
+        torch.cuda.synchronize()
+        assert mismatch(got[inv], ref) == 0
+        assert mismatch(st[inv], ref_st) == 0
+
+
+def test_composition_bitwise(setup):
+    W, h, y = setup["W"], setup["h"], setup["y"]
+    ref, ref_st = score(W, h, y)
+    emb = setup["pool"]["embed"]
+    pos = emb["positions"].cuda()
+    for rep in range(2):
+        got, st = score(W, dev(emb["hidden"]), dev(emb["targets"]))
+        torch.cuda.synchronize()
+        assert mismatch(got[pos], ref) == 0
+        assert mismatch(st[pos], ref_st) == 0
+
+
+def test_dhidden_rows_bitwise(setup):
+    W, h, y, dl = setup["W"], setup["h"], setup["y"], setup["dlogp"]
+    _, st = score(W, h, y)
+    ref, _ = rlk.bwd(h, W, y, st, dl, None, want_dweight=False)
+    torch.cuda.synchronize()
+    # single rows and a batch of 4 at various positions
+    for r in (0, 17, 63):
+        got, _ = rlk.bwd(h[r:r + 1].contiguous(), W, y[r:r + 1].contiguous(), st[r:r + 1].contiguous(),
+                         dl[r:r + 1].contiguous(), None, want_dweight=False)
+        torch.cuda.synchronize()
+        assert bits_equal(got[0], ref[r]), f"row {r}"
+    got, _ = rlk.bwd(h[8:12].contiguous(), W, y[8:12].contiguous(), st[8:12].contiguous(),
+                     dl[8:12].contiguous(), None, want_dweight=False)
+    torch.cuda.synchronize()
+    assert bits_equal(got, ref[8:12])
+    # embedded in the 512-row batch (large-tile path)
+    emb = setup["pool"]["embed"]
+    he, ye = dev(emb["hidden"]), dev(emb["targets"])
+    _, ste = score(W, he, ye)
+    dle = torch.zeros(512, device="cuda")
+    pos = emb["positions"].cuda()
+    dle[pos] = dl
+    got, _ = rlk.bwd(he, W, ye, ste, dle, None, want_dweight=False)
+    torch.cuda.synchronize()
+    assert bits_equal(got[pos], ref)
+
+
+def test_dweight_repeat_deterministic(setup):
+    W, h, y, dl = setup["W"], setup["h"], setup["y"], setup["dlogp"]
+    _, st = score(W, h, y)
+    dh1, dw1 = rlk.bwd(h, W, y, st, dl, None)
+    dh2, dw2 = rlk.bwd(h, W, y, st, dl, None)
+    torch.cuda.synchronize()
+    assert bits_equal(dw1, dw2) and bits_equal(dh1, dh2)

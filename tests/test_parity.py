@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances of the operator: |d logp| <= 1e-3 per row, relative d entropy <=
+1e-3 per row, relative (Frobenius) d gradient <= 5e-3 per tensor. Small cases
+are compared element by element; the full-size cases (T = 512, 5208, 7168 at
+H = 4096, V = 151936) run the GPU on the whole batch, in the launch
+configuration the benchmark times, and compare sampled rows, plus the
+dW column-sum invariant (sum_v dW[v, :] = 0) on the whole output.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import rollout_rlk_linear_amd as rlk
+import workloads as wl
+from oracle import backward, decode_bf16, forward, slice_partials
+from tests._util import (case_to_device, check_entropy, check_grad, check_logp, dev, f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rlk.load_library()
+
+
+def run_fwd(d, **kw):
+    o = rlk.fwd(d["hidden"], d["weight"], d["targets"], **kw)
+    torch.cuda.synchronize()
+    return o
+
+
+# ------------------------------------------------------------------ tiny
+
+def test_tiny_forward():
+    c = wl.tiny()
+    d = case_to_device(c)
+    o = run_fwd(d)
+    ref = forward(c.hidden, c.weight, c.targets)
+    check_logp(o["logp"].cpu().numpy(), ref["logp"], "tiny logp")
+    check_entropy(o["entropy"].cpu().numpy(), ref["entropy"], "tiny entropy")
+    st = o["stats"].cpu().double().numpy()
+    np.testing.assert_allclose(st[:, 0], ref["m"], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(np.log1p(st[:, 1]), np.log1p(ref["R"]), rtol=1e-4, atol=1e-5)
+
+
+@pytest.mark.parametrize("with_dent", [True, False])
+@pytest.mark.parametrize("dh_f32", [False, True])
+def test_tiny_backward(with_dent, dh_f32):
+    c = wl.tiny()
+    d = case_to_device(c)
+    o = run_fwd(d)
+    de = d["dentropy"] if with_dent else None
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], de,
+                     dhidden_f32=dh_f32)
+    torch.cuda.synchronize()
+    ref = backward(c.hidden, c.weight, c.targets, c.dlogp, c.dentropy if with_dent else None)
+    assert dh.dtype == (torch.float32 if dh_f32 else torch.bfloat16)
+    check_grad(f64(dh), ref["dH"], "tiny dH")
+    check_grad(f64(dw), ref["dW"], "tiny dW")
+
+
+# ---------------------------------------------------- ragged / edge shapes
+
+RAGGED = [(1, 64, 1), (1, 64, 2), (2, 64, 31), (3, 128, 33), (64, 64, 257), (65, 192, 1000),
+          (70, 128, 4099), (300, 64, 777), (257, 256, 2304), (33, 320, 5000)]
+
+
+@pytest.mark.parametrize("T,H,V", RAGGED)
+def test_ragged_shapes(T, H, V):
+    c = wl.make_case("ragged", T, H, V, seed=1000 + T + V, rms=True)
+    c.weight = wl.to_bf16(c.weight.float() * 20)  # logits of spread ~ 1.3
+    d = case_to_device(c)
+    o = run_fwd(d)
+    ref = forward(c.hidden, c.weight, c.targets)
+    check_logp(o["logp"].cpu().numpy(), ref["logp"], f"logp {T,H,V}")
+    check_entropy(o["entropy"].cpu().numpy(), np.maximum(ref["entropy"], 0), f"entropy {T,H,V}")
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], d["dentropy"])
+    torch.cuda.synchronize()
+    rb = backward(c.hidden, c.weight, c.targets, c.dlogp, c.dentropy)
+    if V > 1:
+        check_grad(f64(dh), rb["dH"], f"dH {T,H,V}")
+        check_grad(f64(dw), rb["dW"], f"dW {T,H,V}")
+    else:  # one vocabulary entry: every gradient is exactly zero
+        assert float(dh.float().abs().max()) == 0.0 and float(dw.abs().max()) == 0.0
+
+
+def test_single_entry_vocabulary():
+    c = wl.make_case("v1", 5, 64, 1, seed=3)
+    o = run_fwd(case_to_device(c))
+    assert torch.all(o["logp"] == 0).item() and torch.all(o["entropy"] == 0).item()
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_uniform_logits_on_gpu():
+    T, H, V = 40, 128, 3000
+    hidden = wl.to_bf16(torch.randn(T, H, generator=torch.Generator().manual_seed(1)))
+    tg = torch.randint(0, V, (T,), generator=torch.Generator().manual_seed(2), dtype=torch.int32)
+    for W in (torch.zeros(V, H, dtype=torch.bfloat16),
+              wl.to_bf16(torch.randn(1, H, generator=torch.Generator().manual_seed(3))).repeat(V, 1)):
+        o = rlk.fwd(dev(hidden), dev(W), dev(tg))
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(o["logp"].cpu().numpy(), -math.log(V), rtol=2e-6)
+        np.testing.assert_allclose(o["entropy"].cpu().numpy(), math.log(V), rtol=2e-6)
+        # every column ties at the max: R counts them exactly
+        assert torch.all(o["stats"][:, 1] == V - 1).item()
+
+
+@pytest.mark.parametrize("c_val", [64.0, 4.0])
+def test_one_hot_dominant_on_gpu(c_val):
+    V, H = 1024, 64
+    a = math.sqrt(c_val)
+    ys = [0, 31, 32, 255, 256, 1023]
+    hidden = torch.zeros(len(ys), H)
+    hidden[:, 0] = a
+    outs_l, outs_e = [], []
+    for i, y in enumerate(ys):
+        W = torch.zeros(V, H)
+        W[y, 0] = a
+        o = rlk.fwd(dev(wl.to_bf16(hidden[i:i + 1])), dev(wl.to_bf16(W)),
+                    dev(torch.tensor([y], dtype=torch.int32)))
+        torch.cuda.synchronize()
+        outs_l.append(o["logp"].item())
+        outs_e.append(o["entropy"].item())
+    ab = float(wl.to_bf16(torch.tensor(a)).float()) ** 2  # the exact bf16 logit
+    q = (V - 1) * math.exp(-ab)
+    np.testing.assert_allclose(outs_l, -math.log1p(q), rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(outs_e, math.log1p(q) + ab * q / (1 + q), rtol=1e-4)
+
+
+def test_out_of_range_target_gives_nan():
+    c = wl.make_case("oor", 4, 64, 100, seed=9)
+    c.targets[1] = 100
+    c.targets[2] = -1
+    o = run_fwd(case_to_device(c))
+    lp = o["logp"].cpu()
+    assert torch.isnan(lp[1]) and torch.isnan(lp[2]) and torch.isfinite(lp[[0, 3]]).all()
+
+
+def test_autograd_wrapper_matches_bwd():
+    c = wl.tiny()
+    d = case_to_device(c)
+    h = d["hidden"].clone().requires_grad_(True)
+    W = d["weight"].clone().requires_grad_(True)
+    logp, ent = rlk.linear_logp(h, W, d["targets"])
+    (logp * d["dlogp"] + ent * d["dentropy"]).sum().backward()
+    o = run_fwd(d)
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], d["dentropy"])
+    torch.cuda.synchronize()
+    assert torch.equal(h.grad, dh)
+    assert torch.equal(W.grad, dw.to(torch.bfloat16))
+
+
+# ----------------------------------------------- full size: T = 512 (bench)
+
+@pytest.fixture(scope="module")
+def qwen():
+    c = wl.qwen512()
+    return c, case_to_device(c)
+
+
+def test_qwen512_forward_all_rows(qwen):
+    c, d = qwen
+    o = run_fwd(d)
+    ref = forward(c.hidden, c.weight, c.targets)
+    check_logp(o["logp"].cpu().numpy(), ref["logp"], "qwen512 logp")
+    check_entropy(o["entropy"].cpu().numpy(), ref["entropy"], "qwen512 entropy")
+
+
+def test_qwen512_backward_sampled(qwen):
+    c, d = qwen
+    o = run_fwd(d)
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], None)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(11)
+    rows = torch.randperm(c.T, generator=g)[:64].sort().values.numpy()
+    vrows = np.unique(np.concatenate([torch.randperm(c.V, generator=g)[:192].numpy(),
+                                      c.targets[:64].numpy(), [0, c.V - 1]]))
+    ref = backward(c.hidden, c.weight, c.targets, c.dlogp, None, dh_rows=rows, dw_rows=vrows)
+    check_grad(f64(dh[torch.from_numpy(rows).cuda()]), ref["dH"], "qwen512 dH rows")
+    check_grad(f64(dw[torch.from_numpy(vrows).cuda()]), ref["dW"], "qwen512 dW rows")
+    colsum = dw.double().sum(dim=0)
+    assert float(colsum.norm()) <= 1e-3 * float(dw.double().norm())
+
+
+# ------------------------------------------ full size: T = 5208 (full step)
+
+@pytest.mark.slow
+def test_step5208_sampled():
+    c = wl.step5208()
+    d = case_to_device(c)
+    o = run_fwd(d)
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], None)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(12)
+    rows = torch.randperm(c.T, generator=g)[:256].sort().values
+    ref = forward(c.hidden[rows], c.weight, c.targets[rows])
+    check_logp(o["logp"].cpu()[rows].numpy(), ref["logp"], "step5208 logp")
+    check_entropy(o["entropy"].cpu()[rows].numpy(), ref["entropy"], "step5208 entropy")
+    drow = rows[:32].numpy()
+    vrows = np.unique(np.concatenate([torch.randperm(c.V, generator=g)[:96].numpy(),
+                                      c.targets[drow].numpy()]))
+    rb = backward(c.hidden, c.weight, c.targets, c.dlogp, None, dh_rows=drow, dw_rows=vrows)
+    check_grad(f64(dh[torch.from_numpy(drow).cuda()]), rb["dH"], "step5208 dH rows")
+    check_grad(f64(dw[torch.from_numpy(vrows).cuda()]), rb["dW"], "step5208 dW rows")
+    assert float(dw.double().sum(dim=0).norm()) <= 1e-3 * float(dw.double().norm())
+
+
+# --------------------------------- full size: T = 7168, TP=4 vocabulary slices
+
+@pytest.mark.slow
+def test_slice7168_partials_combine_and_backward():
+    c = wl.slice7168()
+    hd, td = dev(c.hidden), dev(c.targets)
+    g = torch.Generator().manual_seed(13)
+    rows = torch.randperm(c.T, generator=g)[:192].sort().values
+    parts = []
+    for (a, b) in c.meta["slices"]:
+        Ws = dev(c.weight[a:b])
+        o = rlk.fwd(hd, Ws, td, vocab_start=a, vocab_total=c.V)
+        torch.cuda.synchronize()
+        assert o["logp"] is None and o["entropy"] is None
+        st = o["stats"].cpu()
+        parts.append(st)
+        m, R, B, zy = slice_partials(c.hidden[rows], c.weight[a:b], c.targets[rows], a)
+        np.testing.assert_allclose(st[rows, 0].double().numpy(), m, rtol=1e-5, atol=1e-4)
+        in_slice = np.isfinite(zy)
+        assert np.array_equal(np.isfinite(st[rows, 3].numpy()), in_slice)
+        np.testing.assert_allclose(st[rows, 3].double().numpy()[in_slice], zy[in_slice], atol=2e-4)
+        del Ws
+    logp, ent, stats = rlk.combine_host(parts)
+    ref = forward(c.hidden[rows], c.weight, c.targets[rows])
+    check_logp(logp[rows].numpy(), ref["logp"], "slice7168 logp")
+    check_entropy(ent[rows].numpy(), ref["entropy"], "slice7168 entropy")
+    # backward per slice with the combined statistics
+    stats_d = dev(stats)
+    drow = rows[:24].numpy()
+    vsel = []
+    dh_sum = None
+    dw_rows = []
+    for s, (a, b) in enumerate(c.meta["slices"]):
+        Ws = dev(c.weight[a:b])
+        dh, dw = rlk.bwd(hd, Ws, td, stats_d, dev(c.dlogp), None, vocab_start=a,
+                         vocab_total=c.V, dhidden_f32=True)
+        torch.cuda.synchronize()
+        dh_s = dh[torch.from_numpy(drow).cuda()].double().cpu()
+        dh_sum = dh_s if dh_sum is None else dh_sum + dh_s
+        loc = torch.randperm(b - a, generator=g)[:24].sort().values
+        vsel.append(loc.numpy() + a)
+        dw_rows.append(dw[loc.cuda()].double().cpu())
+        assert float(dw.double().sum(dim=0).norm()) > 0
+        del Ws, dh, dw
+    vsel = np.concatenate(vsel)
+    rb = backward(c.hidden, c.weight, c.targets, c.dlogp, None, dh_rows=drow, dw_rows=vsel)
+    check_grad(dh_sum.numpy(), rb["dH"], "slice7168 dH (sum of slices)")
+    check_grad(torch.cat(dw_rows).numpy(), rb["dW"], "slice7168 dW rows")
