@@ -143,6 +143,19 @@ RLK_API const char* rlk_backend_id(void);
 RLK_API uint64_t rlk_call_count(int which);
 RLK_API int rlk_abi_version(void);
 
+/* Per-launch event timer, for measurement. After rlk_profile_begin every
+ * kernel launch of the library is bracketed by two HIP events recorded on the
+ * launch's own stream (launch order and work are unchanged).
+ * rlk_profile_end waits for those events, stops the timer and writes, per
+ * kernel id in [0, n), the summed elapsed milliseconds and the number of
+ * launches (host arrays of n entries; n = rlk_profile_kernel_count() covers
+ * every kernel). Returns RLK_ERR_HIP if an event could not be created,
+ * recorded or read. Not thread-safe against concurrent begin/end. */
+RLK_API rlk_status rlk_profile_begin(void);
+RLK_API rlk_status rlk_profile_end(double* total_ms, uint64_t* launches, int n);
+RLK_API int rlk_profile_kernel_count(void);
+RLK_API const char* rlk_profile_kernel_name(int id);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,14 @@ def load_library(path: str | None = None):
     lib.rlk_call_count.restype = ctypes.c_uint64
     lib.rlk_abi_version.argtypes = []
     lib.rlk_abi_version.restype = ctypes.c_int
+    lib.rlk_profile_begin.argtypes = []
+    lib.rlk_profile_begin.restype = ctypes.c_int
+    lib.rlk_profile_end.argtypes = [vp, vp, ctypes.c_int]
+    lib.rlk_profile_end.restype = ctypes.c_int
+    lib.rlk_profile_kernel_count.argtypes = []
+    lib.rlk_profile_kernel_count.restype = ctypes.c_int
+    lib.rlk_profile_kernel_name.argtypes = [ctypes.c_int]
+    lib.rlk_profile_kernel_name.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
@@ -103,6 +111,21 @@ def call_count(which: int) -> int:
     return int(load_library().rlk_call_count(which))
 
 
+def profile_begin():
+    """Start the library's per-launch HIP-event timer."""
+    _check(load_library().rlk_profile_begin())
+
+
+def profile_end() -> dict:
+    """Stop the timer; returns {kernel name: (summed ms, launches)}."""
+    lib = load_library()
+    n = lib.rlk_profile_kernel_count()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_uint64 * n)()
+    _check(lib.rlk_profile_end(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(cnt, ctypes.c_void_p), n))
+    return {lib.rlk_profile_kernel_name(i).decode(): (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
 def fwd_workspace_bytes(T: int, H: int, V: int) -> int:
     return int(load_library().rlk_linear_logp_fwd_workspace_bytes(T, H, V))
 
@@ -113,6 +136,14 @@ def bwd_workspace_bytes(T: int, H: int, V: int, flags: int = 0, want_dhidden: bo
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _reuse(out: dict, key: str, shape, dtype):
+    """A caller-provided output tensor from ``out`` if it fits, else None."""
+    t = out.get(key)
+    if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        return None
+    return t
 
 
 def _check_inputs(hidden, weight, targets):
@@ -141,9 +172,9 @@ def fwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, *,
     full = vocab_start == 0 and V == vt
     dev = hidden.device
     out = {} if out is None else out
-    logp = out.get("logp") if full and want_logp else None
-    ent = out.get("entropy") if full and want_entropy else None
-    stats = out.get("stats") if want_stats or not full else None
+    logp = _reuse(out, "logp", (T,), torch.float32) if full and want_logp else None
+    ent = _reuse(out, "entropy", (T,), torch.float32) if full and want_entropy else None
+    stats = _reuse(out, "stats", (T, 4), torch.float32) if want_stats or not full else None
     if full and want_logp and logp is None:
         logp = torch.empty(T, dtype=torch.float32, device=dev)
     if full and want_entropy and ent is None:
@@ -154,6 +185,7 @@ def fwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, *,
     ws = out.get("_ws_fwd")
     if ws is None or ws.numel() < nws:
         ws = _workspace(nws, dev)
+    out.update({"logp": logp, "entropy": ent, "stats": stats, "_ws_fwd": ws})
     _check(lib.rlk_linear_logp_fwd(_ptr(hidden), _ptr(weight), _ptr(targets), T, H, V,
                                    vocab_start, vt, _ptr(logp), _ptr(ent), _ptr(stats),
                                    _ptr(ws), ws.numel(), _stream(dev)))
@@ -181,8 +213,9 @@ def bwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, stats
         if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 device tensor")
     flags = RLK_DH_F32 if dhidden_f32 else 0
-    dh = out.get("dhidden") if want_dhidden else None
-    dw = out.get("dweight") if want_dweight else None
+    dh = (_reuse(out, "dhidden", (T, H), torch.float32 if dhidden_f32 else torch.bfloat16)
+          if want_dhidden else None)
+    dw = _reuse(out, "dweight", (V, H), torch.float32) if want_dweight else None
     if want_dhidden and dh is None:
         dh = torch.empty(T, H, dtype=torch.float32 if dhidden_f32 else torch.bfloat16, device=dev)
     if want_dweight and dw is None:
@@ -191,6 +224,7 @@ def bwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, stats
     ws = out.get("_ws_bwd")
     if ws is None or ws.numel() < nws:
         ws = _workspace(nws, dev)
+    out.update({"dhidden": dh, "dweight": dw, "_ws_bwd": ws})
     _check(lib.rlk_linear_logp_bwd(_ptr(hidden), _ptr(weight), _ptr(targets), T, H, V,
                                    vocab_start, vt, _ptr(stats), _ptr(dlogp), _ptr(dentropy),
                                    _ptr(dh), _ptr(dw), flags, _ptr(ws), ws.numel(), _stream(dev)))

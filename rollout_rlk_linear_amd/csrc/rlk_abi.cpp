@@ -6,6 +6,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "rlk_internal.h"
 #include "../../include/rlk_linear.h"
@@ -48,9 +50,66 @@ rlk_status check_device() {
   return ok ? RLK_OK : RLK_ERR_UNSUPPORTED_DEVICE;
 }
 
+// Per-launch event timer: while on, every launch is bracketed by two HIP
+// events on its stream; rlk_profile_end sums the elapsed times per kernel.
+struct Profiler {
+  std::atomic<bool> on{false};
+  std::mutex mu;
+  struct Rec {
+    int id;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t next = 0;
+  bool failed = false;
+
+  hipEvent_t take() {
+    if (next == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) {
+        failed = true;
+        return nullptr;
+      }
+      pool.push_back(e);
+    }
+    return pool[next++];
+  }
+};
+Profiler g_prof;
+
 }  // namespace
 
 namespace rlk {
+
+const char* const kKernelNames[K_COUNT] = {
+    "fwd_tile", "fwd_combine", "bwd_rowprep", "bwd_recompute",
+    "bwd_dw",   "bwd_dh",      "bwd_dh_reduce", "fill_zero"};
+
+void prof_before(int id, hipStream_t st) {
+  if (!g_prof.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  hipEvent_t e = g_prof.take();
+  if (!e) return;
+  if (hipEventRecord(e, st) != hipSuccess) {
+    g_prof.failed = true;
+    return;
+  }
+  g_prof.recs.push_back({id, e, nullptr});
+}
+
+void prof_after(int id, hipStream_t st) {
+  if (!g_prof.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (g_prof.recs.empty() || g_prof.recs.back().id != id || g_prof.recs.back().b) return;
+  hipEvent_t e = g_prof.take();
+  if (!e) return;
+  if (hipEventRecord(e, st) != hipSuccess) {
+    g_prof.failed = true;
+    return;
+  }
+  g_prof.recs.back().b = e;
+}
 
 size_t fwd_workspace(int64_t T, int64_t H, int64_t V) {
   (void)H;
@@ -262,5 +321,50 @@ RLK_API uint64_t rlk_call_count(int which) {
 }
 
 RLK_API int rlk_abi_version(void) { return kAbiVersion; }
+
+RLK_API rlk_status rlk_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.recs.clear();
+  g_prof.next = 0;
+  g_prof.failed = false;
+  g_prof.on.store(true);
+  return RLK_OK;
+}
+
+RLK_API rlk_status rlk_profile_end(double* total_ms, uint64_t* launches, int n) {
+  if (n < 0 || (n > 0 && (!total_ms || !launches))) return RLK_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on.store(false);
+  for (int i = 0; i < n; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  rlk_status st = g_prof.failed ? RLK_ERR_HIP : RLK_OK;
+  for (const auto& r : g_prof.recs) {
+    if (!r.b) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) {
+      st = RLK_ERR_HIP;
+      continue;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = RLK_ERR_HIP;
+      continue;
+    }
+    if (r.id >= 0 && r.id < n) {
+      total_ms[r.id] += ms;
+      launches[r.id] += 1;
+    }
+  }
+  g_prof.recs.clear();
+  g_prof.next = 0;
+  return st;
+}
+
+RLK_API int rlk_profile_kernel_count(void) { return rlk::K_COUNT; }
+
+RLK_API const char* rlk_profile_kernel_name(int id) {
+  return (id >= 0 && id < rlk::K_COUNT) ? rlk::kKernelNames[id] : "";
+}
 
 }  // extern "C"

@@ -61,6 +61,24 @@ struct BwdArgs {
   float* part;
 };
 
+// Kernel ids for the optional per-launch event timer (rlk_profile_*).
+enum KernelId {
+  K_FWD_TILE = 0,
+  K_FWD_COMBINE,
+  K_BWD_ROWPREP,
+  K_BWD_RECOMPUTE,
+  K_BWD_DW,
+  K_BWD_DH,
+  K_BWD_DH_REDUCE,
+  K_FILL_ZERO,
+  K_COUNT
+};
+extern const char* const kKernelNames[K_COUNT];
+// Record a HIP event on `st` before / after a launch of kernel `id`; no-ops
+// unless the timer is on.
+void prof_before(int id, hipStream_t st);
+void prof_after(int id, hipStream_t st);
+
 size_t fwd_workspace(int64_t T, int64_t H, int64_t V);
 BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh);
 

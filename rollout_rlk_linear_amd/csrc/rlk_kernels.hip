@@ -369,28 +369,35 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// Launch with the optional per-launch event timer around it.
+#define RLK_LAUNCH(id, kernel, grid, st, ...)                                   \
+  do {                                                                          \
+    prof_before(id, st);                                                        \
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, __VA_ARGS__); \
+    prof_after(id, st);                                                         \
+  } while (0)
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   const int G = cdiv(a.V, GROUP);
   const int G8 = cdiv(G, 8) * 8;
   if (a.T <= kSmallT) {
     const int nt = cdiv(a.T, 32);
-    hipLaunchKernelGGL((fwd_tile_kernel<32, 1, 4>), dim3(G8 * nt), dim3(kThreads), 0, st, a.hidden,
-                       a.weight, a.targets, a.T, a.H, a.V, a.vocab_start, G, nt, a.part);
+    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<32, 1, 4>), G8 * nt, st, a.hidden, a.weight, a.targets,
+               a.T, a.H, a.V, a.vocab_start, G, nt, a.part);
   } else {
     const int nt = cdiv(a.T, 256);
-    hipLaunchKernelGGL((fwd_tile_kernel<256, 2, 2>), dim3(G8 * nt), dim3(kThreads), 0, st,
-                       a.hidden, a.weight, a.targets, a.T, a.H, a.V, a.vocab_start, G, nt, a.part);
+    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2>), G8 * nt, st, a.hidden, a.weight,
+               a.targets, a.T, a.H, a.V, a.vocab_start, G, nt, a.part);
   }
-  hipLaunchKernelGGL(fwd_combine_kernel, dim3(cdiv(a.T, kThreads / 64)), dim3(kThreads), 0, st,
-                     a.part, a.targets, a.T, G, a.vocab_total, a.full, a.logp, a.entropy,
-                     a.stats);
+  RLK_LAUNCH(K_FWD_COMBINE, fwd_combine_kernel, cdiv(a.T, kThreads / 64), st, a.part, a.targets,
+             a.T, G, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
   const int T = a.T, H = a.H, V = a.V;
-  hipLaunchKernelGGL(bwd_rowprep_kernel, dim3(cdiv(T, kThreads)), dim3(kThreads), 0, st, a.stats,
-                     a.dlogp, a.dentropy, a.targets, T, a.vocab_start, a.rowc);
+  RLK_LAUNCH(K_BWD_ROWPREP, bwd_rowprep_kernel, cdiv(T, kThreads), st, a.stats, a.dlogp,
+             a.dentropy, a.targets, T, a.vocab_start, a.rowc);
   const bool small = T <= kSmallT;
   const int bm = small ? 32 : 256;
   const int nt = cdiv(T, bm);
@@ -398,48 +405,46 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
   for (int c = 0; c < p.nchunks; ++c) {
     const int s0 = c * p.splits_per_chunk;
     const int s1 = s0 + p.splits_per_chunk < p.nsplits ? s0 + p.splits_per_chunk : p.nsplits;
-    const int v0 = s0 * p.split_w;                           // call-local
+    const int v0 = s0 * p.split_w;  // call-local
     const int v1 = (s1 * p.split_w < V) ? s1 * p.split_w : V;
     const int width = v1 - v0;
     const int ngroups = cdiv(width, GROUP);
     const int chunk_g0 = v0 / GROUP;
     const int ng8 = cdiv(ngroups, 8) * 8;
     if (small)
-      hipLaunchKernelGGL((bwd_recompute_kernel<32, 1, 4>), dim3(ng8 * nt), dim3(kThreads), 0, st,
-                         a.hidden, a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, 1, 4>), ng8 * nt, st, a.hidden,
+                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
     else
-      hipLaunchKernelGGL((bwd_recompute_kernel<256, 2, 2>), dim3(ng8 * nt), dim3(kThreads), 0, st,
-                         a.hidden, a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 2, 2>), ng8 * nt, st, a.hidden,
+                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
     if (a.dweight) {
       const int nvt = cdiv(width, 256);
       const int nht8 = cdiv(nht, 8) * 8;
-      hipLaunchKernelGGL(bwd_dw_kernel, dim3(nht8 * nvt), dim3(kThreads), 0, st, a.gtv, p.ldg,
-                         a.hidden, T, H, V, v0, ngroups * GROUP, nvt, nht, a.dweight);
+      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, nht8 * nvt, st, a.gtv, p.ldg, a.hidden, T, H, V, v0,
+                 ngroups * GROUP, nvt, nht, a.dweight);
     }
     if (a.dhidden) {
       const int nsp = s1 - s0;
       const int rest8 = cdiv(nht * nsp, 8) * 8;
       if (small)
-        hipLaunchKernelGGL((bwd_dh_kernel<32, 1, 4>), dim3(rest8 * nt), dim3(kThreads), 0, st,
-                           a.gtv, p.ldg, a.weight, T, H, V, v0, p.split_w, nsp, s0, nt, nht,
-                           a.part);
+        RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<32, 1, 4>), rest8 * nt, st, a.gtv, p.ldg, a.weight, T,
+                   H, V, v0, p.split_w, nsp, s0, nt, nht, a.part);
       else
-        hipLaunchKernelGGL((bwd_dh_kernel<256, 2, 2>), dim3(rest8 * nt), dim3(kThreads), 0, st,
-                           a.gtv, p.ldg, a.weight, T, H, V, v0, p.split_w, nsp, s0, nt, nht,
-                           a.part);
+        RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<256, 2, 2>), rest8 * nt, st, a.gtv, p.ldg, a.weight,
+                   T, H, V, v0, p.split_w, nsp, s0, nt, nht, a.part);
     }
   }
   if (a.dhidden) {
     const int64_t n = (int64_t)T * H;
-    hipLaunchKernelGGL(bwd_dh_reduce_kernel, dim3(cdiv(n / 4, kThreads)), dim3(kThreads), 0, st,
-                       a.part, p.nsplits, n, a.dh_f32, a.dhidden);
+    RLK_LAUNCH(K_BWD_DH_REDUCE, bwd_dh_reduce_kernel, cdiv(n / 4, kThreads), st, a.part,
+               p.nsplits, n, a.dh_f32, a.dhidden);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(cdiv(n, kThreads)), dim3(kThreads), 0, st, p, n);
+  RLK_LAUNCH(K_FILL_ZERO, fill_zero_kernel, cdiv(n, kThreads), st, p, n);
   return hipGetLastError();
 }
 

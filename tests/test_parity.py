@@ -17,7 +17,8 @@ import torch
 import rollout_rlk_linear_amd as rlk
 import workloads as wl
 from oracle import backward, decode_bf16, forward, slice_partials
-from tests._util import (case_to_device, check_entropy, check_grad, check_logp, dev, f64)
+from tests._util import (GRAD_REL, case_to_device, check_entropy, check_grad, check_logp, dev,
+                         f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +28,19 @@ def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     rlk.load_library()
+
+
+def check_column_sum(dw, what):
+    """sum_v G[t, v] = 0 for every row, so the columns of dW sum to zero.
+
+    The kernels multiply the bf16-rounded logit gradient, whose rounding does
+    not cancel: per row the sum over v of the rounding errors is about
+    2^-9 / sqrt(3) ~ 1.1e-3 of ||G_t||, and the same fraction of ||dW||
+    carries over to the column sum. The bound is the gradient tolerance.
+    """
+    colsum = dw.double().sum(dim=0)
+    ratio = float(colsum.norm()) / float(dw.double().norm())
+    assert ratio <= GRAD_REL, f"{what}: ||sum_v dW[v]|| / ||dW|| = {ratio:.3e}"
 
 
 def run_fwd(d, **kw):
@@ -185,8 +199,7 @@ def test_qwen512_backward_sampled(qwen):
     ref = backward(c.hidden, c.weight, c.targets, c.dlogp, None, dh_rows=rows, dw_rows=vrows)
     check_grad(f64(dh[torch.from_numpy(rows).cuda()]), ref["dH"], "qwen512 dH rows")
     check_grad(f64(dw[torch.from_numpy(vrows).cuda()]), ref["dW"], "qwen512 dW rows")
-    colsum = dw.double().sum(dim=0)
-    assert float(colsum.norm()) <= 1e-3 * float(dw.double().norm())
+    check_column_sum(dw, "qwen512")
 
 
 # ------------------------------------------ full size: T = 5208 (full step)
@@ -209,7 +222,7 @@ def test_step5208_sampled():
     rb = backward(c.hidden, c.weight, c.targets, c.dlogp, None, dh_rows=drow, dw_rows=vrows)
     check_grad(f64(dh[torch.from_numpy(drow).cuda()]), rb["dH"], "step5208 dH rows")
     check_grad(f64(dw[torch.from_numpy(vrows).cuda()]), rb["dW"], "step5208 dW rows")
-    assert float(dw.double().sum(dim=0).norm()) <= 1e-3 * float(dw.double().norm())
+    check_column_sum(dw, "step5208")
 
 
 # --------------------------------- full size: T = 7168, TP=4 vocabulary slices
