@@ -33,6 +33,12 @@ constexpr int CHUNKS_PER_GROUP = GROUP / CHUNK;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Wave index within the workgroup, as a value the compiler knows is uniform
+// across the wave (so choices made from it stay scalar).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ---------------------------------------------------------------- bf16 --
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
@@ -277,7 +283,7 @@ struct TileGemm {
                                       int k_end) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = wave_id();
     const int wm = wave % WM, wn = wave / WM;
     OperandTile<BM, AT> ta;
     OperandTile<BN, BT> tb;
@@ -303,6 +309,205 @@ struct TileGemm {
       }
       __syncthreads();
     }
+  }
+};
+
+}  // namespace rlk
+
+namespace rlk {
+
+// ------------------------------------------------ async (LDS-DMA) mainloop
+//
+// gfx950 buffer loads can write straight into LDS: `buffer_load_dwordx4 ...
+// lds` stores lane i's 16 bytes at (LDS base + 16 i), so one instruction
+// fills 1 KB. Operand rows are staged as 64-byte rows (32 bf16 = one MFMA
+// k-step) in a ring of four stages; the 16-byte pieces of row r are stored
+// XOR-swizzled, piece c at slot c ^ ((r >> 2) & 3), which keeps the 16-row
+// fragment reads free of bank conflicts. Rows past the valid range read as
+// zero through the buffer's hardware range check (num_records), the k offset
+// of a stage travels in the scalar offset, so the steady-state loop issues
+// no vector ALU work for addressing and holds no staging registers.
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// C[BM x BN] += A[BM x K] * B[BN x K]^T, both operands K-contiguous
+// (element (r, k) at base[r * ld + k]). k runs over [k_begin, k_end) in
+// ascending MFMA steps of 32, starting at k_begin; (k_end - k_begin) must be
+// a multiple of 32 and every row must hold at least k_end elements past its
+// start. WM x WN waves (4 or 8, i.e. 256 or 512 threads); same accumulator
+// layout as TileGemm. With DB the fragments of stage s+1 are read from LDS
+// while the MFMAs of stage s run (two fragment register sets).
+template <int BM, int BN, int WM, int WN, bool DB = false>
+struct AsyncGemm {
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = 64 * NW;                    // threads
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row DMA blocks");
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int MI = WTM / 16, NJ = WTN / 16;
+  static constexpr int NST = 4;
+  static constexpr int ROWB = 64;                       // bytes per staged row
+  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+  static constexpr int NI_A = BM / 16, NI_B = BN / 16;  // 1 KB DMA blocks per stage
+  static constexpr int NI = NI_A + NI_B;
+  static constexpr int NI_W_MAX = (NI + NW - 1) / NW;   // blocks issued by one wave per stage
+  static constexpr int NI_W_MIN = NI / NW;
+
+  f32x4 acc[MI][NJ];
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // lds: LDS_BYTES of shared memory (16-byte aligned).
+  // A, B: row 0 of the tile; lda, ldb in elements; a_rows, b_rows: valid rows (<= 0: none).
+  __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
+                                      int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
+                                      int k_begin, int k_end) {
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int wm = wave % WM, wn = wave / WM;
+    const int nsteps = (k_end - k_begin) / 32;
+    if (nsteps <= 0) return;
+
+    // buffer resources over the valid rows only (rows past them read as zero)
+    const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
+    const int br = b_rows < 0 ? 0 : (b_rows > BN ? BN : b_rows);
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
+    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
+    // lane -> (row within a 16-row block, logical 16-byte piece) of one DMA block
+    const int drow = lane >> 2;
+    const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);
+    int voff[NI_W_MAX];
+#pragma unroll
+    for (int ii = 0; ii < NI_W_MAX; ++ii) {
+      const int j = wave + NW * ii;
+      if (j < NI_A)
+        voff[ii] = (int)((16 * j + drow) * lda * 2) + 16 * dpiece;
+      else
+        voff[ii] = (int)((16 * (j - NI_A) + drow) * ldb * 2) + 16 * dpiece;
+    }
+
+    auto issue = [&](int s) {
+      unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+      const int koff = (k_begin + 32 * s) * 2;
+#pragma unroll
+      for (int ii = 0; ii < NI_W_MAX; ++ii) {
+        const int j = wave + NW * ii;
+        if (j < NI) {
+          if (j < NI_A)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void_ptr)(st + j * 1024), 16,
+                                                     voff[ii], koff, 0, 0);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_ptr)(st + j * 1024), 16,
+                                                     voff[ii], koff, 0, 0);
+        }
+      }
+    };
+
+    // fragment read offset of this lane inside a 16-row block (swizzled)
+    const int frow = lane & 15;
+    const int fpiece = (lane >> 4) ^ ((lane >> 2) & 3);
+    const int foff = frow * ROWB + 16 * fpiece;
+    auto read_frags = [&](int s, bf16x8 (&af)[MI], bf16x8 (&bfr)[NJ]) {
+      const unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        af[i] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB + foff));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        bfr[j] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn * WTN + 16 * j) * ROWB + foff));
+      // keep every fragment read ahead of the MFMAs (no load-wait-compute chains)
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mfmas = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    // wait until stage `want` has landed; stages up to `last` have been issued
+    auto wait_stage = [&](int want, int last) {
+      const int after = last - want;
+      if (after >= 3)
+        wait_vmcnt<3 * NI_W_MIN>();
+      else if (after == 2)
+        wait_vmcnt<2 * NI_W_MIN>();
+      else if (after == 1)
+        wait_vmcnt<NI_W_MIN>();
+      else
+        wait_vmcnt<0>();
+    };
+    auto last_of = [&](int s) { return s < nsteps - 1 ? s : nsteps - 1; };
+
+    if constexpr (!DB) {
+      // ring of 4 slots: stage s computes while s+1..s+3 are in flight; slot
+      // s-1 is refilled (with s+3) once every wave is past the barrier of
+      // stage s, which it reaches only after its MFMAs of s-1 consumed their reads
+      for (int s = 0; s < 3 && s < nsteps; ++s) issue(s);
+      for (int s = 0; s < nsteps; ++s) {
+        wait_stage(s, last_of(s + 2));
+        barrier_only();
+        if (s + 3 < nsteps) issue(s + 3);
+        bf16x8 af[MI], bfr[NJ];
+        read_frags(s, af, bfr);
+        mfmas(af, bfr);
+      }
+    } else {
+      // fragments of stage s+1 are read while the MFMAs of stage s run; slot
+      // s is refilled (with s+4) only after every wave has waited for its own
+      // reads of it (lgkmcnt(0)) and passed the barrier
+      auto step = [&](int s, bf16x8 (&afc)[MI], bf16x8 (&bfc)[NJ], bf16x8 (&afn)[MI],
+                      bf16x8 (&bfn)[NJ]) {
+        if (s + 1 < nsteps) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): stage s fragments are in registers
+          wait_stage(s + 1, last_of(s + 3));
+          barrier_only();
+          if (s + NST < nsteps) issue(s + NST);
+          read_frags(s + 1, afn, bfn);
+        }
+        mfmas(afc, bfc);
+      };
+      for (int s = 0; s < NST && s < nsteps; ++s) issue(s);
+      wait_stage(0, last_of(NST - 1));
+      barrier_only();
+      bf16x8 a0[MI], b0[NJ], a1[MI], b1[NJ];
+      read_frags(0, a0, b0);
+      int s = 0;
+      for (; s + 1 < nsteps; s += 2) {
+        step(s, a0, b0, a1, b1);
+        step(s + 1, a1, b1, a0, b0);
+      }
+      if (s < nsteps) step(s, a0, b0, a1, b1);
+    }
+    // all DMA done and every wave past its last fragment read: LDS is free
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 };
 

@@ -40,8 +40,8 @@ struct BwdPlan {
   int splits_per_chunk;
   int nchunks;
   int64_t ldg;          // row stride of the G chunk buffer (columns)
-  int64_t Tp;           // rows reserved for rowc (T rounded up)
-  size_t off_rowc, off_gtv, off_part, total;
+  int64_t Tp;           // T rounded up to the dW k-step granularity (32 or 64)
+  size_t off_rowc, off_hT, off_gtv, off_gvt, off_part, total;
 };
 
 struct BwdArgs {
@@ -57,7 +57,9 @@ struct BwdArgs {
   int dh_f32;
   float* dweight;
   float4* rowc;
-  uint16_t* gtv;
+  uint16_t* hT;   // [H][Tp] transposed hidden (dW operand)
+  uint16_t* gtv;  // [Tp][ldg] logit gradient, rows t (dH operand)
+  uint16_t* gvt;  // [ldg][Tp] logit gradient, rows v (dW operand)
   float* part;
 };
 
@@ -71,6 +73,7 @@ enum KernelId {
   K_BWD_DH,
   K_BWD_DH_REDUCE,
   K_FILL_ZERO,
+  K_BWD_TRANSPOSE,
   K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];

@@ -48,8 +48,9 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int V, int64_t vocab_start, int G,
     int n_ttiles, float4* __restrict__ part) {
-  using Gm = TileGemm<BM, GROUP, WM, WN, false, false>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Gm::LDS_BYTES / 2];
+  using Gm = AsyncGemm<BM, GROUP, WM, WN>;
+  static_assert(BM * CHUNKS_PER_GROUP * 3 * 4 <= Gm::LDS_BYTES, "chunk stats fit in the stages");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
   __shared__ int ycol[BM];
   __shared__ float zys[BM];
 
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
 
   float* cst = reinterpret_cast<float*>(lds);  // [BM][8 chunks][3]
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
   const int vlim = V - col0;
 #pragma unroll
@@ -183,16 +184,22 @@ __global__ __launch_bounds__(kThreads) void bwd_rowprep_kernel(
   rowc[2 * t + 1] = make_float4(de, __int_as_float(yli), 0.f, 0.f);
 }
 
-// G for one (T-tile, group) of the chunk, bf16 into gtv[t][lg*256 + c].
+// G for one (T-tile, group) of the chunk, rounded to bf16 and stored twice:
+// gtv[t][lg*256 + c] (row t, for dH) and gvt[lg*256 + c][t] (row v, for dW),
+// both through an LDS staging tile so every global store is a full row piece.
+// Rows t in [T, Tp) of gvt are written as zeros (dW reads K = Tp).
 template <int BM, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
     int V, int chunk_g0, int n_groups, int n_ttiles, const float4* __restrict__ rowc,
-    uint16_t* __restrict__ gtv, int64_t ldg) {
-  using Gm = TileGemm<BM, GROUP, WM, WN, false, false>;
-  constexpr int LDG_S = GROUP + 8;  // staging row (bf16), 528 B
-  static_assert(BM * LDG_S * 2 <= Gm::LDS_BYTES, "staging tile must fit in the stages");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Gm::LDS_BYTES / 2];
+    uint16_t* __restrict__ gtv, int64_t ldg, uint16_t* __restrict__ gvt, int Tp) {
+  using Gm = AsyncGemm<BM, GROUP, WM, WN>;
+  constexpr int LDG_S = GROUP + 8;  // [t][v] staging row (bf16), 528 B
+  constexpr int LDT_S = BM + 8;     // [v][t] staging row (bf16)
+  constexpr int STG = (BM * LDG_S > GROUP * LDT_S ? BM * LDG_S : GROUP * LDT_S) * 2;
+  constexpr int LDSB = Gm::LDS_BYTES > STG ? Gm::LDS_BYTES : STG;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
+  uint16_t* stg = reinterpret_cast<uint16_t*>(lds);
 
   int lg, tt;
   xcd_decode(blockIdx.x, n_ttiles, lg, tt);
@@ -208,9 +215,10 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
          H);
 
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
   const int vlim = V - col0;
+  // logit gradient in place of the logits (fp32), rounded to bf16 below
 #pragma unroll
   for (int i = 0; i < Gm::MI; ++i) {
 #pragma unroll
@@ -235,43 +243,100 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
           const float onehot_term = (cl == yloc) ? -expm1f(lp) : -p;  // [v==y] - p
           gv = dl * onehot_term - de * (p * (zd + Hb));
         }
-        lds[rl * LDG_S + cl] = (uint16_t)f32_to_bf16_rne(gv);
+        gm.acc[i][j][r] = gv;
       }
     }
   }
-  __syncthreads();
-  // coalesced store: 32 threads per row, 16 B each
-  const int c8 = (tid & 31) * 8;
-  for (int rl = tid >> 5; rl < BM; rl += kThreads / 32) {
-    const int t = row0 + rl;
-    if (t >= T) break;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + rl * LDG_S + c8);
-    *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * GROUP + c8) = v;
+  // (1) [v][t] tile -> gvt rows: each lane holds 4 consecutive t of one column
+  if (gvt) {
+#pragma unroll
+    for (int i = 0; i < Gm::MI; ++i) {
+      const int rl0 = wm * Gm::WTM + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < Gm::NJ; ++j) {
+        const int cl = wn * Gm::WTN + 16 * j + (lane & 15);
+        const uint32_t lo = f32_to_bf16_rne(gm.acc[i][j][0]) | (f32_to_bf16_rne(gm.acc[i][j][1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(gm.acc[i][j][2]) | (f32_to_bf16_rne(gm.acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(stg + cl * LDT_S + rl0) = make_uint2(lo, hi);
+      }
+    }
+    __syncthreads();
+    // rows of BM t values; 16 B per thread
+    constexpr int TPR = BM / 8;  // threads per row
+    const int tcol = (tid % TPR) * 8;
+    const int t = row0 + tcol;
+    if (t < Tp) {
+      for (int cl = tid / TPR; cl < GROUP; cl += kThreads / TPR) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + cl * LDT_S + tcol);
+        *reinterpret_cast<u32x4*>(gvt + ((int64_t)lg * GROUP + cl) * Tp + t) = v;
+      }
+    }
+    __syncthreads();
+  }
+  // (2) [t][v] tile -> gtv rows
+  if (gtv) {
+#pragma unroll
+    for (int i = 0; i < Gm::MI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
+#pragma unroll
+        for (int j = 0; j < Gm::NJ; ++j) {
+          const int cl = wn * Gm::WTN + 16 * j + (lane & 15);
+          stg[rl * LDG_S + cl] = (uint16_t)f32_to_bf16_rne(gm.acc[i][j][r]);
+        }
+      }
+    }
+    __syncthreads();
+    const int c8 = (tid & 31) * 8;
+    for (int rl = tid >> 5; rl < BM; rl += kThreads / 32) {
+      const int t = row0 + rl;
+      if (t >= T) break;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * LDG_S + c8);
+      *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * GROUP + c8) = v;
+    }
   }
 }
 
-// dW[chunk_v0 + v, h] = sum_t G[t, v] h[t, h]; tile 256 (v) x 256 (h).
+// hT[h][t] = hidden[t][h] for t < T, 0 for T <= t < Tp (64 x 64 tiles via LDS).
+__global__ __launch_bounds__(kThreads) void transpose_hidden_kernel(
+    const uint16_t* __restrict__ hidden, int T, int H, int Tp, uint16_t* __restrict__ hT) {
+  __shared__ uint16_t tile[64][66];
+  const int t0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int t = t0 + r;
+    tile[r][tx] = (t < T) ? hidden[(int64_t)t * H + h0 + tx] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int t = t0 + tx;
+    if (t < Tp) hT[(int64_t)(h0 + r) * Tp + t] = tile[tx][r];
+  }
+}
+
+// dW[chunk_v0 + v, h] = sum_t G[t, v] h[t, h] = sum_t gvt[v][t] hT[h][t];
+// tile 256 (v) x 256 (h), K = Tp (rows t >= T are zeros in both operands).
 __global__ __launch_bounds__(kThreads) void bwd_dw_kernel(
-    const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ hidden, int T,
-    int H, int V, int chunk_v0, int chunk_w, int n_vtiles, int n_htiles,
-    float* __restrict__ dweight) {
-  using Gm = TileGemm<256, 256, 2, 2, true, true>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Gm::LDS_BYTES / 2];
-  // v-tiles fastest within an XCD so the h columns stay hot
+    const uint16_t* __restrict__ gvt, const uint16_t* __restrict__ hT, int Tp, int H, int V,
+    int chunk_v0, int chunk_w, int n_vtiles, int n_htiles, float* __restrict__ dweight) {
+  using Gm = AsyncGemm<256, 256, 2, 2>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
+  // h-tiles fastest within an XCD: one G^T tile stays hot in L2 for all of H
   int vt, ht;
   {
     const int b = blockIdx.x;
     const int xcd = b & 7, seq = b >> 3;
-    ht = xcd + 8 * (seq / n_vtiles);
-    vt = seq % n_vtiles;
+    vt = xcd + 8 * (seq / n_htiles);
+    ht = seq % n_htiles;
   }
-  if (ht >= n_htiles) return;
+  if (vt >= n_vtiles) return;
   const int v0 = vt * 256, h0 = ht * 256;
   Gm gm;
   gm.zero();
-  gm.run(lds, gtv + v0, ldg, chunk_w - v0, hidden + h0, H, H - h0, 0, T);
+  gm.run(lds, gvt + (int64_t)v0 * Tp, Tp, chunk_w - v0, hT + (int64_t)h0 * Tp, Tp, H - h0, 0, Tp);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int wm = wave % 2, wn = wave / 2;
 #pragma unroll
   for (int i = 0; i < Gm::MI; ++i) {
@@ -318,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
   gm.run(lds, gtv + (int64_t)row0 * ldg, ldg, T - row0, weight + (int64_t)chunk_v0 * H + h0, H,
          H - h0, s_begin, s_end);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
   float* out = part + (int64_t)(split_base + si) * T * H;
 #pragma unroll
@@ -365,6 +430,28 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   if (i < n) p[i] = 0.f;
 }
 
+// Explicit instantiations: every launched template kernel gets its host stub
+// even where the host pass would not instantiate it implicitly.
+#define RLK_FWD_TILE(BM, WM, WN)                                                              \
+  template __global__ void fwd_tile_kernel<BM, WM, WN>(                                       \
+      const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__, \
+      int, int, int, int64_t, int, int, float4* __restrict__);
+#define RLK_RECOMPUTE(BM, WM, WN)                                                             \
+  template __global__ void bwd_recompute_kernel<BM, WM, WN>(                                  \
+      const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
+      const float4* __restrict__, uint16_t* __restrict__, int64_t, uint16_t* __restrict__, int);
+#define RLK_DH(BM, WM, WN)                                                                     \
+  template __global__ void bwd_dh_kernel<BM, WM, WN>(const uint16_t* __restrict__, int64_t,    \
+                                                     const uint16_t* __restrict__, int, int, int, \
+                                                     int, int, int, int, int, int,              \
+                                                     float* __restrict__);
+RLK_FWD_TILE(32, 1, 4)
+RLK_FWD_TILE(256, 2, 2)
+RLK_RECOMPUTE(32, 1, 4)
+RLK_RECOMPUTE(256, 2, 2)
+RLK_DH(32, 1, 4)
+RLK_DH(256, 2, 2)
+
 // ======================================================== launchers ======
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -396,8 +483,17 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
   const int T = a.T, H = a.H, V = a.V;
+  const int Tp = (int)p.Tp;
   RLK_LAUNCH(K_BWD_ROWPREP, bwd_rowprep_kernel, cdiv(T, kThreads), st, a.stats, a.dlogp,
              a.dentropy, a.targets, T, a.vocab_start, a.rowc);
+  if (a.dweight) {
+    prof_before(K_BWD_TRANSPOSE, st);
+    hipLaunchKernelGGL(transpose_hidden_kernel, dim3(cdiv(Tp, 64), cdiv(H, 64)), dim3(kThreads), 0,
+                       st, a.hidden, T, H, Tp, a.hT);
+    prof_after(K_BWD_TRANSPOSE, st);
+  }
+  uint16_t* gtv = a.dhidden ? a.gtv : nullptr;
+  uint16_t* gvt = a.dweight ? a.gvt : nullptr;
   const bool small = T <= kSmallT;
   const int bm = small ? 32 : 256;
   const int nt = cdiv(T, bm);
@@ -413,14 +509,14 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
     const int ng8 = cdiv(ngroups, 8) * 8;
     if (small)
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, 1, 4>), ng8 * nt, st, a.hidden,
-                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
+                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, gtv, p.ldg, gvt, Tp);
     else
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 2, 2>), ng8 * nt, st, a.hidden,
-                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
+                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, gtv, p.ldg, gvt, Tp);
     if (a.dweight) {
       const int nvt = cdiv(width, 256);
-      const int nht8 = cdiv(nht, 8) * 8;
-      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, nht8 * nvt, st, a.gtv, p.ldg, a.hidden, T, H, V, v0,
+      const int nvt8 = cdiv(nvt, 8) * 8;
+      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, nvt8 * nht, st, a.gvt, a.hT, Tp, H, V, v0,
                  ngroups * GROUP, nvt, nht, a.dweight);
     }
     if (a.dhidden) {
