@@ -36,7 +36,7 @@ def hipcc() -> str:
 def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-function",
+            "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -41,13 +41,16 @@ __device__ __forceinline__ int wave_id() {
 
 // ---------------------------------------------------------------- bf16 --
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even, by the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+// fp32 -> bf16 bits (same rounding).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -136,6 +139,23 @@ __device__ __forceinline__ Part part_merge(const Part& l, const Part& r) {
   out.R = b.R + e * one_r;
   out.B = b.B + e * (o.B + one_r * d);
   return out;
+}
+
+// ------------------------------------------------ rolled epilogues -----
+// Copies row block i of an accumulator array into blk through a chain of
+// uniform branches, so epilogues can loop over i without unrolling (a fully
+// unrolled epilogue does not fit the instruction cache).
+template <int K, int MI, int NJ>
+__device__ __forceinline__ void acc_row_block(const f32x4 (&acc)[MI][NJ], int i,
+                                              f32x4 (&blk)[NJ]) {
+  if constexpr (K < MI) {
+    if (i == K) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) blk[j] = acc[K][j];
+      return;
+    }
+    acc_row_block<K + 1>(acc, i, blk);
+  }
 }
 
 // ------------------------------------------------------ global loads ----
@@ -329,9 +349,38 @@ namespace rlk {
 // no vector ALU work for addressing and holds no staging registers.
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+// Buffer resource (V#) for a raw byte buffer: base, stride 0, num_records =
+// bytes (loads at or past it return zero), gfx9 dword 3.
+// All arguments must be wave-uniform; the words are passed through
+// readfirstlane so they live in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 32-bit LDS address of a shared-memory pointer (what M0 expects).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
+}
+
+// One 1 KB LDS-DMA block: lane i's 16 bytes from (base + voff + soff) land at
+// LDS (addr + 16 i). Written as inline asm so that the compiler does not
+// track these LDS writes: its own conservative waits (vmcnt(0) before every
+// LDS read) would drain the prefetch pipeline. Ordering is the caller's:
+// explicit vmcnt waits and barriers (all with memory clobbers).
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t addr, int voff, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane((int)addr)), "v"(voff), "s"(rsrc),
+        "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory", "m0");
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
@@ -395,8 +444,9 @@ struct AsyncGemm {
     // buffer resources over the valid rows only (rows past them read as zero)
     const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
     const int br = b_rows < 0 ? 0 : (b_rows > BN ? BN : b_rows);
-    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
-    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
+    const i32x4 rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
+    const i32x4 rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
+    const uint32_t lds0 = lds_addr(lds);
     // lane -> (row within a 16-row block, logical 16-byte piece) of one DMA block
     const int drow = lane >> 2;
     const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);
@@ -411,18 +461,16 @@ struct AsyncGemm {
     }
 
     auto issue = [&](int s) {
-      unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+      const uint32_t st = lds0 + (uint32_t)((s % NST) * STAGE_BYTES);
       const int koff = (k_begin + 32 * s) * 2;
 #pragma unroll
       for (int ii = 0; ii < NI_W_MAX; ++ii) {
         const int j = wave + NW * ii;
         if (j < NI) {
           if (j < NI_A)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void_ptr)(st + j * 1024), 16,
-                                                     voff[ii], koff, 0, 0);
+            dma16(rsA, st + j * 1024, voff[ii], koff);
           else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_ptr)(st + j * 1024), 16,
-                                                     voff[ii], koff, 0, 0);
+            dma16(rsB, st + j * 1024, voff[ii], koff);
         }
       }
     };

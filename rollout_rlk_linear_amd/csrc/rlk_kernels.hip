@@ -43,16 +43,46 @@ __device__ __forceinline__ void xcd_decode(int b, int n_ttiles, int& g, int& tt)
 
 // ======================================================= forward tile ====
 
+// Statistics of one row over one wave's 128 columns (a "chunk"): the lane
+// holds the row's values at columns 16 j + (lane % 16), j = 0..7. In-lane
+// pairwise tree over j, then the 16-lane DPP tree. Invalid columns are -inf.
+struct ChunkStats {
+  float m, R, B;
+};
+__device__ __forceinline__ ChunkStats chunk_stats(const float (&z)[8]) {
+  float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                   fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+  const float m = row16_max(mx);
+  int nt = 0;
+  float e[8], t[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool tie = z[j] == m;
+    const bool valid = z[j] != neg_inf();
+    nt += tie ? 1 : 0;
+    const float d = valid ? z[j] - m : 0.f;
+    e[j] = (tie || !valid) ? 0.f : exp_fast(d);
+    t[j] = e[j] * d;
+  }
+  const float rs = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  const float bs = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+  ChunkStats c;
+  c.m = m;
+  c.R = row16_sum(rs) + (float)(row16_sum_i(nt) - 1);
+  c.B = row16_sum(bs);
+  return c;
+}
+
 template <int BM, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int V, int64_t vocab_start, int G,
     int n_ttiles, float4* __restrict__ part) {
   using Gm = AsyncGemm<BM, GROUP, WM, WN>;
-  static_assert(BM * CHUNKS_PER_GROUP * 3 * 4 <= Gm::LDS_BYTES, "chunk stats fit in the stages");
+  static_assert(WN == 2 && Gm::WTN == 128 && Gm::NJ == 8, "one 128-column chunk per wave");
+  static_assert(BM * 2 * 16 <= Gm::LDS_BYTES, "chunk records fit in the stages");
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
   __shared__ int ycol[BM];
-  __shared__ float zys[BM];
 
   int g, tt;
   xcd_decode(blockIdx.x, n_ttiles, g, tt);
@@ -68,61 +98,60 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
       if (y >= 0 && y < GROUP && y < (int64_t)(V - col0)) yc = (int)y;
     }
     ycol[tid] = yc;
-    zys[tid] = neg_inf();
   }
 
   Gm gm;
   gm.zero();
   gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, V - col0, 0,
          H);
-  // run() ends on a barrier: the LDS stages are free and ycol/zys are visible.
+  // run() ends on a barrier: the LDS stages are free and ycol is visible.
 
-  float* cst = reinterpret_cast<float*>(lds);  // [BM][8 chunks][3]
+  float4* rec = reinterpret_cast<float4*>(lds);  // [BM][2 chunks] {m, R, B, zy}
   const int lane = tid & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
+  const int cbase = wn * 128;  // this wave's chunk within the group
   const int vlim = V - col0;
+  if (cbase < vlim) {
+    bool cvalid[8];
 #pragma unroll
-  for (int i = 0; i < Gm::MI; ++i) {
+    for (int j = 0; j < 8; ++j) cvalid[j] = cbase + 16 * j + (lane & 15) < vlim;
+#pragma unroll 1
+    for (int i = 0; i < Gm::MI; ++i) {
+      f32x4 blk[8];
+      acc_row_block<0>(gm.acc, i, blk);
+      int yc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
-      const int yc = ycol[rl];
+      for (int r = 0; r < 4; ++r) yc[r] = ycol[wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r] - cbase;
+      // straight-line over the four rows (no branches: rows interleave)
 #pragma unroll
-      for (int q = 0; q < Gm::NJ / 2; ++q) {
-        const int c0 = wn * Gm::WTN + CHUNK * q + (lane & 15);
-        const int c1 = c0 + 16;
-        const bool va = c0 < vlim, vb = c1 < vlim;
-        const float za = va ? gm.acc[i][2 * q][r] : neg_inf();
-        const float zb = vb ? gm.acc[i][2 * q + 1][r] : neg_inf();
-        if (c0 == yc) zys[rl] = za;
-        if (c1 == yc) zys[rl] = zb;
-        // chunk = columns c0 and c1 of the 16 lanes of this row group
-        const float m = row16_max(fmaxf(za, zb));
-        const bool ta = va && za == m, tb = vb && zb == m;
-        const int nties = row16_sum_i((int)ta + (int)tb);
-        const float da = va ? za - m : 0.f;
-        const float db = vb ? zb - m : 0.f;
-        const float ea = (ta || !va) ? 0.f : exp_fast(da);
-        const float eb = (tb || !vb) ? 0.f : exp_fast(db);
-        const float R = row16_sum(ea + eb) + (float)(nties - 1);
-        const float B = row16_sum(ea * da + eb * db);
-        if ((lane & 15) == 0) {
-          float* p = cst + (rl * CHUNKS_PER_GROUP + wn * (Gm::WTN / CHUNK) + q) * 3;
-          p[0] = m;
-          p[1] = R;
-          p[2] = B;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
+        float z[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = cvalid[j] ? blk[j][r] : neg_inf();
+        const ChunkStats c = chunk_stats(z);
+        // target logit: held by one lane of the 16 (if in this chunk), spread by a max
+        const bool yin = yc[r] >= 0 && yc[r] < 128;
+        const int jt = yc[r] >> 4;
+        float zl = neg_inf();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zl = (j == jt) ? z[j] : zl;
+        zl = (yin && (yc[r] & 15) == (lane & 15)) ? zl : neg_inf();
+        const float zy = row16_max(zl);
+        // all 16 lanes hold the same record and store it to the same slot
+        rec[rl * 2 + wn] = make_float4(c.m, c.R, c.B, zy);
       }
     }
   }
   __syncthreads();
   if (tid < BM && row0 + tid < T) {
-    const int nvc = min(CHUNKS_PER_GROUP, (vlim + CHUNK - 1) / CHUNK);
-    const float* p = cst + tid * CHUNKS_PER_GROUP * 3;
-    Part acc{p[0], p[1], p[2], neg_inf()};
-    for (int c = 1; c < nvc; ++c) acc = part_merge(acc, Part{p[3 * c], p[3 * c + 1], p[3 * c + 2], neg_inf()});
-    acc.zy = zys[tid];
+    const float4 a = rec[tid * 2];
+    Part acc{a.x, a.y, a.z, a.w};
+    if (128 < vlim) {
+      const float4 b = rec[tid * 2 + 1];
+      acc = part_merge(acc, Part{b.x, b.y, b.z, b.w});
+    }
     part[(int64_t)(row0 + tid) * G + g] = make_float4(acc.m, acc.R, acc.B, acc.zy);
   }
 }
@@ -166,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(
 // ======================================================== backward =======
 
 // rowc[2t]   = {m, log1p(R), -B/(1+R), dlogp}
-// rowc[2t+1] = {dentropy, bits of (y - vocab_start), 0, 0}
+// rowc[2t+1] = {dentropy, bits of (y - vocab_start), R/(1+R), 0}
 __global__ __launch_bounds__(kThreads) void bwd_rowprep_kernel(
     const float4* __restrict__ stats, const float* __restrict__ dlogp,
     const float* __restrict__ dent, const int32_t* __restrict__ targets, int T,
@@ -181,13 +210,13 @@ __global__ __launch_bounds__(kThreads) void bwd_rowprep_kernel(
   const int64_t yl = (int64_t)targets[t] - vocab_start;
   const int yli = (yl < INT32_MIN || yl > INT32_MAX) ? -1 : (int)yl;
   rowc[2 * t] = make_float4(s.x, L, Hb, dl);
-  rowc[2 * t + 1] = make_float4(de, __int_as_float(yli), 0.f, 0.f);
+  rowc[2 * t + 1] = make_float4(de, __int_as_float(yli), s.y / (1.f + s.y), 0.f);
 }
 
-// G for one (T-tile, group) of the chunk, rounded to bf16 and stored twice:
-// gtv[t][lg*256 + c] (row t, for dH) and gvt[lg*256 + c][t] (row v, for dW),
-// both through an LDS staging tile so every global store is a full row piece.
-// Rows t in [T, Tp) of gvt are written as zeros (dW reads K = Tp).
+// G for one (T-tile, group) of the chunk, rounded to bf16 into an LDS tile
+// [t][v], then stored twice: gtv[t][lg*256 + c] (row t, for dH; 16-byte row
+// pieces) and gvt[lg*256 + c][t] (row v, for dW; 8 t gathered down a column
+// per 16-byte store). Rows t in [T, Tp) of gvt are zeros (dW reads K = Tp).
 template <int BM, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
@@ -195,8 +224,7 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     uint16_t* __restrict__ gtv, int64_t ldg, uint16_t* __restrict__ gvt, int Tp) {
   using Gm = AsyncGemm<BM, GROUP, WM, WN>;
   constexpr int LDG_S = GROUP + 8;  // [t][v] staging row (bf16), 528 B
-  constexpr int LDT_S = BM + 8;     // [v][t] staging row (bf16)
-  constexpr int STG = (BM * LDG_S > GROUP * LDT_S ? BM * LDG_S : GROUP * LDT_S) * 2;
+  constexpr int STG = BM * LDG_S * 2;
   constexpr int LDSB = Gm::LDS_BYTES > STG ? Gm::LDS_BYTES : STG;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
   uint16_t* stg = reinterpret_cast<uint16_t*>(lds);
@@ -218,82 +246,74 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
   const int vlim = V - col0;
-  // logit gradient in place of the logits (fp32), rounded to bf16 below
+  // logit gradient, rounded to bf16, into the [t][v] staging tile
+  bool cvalid[Gm::NJ];
 #pragma unroll
+  for (int j = 0; j < Gm::NJ; ++j) cvalid[j] = wn * Gm::WTN + 16 * j + (lane & 15) < vlim;
+#pragma unroll 1
   for (int i = 0; i < Gm::MI; ++i) {
+    f32x4 blk[Gm::NJ];
+    acc_row_block<0>(gm.acc, i, blk);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
       const int t = row0 + rl;
-      float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
-      if (t < T) {
-        c0 = rowc[2 * t];
-        c1 = rowc[2 * t + 1];
-      }
+      const bool rv = t < T;
+      const int tc = rv ? t : T - 1;  // rows past T load row T-1 and are zeroed below
+      const float4 c0 = rowc[2 * tc];
+      const float4 c1 = rowc[2 * tc + 1];
       const float m = c0.x, L = c0.y, Hb = c0.z, dl = c0.w, de = c1.x;
       const int yloc = __float_as_int(c1.y) - col0;
+      const float Rn = c1.z;  // R / (1 + R) = 1 - p at the row maximum
 #pragma unroll
-      for (int j = 0; j < Gm::NJ; ++j) {
-        const int cl = wn * Gm::WTN + 16 * j + (lane & 15);
-        float gv = 0.f;
-        if (t < T && cl < vlim) {
-          const float zd = gm.acc[i][j][r] - m;
-          const float lp = zd - L;
-          const float p = exp_fast(lp);
-          const float onehot_term = (cl == yloc) ? -expm1f(lp) : -p;  // [v==y] - p
-          gv = dl * onehot_term - de * (p * (zd + Hb));
+      for (int j = 0; j < Gm::NJ; j += 2) {
+        float gv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int cl = wn * Gm::WTN + 16 * (j + u) + (lane & 15);
+          const float zd = blk[j + u][r] - m;
+          const float p = exp_fast(zd - L);
+          // [v == y] - p; at the target, 1 - p is exactly R/(1+R) when z_y is
+          // the row maximum (zd == 0) and has no cancellation otherwise (p <= 1/2)
+          const float omp = (zd == 0.f) ? Rn : 1.f - p;
+          const float onehot_term = (cl == yloc) ? omp : -p;
+          const float g = dl * onehot_term - de * (p * (zd + Hb));
+          gv[u] = (rv && cvalid[j + u]) ? g : 0.f;
         }
-        gm.acc[i][j][r] = gv;
+        const uint32_t pk = pack_bf16x2(gv[0], gv[1]);
+        const int cl0 = wn * Gm::WTN + 16 * j + (lane & 15);
+        stg[rl * LDG_S + cl0] = (uint16_t)pk;
+        stg[rl * LDG_S + cl0 + 16] = (uint16_t)(pk >> 16);
       }
     }
   }
-  // (1) [v][t] tile -> gvt rows: each lane holds 4 consecutive t of one column
-  if (gvt) {
-#pragma unroll
-    for (int i = 0; i < Gm::MI; ++i) {
-      const int rl0 = wm * Gm::WTM + 16 * i + 4 * (lane >> 4);
-#pragma unroll
-      for (int j = 0; j < Gm::NJ; ++j) {
-        const int cl = wn * Gm::WTN + 16 * j + (lane & 15);
-        const uint32_t lo = f32_to_bf16_rne(gm.acc[i][j][0]) | (f32_to_bf16_rne(gm.acc[i][j][1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(gm.acc[i][j][2]) | (f32_to_bf16_rne(gm.acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(stg + cl * LDT_S + rl0) = make_uint2(lo, hi);
-      }
-    }
-    __syncthreads();
-    // rows of BM t values; 16 B per thread
-    constexpr int TPR = BM / 8;  // threads per row
-    const int tcol = (tid % TPR) * 8;
-    const int t = row0 + tcol;
-    if (t < Tp) {
-      for (int cl = tid / TPR; cl < GROUP; cl += kThreads / TPR) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + cl * LDT_S + tcol);
-        *reinterpret_cast<u32x4*>(gvt + ((int64_t)lg * GROUP + cl) * Tp + t) = v;
-      }
-    }
-    __syncthreads();
-  }
-  // (2) [t][v] tile -> gtv rows
+  __syncthreads();
+  // gtv rows: 32 threads per row, 16 B each
   if (gtv) {
-#pragma unroll
-    for (int i = 0; i < Gm::MI; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
-#pragma unroll
-        for (int j = 0; j < Gm::NJ; ++j) {
-          const int cl = wn * Gm::WTN + 16 * j + (lane & 15);
-          stg[rl * LDG_S + cl] = (uint16_t)f32_to_bf16_rne(gm.acc[i][j][r]);
-        }
-      }
-    }
-    __syncthreads();
     const int c8 = (tid & 31) * 8;
     for (int rl = tid >> 5; rl < BM; rl += kThreads / 32) {
       const int t = row0 + rl;
       if (t >= T) break;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * LDG_S + c8);
       *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * GROUP + c8) = v;
+    }
+  }
+  // gvt rows (one per vocabulary column): 8 consecutive t per 16-byte store,
+  // gathered down a column of the staging tile; rows t in [T, Tp) are zeros
+  if (gvt) {
+    constexpr int TPR = BM / 8;  // 16-byte pieces per gvt row segment
+#pragma unroll 1
+    for (int idx = tid; idx < GROUP * TPR; idx += kThreads) {
+      const int cl = idx / TPR;
+      const int tcol = (idx % TPR) * 8;
+      const int t = row0 + tcol;
+      if (t >= Tp) continue;
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = (uint32_t)stg[(tcol + 2 * e) * LDG_S + cl] |
+               ((uint32_t)stg[(tcol + 2 * e + 1) * LDG_S + cl] << 16);
+      *reinterpret_cast<u32x4*>(gvt + ((int64_t)lg * GROUP + cl) * Tp + t) = v;
     }
   }
 }
@@ -419,9 +439,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_reduce_kernel(const float* __
   if (out_f32) {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + i4) = acc;
   } else {
-    const uint32_t lo = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
-    const uint32_t hi = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i4) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i4) =
+        make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
   }
 }
 
@@ -445,9 +464,9 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
                                                      const uint16_t* __restrict__, int, int, int, \
                                                      int, int, int, int, int, int,              \
                                                      float* __restrict__);
-RLK_FWD_TILE(32, 1, 4)
+RLK_FWD_TILE(32, 2, 2)
 RLK_FWD_TILE(256, 2, 2)
-RLK_RECOMPUTE(32, 1, 4)
+RLK_RECOMPUTE(32, 2, 2)
 RLK_RECOMPUTE(256, 2, 2)
 RLK_DH(32, 1, 4)
 RLK_DH(256, 2, 2)
@@ -469,7 +488,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   const int G8 = cdiv(G, 8) * 8;
   if (a.T <= kSmallT) {
     const int nt = cdiv(a.T, 32);
-    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<32, 1, 4>), G8 * nt, st, a.hidden, a.weight, a.targets,
+    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<32, 2, 2>), G8 * nt, st, a.hidden, a.weight, a.targets,
                a.T, a.H, a.V, a.vocab_start, G, nt, a.part);
   } else {
     const int nt = cdiv(a.T, 256);
@@ -508,7 +527,7 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
     const int chunk_g0 = v0 / GROUP;
     const int ng8 = cdiv(ngroups, 8) * 8;
     if (small)
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, 1, 4>), ng8 * nt, st, a.hidden,
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, 2, 2>), ng8 * nt, st, a.hidden,
                  a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, gtv, p.ldg, gvt, Tp);
     else
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 2, 2>), ng8 * nt, st, a.hidden,
