@@ -77,9 +77,14 @@ typedef enum rlk_status {
 /* bwd flags */
 #define RLK_DH_F32 1u /* dhidden is fp32 [T,H] (e.g. one slice's partial); default bf16 */
 
-/* Limits checked by every entry point. */
-#define RLK_MAX_T (1LL << 24)
+/* Limits checked by every entry point. T and V (the rows of W in one call)
+ * are bounded so that the byte offsets inside any 256-row tile of the
+ * kernels' operands fit the 32-bit buffer offsets (RLK_ERR_UNSUPPORTED_SHAPE
+ * beyond them); vocab_total is bounded by the int32 target ids
+ * (RLK_ERR_INVALID_ARG beyond it). */
+#define RLK_MAX_T (1LL << 21)
 #define RLK_MAX_H 65536
+#define RLK_MAX_V (1LL << 24)
 #define RLK_MAX_VOCAB ((1LL << 31) - 1)
 
 /* Bytes of device workspace the forward needs for (T, H, V). 0 when T == 0. */

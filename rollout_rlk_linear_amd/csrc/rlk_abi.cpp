@@ -29,7 +29,8 @@ rlk_status check_shape(int64_t T, int64_t H, int64_t V, int64_t vocab_start, int
   if (T < 0 || H <= 0 || V <= 0 || vocab_start < 0 || vocab_total <= 0) return RLK_ERR_INVALID_ARG;
   if (vocab_total > RLK_MAX_VOCAB || V > vocab_total || vocab_start > vocab_total - V)
     return RLK_ERR_INVALID_ARG;
-  if (T > RLK_MAX_T || H > RLK_MAX_H || (H % 64) != 0) return RLK_ERR_UNSUPPORTED_SHAPE;
+  if (T > RLK_MAX_T || H > RLK_MAX_H || V > RLK_MAX_V || (H % 64) != 0)
+    return RLK_ERR_UNSUPPORTED_SHAPE;
   return RLK_OK;
 }
 

@@ -560,3 +560,164 @@ struct AsyncGemm {
 };
 
 }  // namespace rlk
+
+namespace rlk {
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+
+// C[BM x BN] += A[BM x K] * B[K x BN] with A K-contiguous (element (r, k) at
+// A[r * lda + k]) and B K-major (element (k, n) at B[k * ldb + n]): the
+// contraction over the vocabulary, where B is W in its natural layout.
+// A is staged as in AsyncGemm. A B stage is 32 rows k of BN columns copied
+// verbatim by LDS-DMA, the 16-byte pieces of row k permuted by XOR with
+// 2 (k % 4) + 8 ((k / 8) % 2), which spreads the transposing reads below
+// over all banks. The MFMA B fragment (lane l: column l % 16, k = 8 (l / 16)
+// .. + 7) comes from two ds_read_b64_tr_b16: inside a 16-lane group, lane i
+// returns element i % 4 of what source lanes i / 4 + 4 j (j = 0..3) point at,
+// so source lane s points at row k0 + s / 4, columns n0 + 4 (s % 4) .. + 3,
+// and lane i receives B[k0 + j][n0 + i], j = 0..3.
+// k runs over [k_begin, k_end) in ascending MFMA steps of 32; the span must
+// be a multiple of 32 and every valid row of A must hold k_end elements.
+// Rows of B at or past kb_valid, and columns at or past nb_valid in its last
+// valid row, read as zero; other columns past nb_valid read whatever follows
+// in memory and only reach output columns the caller discards.
+template <int BM, int BN, int WM, int WN>
+struct AsyncGemmKN {
+  static constexpr int NW = WM * WN;
+  static_assert(NW == 4, "4 waves per workgroup");
+  static_assert(BN == 128 || BN == 256, "B rows of 256 or 512 bytes");
+  static_assert(BM % 16 == 0, "16-row A blocks");
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int MI = WTM / 16, NJ = WTN / 16;
+  static constexpr int NST = 4;
+  static constexpr int ROWB_A = 64;
+  static constexpr int ROWB_B = BN * 2;
+  static constexpr int PPR = BN / 8;    // 16-byte pieces per B row
+  static constexpr int RPB = 64 / PPR;  // B rows per 1 KB DMA block
+  static constexpr int STAGE_A = BM * ROWB_A;
+  static constexpr int STAGE_B = 32 * ROWB_B;
+  static constexpr int STAGE_BYTES = STAGE_A + STAGE_B;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+  static constexpr int NI_A = STAGE_A / 1024, NI_B = STAGE_B / 1024;
+  static constexpr int NI = NI_A + NI_B;
+  static constexpr int NI_W_MAX = (NI + NW - 1) / NW;
+  static constexpr int NI_W_MIN = NI / NW;
+
+  f32x4 acc[MI][NJ];
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  static __device__ __forceinline__ int bswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+  __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
+                                      int a_rows, const uint16_t* B, int64_t ldb, int kb_valid,
+                                      int nb_valid, int k_begin, int k_end) {
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int wm = wave % WM, wn = wave / WM;
+    const int nsteps = (k_end - k_begin) / 32;
+    if (nsteps <= 0) return;
+    const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
+    const i32x4 rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
+    const uint32_t lds0 = lds_addr(lds);
+
+    const int drow = lane >> 2;
+    const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);
+    const int brow = lane / PPR, bslot = lane % PPR;
+    int voff[NI_W_MAX];
+#pragma unroll
+    for (int ii = 0; ii < NI_W_MAX; ++ii) {
+      const int j = wave + NW * ii;
+      if (j < NI_A) {
+        voff[ii] = (int)((16 * j + drow) * lda * 2) + 16 * dpiece;
+      } else {
+        const int k = RPB * (j - NI_A) + brow;
+        voff[ii] = (int)(k * ldb * 2) + 16 * (bslot ^ bswz(k));
+      }
+    }
+
+    auto issue = [&](int s) {
+      const uint32_t st = lds0 + (uint32_t)((s % NST) * STAGE_BYTES);
+      const int k0 = k_begin + 32 * s;
+      int brows = kb_valid - k0;
+      brows = brows < 0 ? 0 : (brows > 32 ? 32 : brows);
+      // the resource ends at column nb_valid of the stage's last valid row
+      const uint32_t bbytes = brows > 0 ? (uint32_t)(((brows - 1) * ldb + nb_valid) * 2) : 0u;
+      const i32x4 rsB = make_rsrc(B + (int64_t)k0 * ldb, bbytes);
+#pragma unroll
+      for (int ii = 0; ii < NI_W_MAX; ++ii) {
+        const int j = wave + NW * ii;
+        if (j < NI) {
+          if (j < NI_A)
+            dma16(rsA, st + j * 1024, voff[ii], k0 * 2);
+          else
+            dma16(rsB, st + j * 1024, voff[ii], 0);
+        }
+      }
+    };
+
+    const int foff = (lane & 15) * ROWB_A + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
+    // transposing reads: 16-lane group g, source lane sl; read q covers rows
+    // 8 g + 4 q + sl / 4 at columns n0 + 4 (sl % 4) .. + 3
+    const int g = lane >> 4, sl = lane & 15;
+    uint32_t boff[2][NJ];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int k = 8 * g + 4 * q + (sl >> 2);
+        const int col = wn * WTN + 16 * j + 4 * (sl & 3);
+        boff[q][j] = (uint32_t)(STAGE_A + k * ROWB_B + 16 * ((col >> 3) ^ bswz(k)) + 2 * (col & 7));
+      }
+
+    auto wait_stage = [&](int want, int last) {
+      const int after = last - want;
+      if (after >= 3)
+        wait_vmcnt<3 * NI_W_MIN>();
+      else if (after == 2)
+        wait_vmcnt<2 * NI_W_MIN>();
+      else if (after == 1)
+        wait_vmcnt<NI_W_MIN>();
+      else
+        wait_vmcnt<0>();
+    };
+    auto last_of = [&](int s) { return s < nsteps - 1 ? s : nsteps - 1; };
+
+    // same 4-slot ring as AsyncGemm
+    for (int s = 0; s < 3 && s < nsteps; ++s) issue(s);
+    for (int s = 0; s < nsteps; ++s) {
+      wait_stage(s, last_of(s + 2));
+      barrier_only();
+      if (s + 3 < nsteps) issue(s + 3);
+      unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+      bf16x8 af[MI], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        af[i] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB_A + foff));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[0][j]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[1][j]));
+        bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+};
+
+}  // namespace rlk

@@ -376,32 +376,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dw_kernel(
 }
 
 // dH partial of split (split_base + si): rows t of the T-tile, columns h of
-// the H-tile, v over [s_begin, s_end) of the chunk in ascending order.
-template <int BM, int WM, int WN>
+// the H-tile, v over [s_begin, s_end) of the chunk in ascending order (the
+// G columns past V are zeros and the W rows past V read as zero, so the span
+// is rounded up to whole MFMA steps). Work items (t-tile fastest, then
+// h-tile, then split) are dealt to the 8 XCDs in contiguous runs, so one
+// split's G rows and W rows are fetched into one XCD's L2 and reused there.
+template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
     const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ weight, int T,
     int H, int V, int chunk_v0, int split_w, int n_splits, int split_base, int n_ttiles,
-    int n_htiles, float* __restrict__ part) {
-  using Gm = TileGemm<BM, 256, WM, WN, false, true>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Gm::LDS_BYTES / 2];
-  // T-tiles fastest within an XCD so W[split, h-tile] is shared in L2
-  int tt, rest;
-  {
-    const int b = blockIdx.x;
-    const int xcd = b & 7, seq = b >> 3;
-    rest = xcd + 8 * (seq / n_ttiles);
-    tt = seq % n_ttiles;
-  }
-  if (rest >= n_htiles * n_splits) return;
-  const int ht = rest % n_htiles;
-  const int si = rest / n_htiles;
-  const int row0 = tt * BM, h0 = ht * 256;
+    int n_htiles, int per_xcd, float* __restrict__ part) {
+  using Gm = AsyncGemmKN<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
+  const int seq = blockIdx.x >> 3;
+  if (seq >= per_xcd) return;
+  const int w = (blockIdx.x & 7) * per_xcd + seq;
+  if (w >= n_ttiles * n_htiles * n_splits) return;
+  const int tt = w % n_ttiles;
+  const int ht = (w / n_ttiles) % n_htiles;
+  const int si = w / (n_ttiles * n_htiles);
+  const int row0 = tt * BM, h0 = ht * BN;
   const int s_begin = si * split_w;
   const int s_end = min(s_begin + split_w, V - chunk_v0);
+  const int k_end = s_begin + ((s_end - s_begin + 31) & ~31);
   Gm gm;
   gm.zero();
   gm.run(lds, gtv + (int64_t)row0 * ldg, ldg, T - row0, weight + (int64_t)chunk_v0 * H + h0, H,
-         H - h0, s_begin, s_end);
+         V - chunk_v0, min(BN, H - h0), s_begin, k_end);
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
@@ -459,17 +460,16 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   template __global__ void bwd_recompute_kernel<BM, WM, WN>(                                  \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
       const float4* __restrict__, uint16_t* __restrict__, int64_t, uint16_t* __restrict__, int);
-#define RLK_DH(BM, WM, WN)                                                                     \
-  template __global__ void bwd_dh_kernel<BM, WM, WN>(const uint16_t* __restrict__, int64_t,    \
-                                                     const uint16_t* __restrict__, int, int, int, \
-                                                     int, int, int, int, int, int,              \
-                                                     float* __restrict__);
+#define RLK_DH(BM, BN, WM, WN)                                                             \
+  template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                    \
+      const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, int, \
+      int, int, int, int, int, int, float* __restrict__);
 RLK_FWD_TILE(32, 2, 2)
 RLK_FWD_TILE(256, 2, 2)
 RLK_RECOMPUTE(32, 2, 2)
 RLK_RECOMPUTE(256, 2, 2)
-RLK_DH(32, 1, 4)
-RLK_DH(256, 2, 2)
+RLK_DH(32, 128, 1, 4)
+RLK_DH(256, 256, 2, 2)
 
 // ======================================================== launchers ======
 
@@ -540,13 +540,16 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
     }
     if (a.dhidden) {
       const int nsp = s1 - s0;
-      const int rest8 = cdiv(nht * nsp, 8) * 8;
-      if (small)
-        RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<32, 1, 4>), rest8 * nt, st, a.gtv, p.ldg, a.weight, T,
-                   H, V, v0, p.split_w, nsp, s0, nt, nht, a.part);
-      else
-        RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<256, 2, 2>), rest8 * nt, st, a.gtv, p.ldg, a.weight,
-                   T, H, V, v0, p.split_w, nsp, s0, nt, nht, a.part);
+      if (small) {
+        const int nh = cdiv(H, 128);
+        const int per = cdiv(nt * nh * nsp, 8);
+        RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<32, 128, 1, 4>), 8 * per, st, a.gtv, p.ldg, a.weight,
+                   T, H, V, v0, p.split_w, nsp, s0, nt, nh, per, a.part);
+      } else {
+        const int per = cdiv(nt * nht * nsp, 8);
+        RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<256, 256, 2, 2>), 8 * per, st, a.gtv, p.ldg, a.weight,
+                   T, H, V, v0, p.split_w, nsp, s0, nt, nht, per, a.part);
+      }
     }
   }
   if (a.dhidden) {

@@ -71,7 +71,8 @@ def bwd(lib, hidden=P, weight=P, targets=P, T=4, H=64, V=100, vs=0, vt=None, sta
 
 @pytest.mark.parametrize("kw,code", [
     (dict(T=-1), INVALID), (dict(H=0), INVALID), (dict(V=0), INVALID),
-    (dict(H=96), SHAPE), (dict(H=65536 + 64), SHAPE), (dict(T=(1 << 24) + 1), SHAPE),
+    (dict(H=96), SHAPE), (dict(H=65536 + 64), SHAPE), (dict(T=(1 << 21) + 1), SHAPE),
+    (dict(V=(1 << 24) + 1, vt=(1 << 24) + 1), SHAPE),
     (dict(vs=-1), INVALID), (dict(vt=50), INVALID), (dict(vs=10, vt=105), INVALID),
     (dict(vt=(1 << 31)), INVALID),
     (dict(vs=5, vt=200, stats=P), INVALID),              # slice with logp/entropy requested
