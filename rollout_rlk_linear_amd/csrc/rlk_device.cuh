@@ -1,11 +1,9 @@
 // rlk_device.cuh — device building blocks for the gfx950 linear log-prob kernels.
 //
-// * An LDS-tiled bf16 MFMA mainloop (v_mfma_f32_16x16x32_bf16) that computes
-//   a BM x BN fp32 tile of A * B^T with K walked in ascending blocks of 32.
-//   Either operand may be stored K-contiguous ("row-major [rows][K]") or
-//   K-strided ("row-major [K][rows]"); K-strided operands are transposed in
-//   registers (8x8 blocks) on their way into LDS so that every MFMA fragment
-//   is one 16-byte LDS read.
+// * LDS-DMA fed bf16 MFMA mainloops (v_mfma_f32_16x16x32_bf16) computing a
+//   BM x BN fp32 tile with K walked in ascending steps of 32: AsyncGemm for
+//   two K-contiguous operands (A * B^T), AsyncGemmKN for a K-major B (A * B,
+//   fragments assembled by transposing LDS reads).
 // * The fixed-order reductions that make every output row independent of the
 //   batch: a 16-lane DPP tree, the (m, R, B, zy) merge algebra, bf16 RNE.
 //
@@ -24,12 +22,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 constexpr int kThreads = 256;  // 4 wave64 per workgroup
-constexpr int BK = 64;         // K extent of one LDS stage
-constexpr int LDK = BK + 8;    // padded LDS row, in bf16 elements (144 B): conflict-free
-                               // 16-byte fragment reads for 16 consecutive rows
 constexpr int GROUP = 256;     // vocabulary columns per group (one forward tile width)
-constexpr int CHUNK = 32;      // vocabulary columns per chunk (unit of the row statistics)
-constexpr int CHUNKS_PER_GROUP = GROUP / CHUNK;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -158,184 +151,6 @@ __device__ __forceinline__ void acc_row_block(const f32x4 (&acc)[MI][NJ], int i,
   }
 }
 
-// ------------------------------------------------------ global loads ----
-
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ void sts16(uint16_t* p, const u32x4& v) {
-  *reinterpret_cast<u32x4*>(p) = v;
-}
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-// One operand tile of ROWS rows x BK of K, staged global -> registers -> LDS.
-//   TRANS == false: element (r, k) at src[r * ld + k]  (K contiguous).
-//     Thread t moves the 16-byte piece (k = 8 (t % 8)) of rows t / 8 + 32 i.
-//   TRANS == true:  element (r, k) at src[k * ld + r]  (rows contiguous).
-//     Thread t moves the 8 x 8 block (k = 8 (t % 8) + 0..7, r = 8 (t / 8 + 32 i) + 0..7),
-//     transposing it in registers.
-// Rows >= rows_valid and k >= k_valid read as zero. For TRANS the row test is
-// per 8-row block (rows_valid must be a multiple of 8); for !TRANS the k test
-// is per 8-element piece (k_valid must be a multiple of 8).
-template <int ROWS, bool TRANS>
-struct OperandTile {
-  static_assert(ROWS % 32 == 0, "tile rows must be a multiple of 32");
-  static constexpr int NPIECE = TRANS ? 0 : ROWS * BK / 8 / kThreads;  // 16-B pieces per thread
-  static constexpr int NBLK = TRANS ? (ROWS / 8 * BK / 8 + kThreads - 1) / kThreads : 0;
-  static constexpr int NREG = TRANS ? NBLK * 8 : NPIECE;
-  u32x4 reg[NREG > 0 ? NREG : 1];
-
-  __device__ __forceinline__ void load(const uint16_t* src, int64_t ld, int rows_valid, int k0,
-                                       int k_valid, int tid) {
-    if constexpr (!TRANS) {
-      const int c = tid & 7;
-      const int k = k0 + 8 * c;
-#pragma unroll
-      for (int i = 0; i < NPIECE; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        if (r < rows_valid && k < k_valid)
-          reg[i] = ldg16(src + (int64_t)r * ld + k);
-        else
-          reg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    } else {
-      const int kb = tid & 7;
-#pragma unroll
-      for (int bi = 0; bi < NBLK; ++bi) {
-        const int rb = (tid >> 3) + 32 * bi;
-        const bool rows_ok = (rb < ROWS / 8) && (8 * rb + 8 <= rows_valid);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int k = k0 + 8 * kb + j;
-          if (rows_ok && k < k_valid)
-            reg[bi * 8 + j] = ldg16(src + (int64_t)k * ld + 8 * rb);
-          else
-            reg[bi * 8 + j] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  }
-
-  // Write the registers into an LDS stage laid out [ROWS][LDK] (K contiguous).
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    if constexpr (!TRANS) {
-      const int c = tid & 7;
-#pragma unroll
-      for (int i = 0; i < NPIECE; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        sts16(lds + r * LDK + 8 * c, reg[i]);
-      }
-    } else {
-      const int kb = tid & 7;
-#pragma unroll
-      for (int bi = 0; bi < NBLK; ++bi) {
-        const int rb = (tid >> 3) + 32 * bi;
-        if (rb >= ROWS / 8) continue;
-        // in[j] holds rows 8rb..8rb+7 at k = 8kb + j (two rows per dword);
-        // out[q] holds k = 8kb..8kb+7 at row 8rb + q (two k per dword).
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          u32x4 o;
-          const int dw = q >> 1;
-          const int sh = (q & 1) * 16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = (reg[bi * 8 + 2 * e][dw] >> sh) & 0xffffu;
-            const uint32_t hi = (reg[bi * 8 + 2 * e + 1][dw] >> sh) & 0xffffu;
-            o[e] = lo | (hi << 16);
-          }
-          sts16(lds + (8 * rb + q) * LDK + 8 * kb, o);
-        }
-      }
-    }
-  }
-};
-
-// C[BM x BN] (fp32, in registers) += A[BM x K] * B[BN x K]^T over k in
-// [k_begin, k_end), in ascending MFMA steps of 32 starting at k_begin. Waves
-// form a WM x WN grid; wave (wm, wn) owns rows wm*WTM.. and cols wn*WTN.. of
-// the tile. Accumulator layout (16x16 MFMA): acc[i][j][r] is element
-//   row = wm*WTM + 16 i + 4 (lane / 16) + r,   col = wn*WTN + 16 j + lane % 16.
-template <int BM, int BN, int WM, int WN, bool AT, bool BT>
-struct TileGemm {
-  static_assert(WM * WN == 4, "4 waves per workgroup");
-  static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int MI = WTM / 16, NJ = WTN / 16;
-  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
-  static constexpr int STAGE = (BM + BN) * LDK;        // bf16 elements per LDS stage
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;      // two stages
-
-  f32x4 acc[MI][NJ];
-
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  __device__ __forceinline__ void compute_stage(const uint16_t* As, const uint16_t* Bs, int wm,
-                                                int wn, int lane) {
-    const int fr = lane & 15;
-    const int fk = 8 * (lane >> 4);
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      bf16x8 af[MI], bfr[NJ];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) af[i] = lds_frag(As + (wm * WTM + 16 * i + fr) * LDK + kk * 32 + fk);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[j] = lds_frag(Bs + (wn * WTN + 16 * j + fr) * LDK + kk * 32 + fk);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  // A: base of the tile's row 0 (layout per AT), lda; a_rows valid rows.
-  // B: likewise. k is absolute: element k of the K-contiguous layout sits at
-  // column k, of the K-strided layout at row k.
-  __device__ __forceinline__ void run(uint16_t* lds, const uint16_t* A, int64_t lda, int a_rows,
-                                      const uint16_t* B, int64_t ldb, int b_rows, int k_begin,
-                                      int k_end) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = wave_id();
-    const int wm = wave % WM, wn = wave / WM;
-    OperandTile<BM, AT> ta;
-    OperandTile<BN, BT> tb;
-    const int nsteps = (k_end - k_begin + BK - 1) / BK;
-    if (nsteps <= 0) return;
-    ta.load(A, lda, a_rows, k_begin, k_end, tid);
-    tb.load(B, ldb, b_rows, k_begin, k_end, tid);
-    ta.store(lds, tid);
-    tb.store(lds + BM * LDK, tid);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      uint16_t* cur = lds + (s & 1) * STAGE;
-      uint16_t* nxt = lds + ((s + 1) & 1) * STAGE;
-      const bool more = s + 1 < nsteps;
-      if (more) {
-        ta.load(A, lda, a_rows, k_begin + (s + 1) * BK, k_end, tid);
-        tb.load(B, ldb, b_rows, k_begin + (s + 1) * BK, k_end, tid);
-      }
-      compute_stage(cur, cur + BM * LDK, wm, wn, lane);
-      if (more) {
-        ta.store(nxt, tid);
-        tb.store(nxt + BM * LDK, tid);
-      }
-      __syncthreads();
-    }
-  }
-};
-
-}  // namespace rlk
-
-namespace rlk {
-
 // ------------------------------------------------ async (LDS-DMA) mainloop
 //
 // gfx950 buffer loads can write straight into LDS: `buffer_load_dwordx4 ...
@@ -401,18 +216,24 @@ __device__ __forceinline__ void barrier_only() {
 // (element (r, k) at base[r * ld + k]). k runs over [k_begin, k_end) in
 // ascending MFMA steps of 32, starting at k_begin; (k_end - k_begin) must be
 // a multiple of 32 and every row must hold at least k_end elements past its
-// start. WM x WN waves (4 or 8, i.e. 256 or 512 threads); same accumulator
-// layout as TileGemm. With DB the fragments of stage s+1 are read from LDS
-// while the MFMAs of stage s run (two fragment register sets).
-template <int BM, int BN, int WM, int WN, bool DB = false>
+// start. WM x WN waves (4 or 8); wave (wm, wn) owns rows wm*WTM.. and
+// columns wn*WTN.. of the tile, and acc[i][j][r] is element
+// (row wm*WTM + 16 i + 4 (lane / 16) + r, col wn*WTN + 16 j + lane % 16).
+// NSTG slots (3 or 4) of LDS ring.
+//
+// run() is the whole loop for a workgroup of WM x WN waves. setup(),
+// issue(), wait_for() and compute() are its steps, for kernels that drive
+// several groups of waves through one barrier sequence: wait_for(s), then a
+// barrier, then issue(s + NST - 1) and compute(s).
+template <int BM, int BN, int WM, int WN, int NSTG = 4>
 struct AsyncGemm {
   static constexpr int NW = WM * WN;
-  static constexpr int NT = 64 * NW;                    // threads
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per tile");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row DMA blocks");
+  static_assert(NSTG == 3 || NSTG == 4, "3- or 4-slot ring");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NJ = WTN / 16;
-  static constexpr int NST = 4;
+  static constexpr int NST = NSTG;
   static constexpr int ROWB = 64;                       // bytes per staged row
   static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
   static constexpr int LDS_BYTES = NST * STAGE_BYTES;
@@ -422,6 +243,14 @@ struct AsyncGemm {
   static constexpr int NI_W_MIN = NI / NW;
 
   f32x4 acc[MI][NJ];
+  // loop state (wave-uniform except voff and foff)
+  unsigned char* lds_;
+  uint32_t lds0_;
+  i32x4 rsA_, rsB_;
+  int voff_[NI_W_MAX];
+  int foff_;
+  int wave_, wm_, wn_;
+  int k_begin_, nsteps_;
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -430,138 +259,119 @@ struct AsyncGemm {
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // lds: LDS_BYTES of shared memory (16-byte aligned).
-  // A, B: row 0 of the tile; lda, ldb in elements; a_rows, b_rows: valid rows (<= 0: none).
-  __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
-                                      int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
-                                      int k_begin, int k_end) {
+  // lds: LDS_BYTES of shared memory (16-byte aligned), this tile's ring.
+  // A, B: row 0 of the tile; lda, ldb in elements; a_rows, b_rows: valid
+  // rows (<= 0: none); wave: 0 .. NW-1 within the waves sharing the tile.
+  // Returns the number of k-steps.
+  __device__ __forceinline__ int setup(unsigned char* lds, const uint16_t* A, int64_t lda,
+                                       int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
+                                       int k_begin, int k_end, int wave) {
     const int lane = threadIdx.x & 63;
-    const int wave = wave_id();
-    const int wm = wave % WM, wn = wave / WM;
-    const int nsteps = (k_end - k_begin) / 32;
-    if (nsteps <= 0) return;
-
+    lds_ = lds;
+    lds0_ = lds_addr(lds);
+    wave_ = wave;
+    wm_ = wave % WM;
+    wn_ = wave / WM;
+    k_begin_ = k_begin;
+    nsteps_ = (k_end - k_begin) / 32;
     // buffer resources over the valid rows only (rows past them read as zero)
     const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
     const int br = b_rows < 0 ? 0 : (b_rows > BN ? BN : b_rows);
-    const i32x4 rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
-    const i32x4 rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
-    const uint32_t lds0 = lds_addr(lds);
+    rsA_ = make_rsrc(A, (uint32_t)(ar * lda * 2));
+    rsB_ = make_rsrc(B, (uint32_t)(br * ldb * 2));
     // lane -> (row within a 16-row block, logical 16-byte piece) of one DMA block
     const int drow = lane >> 2;
     const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);
-    int voff[NI_W_MAX];
 #pragma unroll
     for (int ii = 0; ii < NI_W_MAX; ++ii) {
       const int j = wave + NW * ii;
       if (j < NI_A)
-        voff[ii] = (int)((16 * j + drow) * lda * 2) + 16 * dpiece;
+        voff_[ii] = (int)((16 * j + drow) * lda * 2) + 16 * dpiece;
       else
-        voff[ii] = (int)((16 * (j - NI_A) + drow) * ldb * 2) + 16 * dpiece;
+        voff_[ii] = (int)((16 * (j - NI_A) + drow) * ldb * 2) + 16 * dpiece;
     }
-
-    auto issue = [&](int s) {
-      const uint32_t st = lds0 + (uint32_t)((s % NST) * STAGE_BYTES);
-      const int koff = (k_begin + 32 * s) * 2;
-#pragma unroll
-      for (int ii = 0; ii < NI_W_MAX; ++ii) {
-        const int j = wave + NW * ii;
-        if (j < NI) {
-          if (j < NI_A)
-            dma16(rsA, st + j * 1024, voff[ii], koff);
-          else
-            dma16(rsB, st + j * 1024, voff[ii], koff);
-        }
-      }
-    };
-
     // fragment read offset of this lane inside a 16-row block (swizzled)
-    const int frow = lane & 15;
-    const int fpiece = (lane >> 4) ^ ((lane >> 2) & 3);
-    const int foff = frow * ROWB + 16 * fpiece;
-    auto read_frags = [&](int s, bf16x8 (&af)[MI], bf16x8 (&bfr)[NJ]) {
-      const unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+    foff_ = (lane & 15) * ROWB + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
+    return nsteps_;
+  }
+
+  // DMA of stage s into slot s % NST.
+  __device__ __forceinline__ void issue(int s) {
+    const uint32_t st = lds0_ + (uint32_t)((s % NST) * STAGE_BYTES);
+    const int koff = (k_begin_ + 32 * s) * 2;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[i] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB + foff));
+    for (int ii = 0; ii < NI_W_MAX; ++ii) {
+      const int j = wave_ + NW * ii;
+      if (j < NI) {
+        if (j < NI_A)
+          dma16(rsA_, st + j * 1024, voff_[ii], koff);
+        else
+          dma16(rsB_, st + j * 1024, voff_[ii], koff);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void prologue() {
+    for (int s = 0; s < NST - 1 && s < nsteps_; ++s) issue(s);
+  }
+
+  // Wait until this wave's DMA of stage s has landed, given that stages up
+  // to min(s + NST - 2, last) have been issued and nothing else is pending.
+  __device__ __forceinline__ void wait_for(int s) {
+    const int last = s + NST - 2 < nsteps_ - 1 ? s + NST - 2 : nsteps_ - 1;
+    const int after = last - s;
+    if (after >= 3)
+      wait_vmcnt<3 * NI_W_MIN>();
+    else if (after == 2)
+      wait_vmcnt<2 * NI_W_MIN>();
+    else if (after == 1)
+      wait_vmcnt<NI_W_MIN>();
+    else
+      wait_vmcnt<0>();
+  }
+
+  // Fragments of stage s from LDS, then its MFMAs.
+  __device__ __forceinline__ void compute(int s) {
+    const unsigned char* st = lds_ + (s % NST) * STAGE_BYTES;
+    bf16x8 af[MI], bfr[NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      af[i] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * i) * ROWB + foff_));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      bfr[j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn_ * WTN + 16 * j) * ROWB + foff_));
+    // keep every fragment read ahead of the MFMAs (no load-wait-compute chains)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        bfr[j] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn * WTN + 16 * j) * ROWB + foff));
-      // keep every fragment read ahead of the MFMAs (no load-wait-compute chains)
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto mfmas = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ]) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    };
-    // wait until stage `want` has landed; stages up to `last` have been issued
-    auto wait_stage = [&](int want, int last) {
-      const int after = last - want;
-      if (after >= 3)
-        wait_vmcnt<3 * NI_W_MIN>();
-      else if (after == 2)
-        wait_vmcnt<2 * NI_W_MIN>();
-      else if (after == 1)
-        wait_vmcnt<NI_W_MIN>();
-      else
-        wait_vmcnt<0>();
-    };
-    auto last_of = [&](int s) { return s < nsteps - 1 ? s : nsteps - 1; };
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
 
-    if constexpr (!DB) {
-      // ring of 4 slots: stage s computes while s+1..s+3 are in flight; slot
-      // s-1 is refilled (with s+3) once every wave is past the barrier of
-      // stage s, which it reaches only after its MFMAs of s-1 consumed their reads
-      for (int s = 0; s < 3 && s < nsteps; ++s) issue(s);
-      for (int s = 0; s < nsteps; ++s) {
-        wait_stage(s, last_of(s + 2));
-        barrier_only();
-        if (s + 3 < nsteps) issue(s + 3);
-        bf16x8 af[MI], bfr[NJ];
-        read_frags(s, af, bfr);
-        mfmas(af, bfr);
-      }
-    } else {
-      // fragments of stage s+1 are read while the MFMAs of stage s run; slot
-      // s is refilled (with s+4) only after every wave has waited for its own
-      // reads of it (lgkmcnt(0)) and passed the barrier
-      auto step = [&](int s, bf16x8 (&afc)[MI], bf16x8 (&bfc)[NJ], bf16x8 (&afn)[MI],
-                      bf16x8 (&bfn)[NJ]) {
-        if (s + 1 < nsteps) {
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): stage s fragments are in registers
-          wait_stage(s + 1, last_of(s + 3));
-          barrier_only();
-          if (s + NST < nsteps) issue(s + NST);
-          read_frags(s + 1, afn, bfn);
-        }
-        mfmas(afc, bfc);
-      };
-      for (int s = 0; s < NST && s < nsteps; ++s) issue(s);
-      wait_stage(0, last_of(NST - 1));
+  // The whole loop for one workgroup of NW waves: a ring of NST slots,
+  // stage s computes while s+1..s+NST-1 are in flight; slot s-1 is refilled
+  // (with s+NST-1) once every wave is past the barrier of stage s, which it
+  // reaches only after its MFMAs of s-1 consumed their reads.
+  __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
+                                      int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
+                                      int k_begin, int k_end) {
+    const int n = setup(lds, A, lda, a_rows, B, ldb, b_rows, k_begin, k_end, wave_id());
+    if (n <= 0) return;
+    prologue();
+    for (int s = 0; s < n; ++s) {
+      wait_for(s);
       barrier_only();
-      bf16x8 a0[MI], b0[NJ], a1[MI], b1[NJ];
-      read_frags(0, a0, b0);
-      int s = 0;
-      for (; s + 1 < nsteps; s += 2) {
-        step(s, a0, b0, a1, b1);
-        step(s + 1, a1, b1, a0, b0);
-      }
-      if (s < nsteps) step(s, a0, b0, a1, b1);
+      if (s + NST - 1 < n) issue(s + NST - 1);
+      compute(s);
     }
     // all DMA done and every wave past its last fragment read: LDS is free
     wait_vmcnt<0>();
     __syncthreads();
   }
 };
-
-}  // namespace rlk
-
-namespace rlk {
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
@@ -570,7 +380,7 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 // C[BM x BN] += A[BM x K] * B[K x BN] with A K-contiguous (element (r, k) at
 // A[r * lda + k]) and B K-major (element (k, n) at B[k * ldb + n]): the
 // contraction over the vocabulary, where B is W in its natural layout.
-// A is staged as in AsyncGemm. A B stage is 32 rows k of BN columns copied
+// A is staged as in AsyncGemm (same accumulator layout). A B stage is 32 rows k of BN columns copied
 // verbatim by LDS-DMA, the 16-byte pieces of row k permuted by XOR with
 // 2 (k % 4) + 8 ((k / 8) % 2), which spreads the transposing reads below
 // over all banks. The MFMA B fragment (lane l: column l % 16, k = 8 (l / 16)

@@ -20,6 +20,16 @@ constexpr int kMaxSplits = 8;
 constexpr int kSplitCols = 16384;
 // Soft bound on the elements of one bf16 logit-gradient chunk (T x columns).
 constexpr int64_t kChunkElems = int64_t(1) << 27;
+// Columns h of one dW tile (the tile is 256 v x kDwBN h).
+constexpr int kDwBN = 128;
+
+// Assignment of dW tiles to XCDs: `groups` sets of XCDs, each owning
+// h_per_group h-tiles; the 8 / groups XCDs of a set split the v-tiles,
+// v_per_xcd each; per_xcd workgroups per XCD.
+struct DwMap {
+  int groups, h_per_group, v_per_xcd, per_xcd;
+};
+DwMap dw_map(int n_vtiles, int n_htiles);
 
 struct FwdArgs {
   const uint16_t* hidden;

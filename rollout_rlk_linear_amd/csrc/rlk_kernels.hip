@@ -336,41 +336,59 @@ __global__ __launch_bounds__(kThreads) void transpose_hidden_kernel(
 }
 
 // dW[chunk_v0 + v, h] = sum_t G[t, v] h[t, h] = sum_t gvt[v][t] hT[h][t];
-// tile 256 (v) x 256 (h), K = Tp (rows t >= T are zeros in both operands).
-__global__ __launch_bounds__(kThreads) void bwd_dw_kernel(
-    const uint16_t* __restrict__ gvt, const uint16_t* __restrict__ hT, int Tp, int H, int V,
-    int chunk_v0, int chunk_w, int n_vtiles, int n_htiles, float* __restrict__ dweight) {
-  using Gm = AsyncGemm<256, 256, 2, 2>;
+// tile 256 (v) x kDwBN (h), K = Tp (rows t >= T are zeros in both operands).
+// With K as short as one batch, the tile's fp32 output takes about as long
+// to write as its MFMAs take to run. The tile is sized for two workgroups
+// per CU (3-slot ring: 72 KB of LDS, 128 accumulators per lane) so that one
+// can compute while the other writes, and the stores are non-temporal. The
+// h-tiles are split into groups of at most 8, one group per set of XCDs,
+// and the XCDs of a set split the v-tiles: an XCD keeps its 8 h^T tiles in
+// L2 and its ~64 resident workgroups share 8 G^T tiles, so the operands stay
+// in L2 while the output streams past.
+DwMap dw_map(int n_vtiles, int n_htiles) {
+  DwMap m;
+  const int need = (n_htiles + 7) / 8;
+  m.groups = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  m.h_per_group = (n_htiles + m.groups - 1) / m.groups;
+  m.v_per_xcd = (n_vtiles + 8 / m.groups - 1) / (8 / m.groups);
+  m.per_xcd = m.v_per_xcd * m.h_per_group;
+  return m;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+bwd_dw_kernel(const uint16_t* __restrict__ gvt, const uint16_t* __restrict__ hT, int Tp, int H,
+              int V, int chunk_v0, int chunk_w, int n_vtiles, int n_htiles, DwMap map,
+              float* __restrict__ dweight) {
+  using Gm = AsyncGemm<256, kDwBN, 2, 2, 3>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
-  // h-tiles fastest within an XCD: one G^T tile stays hot in L2 for all of H
-  int vt, ht;
-  {
-    const int b = blockIdx.x;
-    const int xcd = b & 7, seq = b >> 3;
-    vt = xcd + 8 * (seq / n_htiles);
-    ht = seq % n_htiles;
-  }
+  const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
+  if (seq >= map.per_xcd) return;
+  const int ht = (xcd % map.groups) * map.h_per_group + seq % map.h_per_group;
+  const int vt = (xcd / map.groups) * map.v_per_xcd + seq / map.h_per_group;
+  if (ht >= n_htiles) return;
   if (vt >= n_vtiles) return;
-  const int v0 = vt * 256, h0 = ht * 256;
+  const int v0 = vt * 256, h0 = ht * kDwBN;
   Gm gm;
   gm.zero();
   gm.run(lds, gvt + (int64_t)v0 * Tp, Tp, chunk_w - v0, hT + (int64_t)h0 * Tp, Tp, H - h0, 0, Tp);
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % 2, wn = wave / 2;
+  // rows past the chunk or the vocabulary are skipped per lane; a 16-column
+  // block is whole or absent (H is a multiple of 64), a wave-uniform test
+  const int vlim = min(chunk_w, V - chunk_v0);
+  const int hb = h0 + wn * Gm::WTN;
+  float* const base = dweight + (int64_t)chunk_v0 * H + hb + (lane & 15);
 #pragma unroll
   for (int i = 0; i < Gm::MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int vl = v0 + wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
-      const int64_t v = (int64_t)chunk_v0 + vl;
-      if (vl >= chunk_w || v >= V) continue;
-      float* rowp = dweight + v * H;
+      if (vl >= vlim) continue;
+      float* rowp = base + (int64_t)vl * H;
 #pragma unroll
-      for (int j = 0; j < Gm::NJ; ++j) {
-        const int h = h0 + wn * Gm::WTN + 16 * j + (lane & 15);
-        if (h < H) rowp[h] = gm.acc[i][j][r];
-      }
+      for (int j = 0; j < Gm::NJ; ++j)
+        if (hb + 16 * j < H) __builtin_nontemporal_store(gm.acc[i][j][r], rowp + 16 * j);
     }
   }
 }
@@ -406,7 +424,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
-  float* out = part + (int64_t)(split_base + si) * T * H;
+  // a 16-column block is whole or absent (H is a multiple of 64): wave-uniform test
+  const int hb = h0 + wn * Gm::WTN;
+  float* const out = part + (int64_t)(split_base + si) * T * H + hb + (lane & 15);
 #pragma unroll
   for (int i = 0; i < Gm::MI; ++i) {
 #pragma unroll
@@ -415,10 +435,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
       if (t >= T) continue;
       float* rowp = out + (int64_t)t * H;
 #pragma unroll
-      for (int j = 0; j < Gm::NJ; ++j) {
-        const int h = h0 + wn * Gm::WTN + 16 * j + (lane & 15);
-        if (h < H) rowp[h] = gm.acc[i][j][r];
-      }
+      for (int j = 0; j < Gm::NJ; ++j)
+        if (hb + 16 * j < H) rowp[16 * j] = gm.acc[i][j][r];
     }
   }
 }
@@ -534,9 +552,10 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
                  a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, gtv, p.ldg, gvt, Tp);
     if (a.dweight) {
       const int nvt = cdiv(width, 256);
-      const int nvt8 = cdiv(nvt, 8) * 8;
-      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, nvt8 * nht, st, a.gvt, a.hT, Tp, H, V, v0,
-                 ngroups * GROUP, nvt, nht, a.dweight);
+      const int nhw = cdiv(H, kDwBN);
+      const DwMap map = dw_map(nvt, nhw);
+      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, 8 * map.per_xcd, st, a.gvt, a.hT, Tp, H, V, v0,
+                 ngroups * GROUP, nvt, nhw, map, a.dweight);
     }
     if (a.dhidden) {
       const int nsp = s1 - s0;
