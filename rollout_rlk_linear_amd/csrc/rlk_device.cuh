@@ -156,9 +156,9 @@ __device__ __forceinline__ void acc_row_block(const f32x4 (&acc)[MI][NJ], int i,
 // gfx950 buffer loads can write straight into LDS: `buffer_load_dwordx4 ...
 // lds` stores lane i's 16 bytes at (LDS base + 16 i), so one instruction
 // fills 1 KB. Operand rows are staged as 64-byte rows (32 bf16 = one MFMA
-// k-step) in a ring of four stages; the 16-byte pieces of row r are stored
-// XOR-swizzled, piece c at slot c ^ ((r >> 2) & 3), which keeps the 16-row
-// fragment reads free of bank conflicts. Rows past the valid range read as
+// k-step) in a ring of stages; the 16-byte pieces of each row are stored
+// XOR-permuted (row_swz below), which keeps the 16-row fragment reads free
+// of bank conflicts. Rows past the valid range read as
 // zero through the buffer's hardware range check (num_records), the k offset
 // of a stage travels in the scalar offset, so the steady-state loop issues
 // no vector ALU work for addressing and holds no staging registers.
@@ -181,6 +181,12 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
 }
+
+// Piece permutation of a staged 64-byte row: row r (within its 16-row block)
+// keeps logical 16-byte piece c at slot c ^ row_swz(r). A fragment read
+// (lane l: row l % 16, piece l / 16) then touches distinct banks whether the
+// LDS serves 16 lanes over 64 banks or 8 lanes over 32 banks per cycle.
+__device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // One 1 KB LDS-DMA block: lane i's 16 bytes from (base + voff + soff) land at
 // LDS (addr + 16 i). Written as inline asm so that the compiler does not
@@ -281,7 +287,7 @@ struct AsyncGemm {
     rsB_ = make_rsrc(B, (uint32_t)(br * ldb * 2));
     // lane -> (row within a 16-row block, logical 16-byte piece) of one DMA block
     const int drow = lane >> 2;
-    const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);
+    const int dpiece = (lane & 3) ^ row_swz(lane >> 2);
 #pragma unroll
     for (int ii = 0; ii < NI_W_MAX; ++ii) {
       const int j = wave + NW * ii;
@@ -291,22 +297,30 @@ struct AsyncGemm {
         voff_[ii] = (int)((16 * (j - NI_A) + drow) * ldb * 2) + 16 * dpiece;
     }
     // fragment read offset of this lane inside a 16-row block (swizzled)
-    foff_ = (lane & 15) * ROWB + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
+    foff_ = (lane & 15) * ROWB + 16 * ((lane >> 4) ^ row_swz(lane & 15));
     return nsteps_;
   }
 
-  // DMA of stage s into slot s % NST.
+  // DMA of stage s into slot s % NST. When the A blocks divide evenly among
+  // the waves, which operand block ii of a wave belongs to is known at
+  // compile time (block wave + NW ii is an A block iff ii < NI_A / NW).
   __device__ __forceinline__ void issue(int s) {
-    const uint32_t st = lds0_ + (uint32_t)((s % NST) * STAGE_BYTES);
+    const uint32_t st = lds0_ + (uint32_t)((s % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave_;
     const int koff = (k_begin_ + 32 * s) * 2;
+    if constexpr (NI_A % NW == 0 && NI % NW == 0) {
 #pragma unroll
-    for (int ii = 0; ii < NI_W_MAX; ++ii) {
-      const int j = wave_ + NW * ii;
-      if (j < NI) {
-        if (j < NI_A)
-          dma16(rsA_, st + j * 1024, voff_[ii], koff);
-        else
-          dma16(rsB_, st + j * 1024, voff_[ii], koff);
+      for (int ii = 0; ii < NI / NW; ++ii)
+        dma16(ii < NI_A / NW ? rsA_ : rsB_, st + 1024u * NW * ii, voff_[ii], koff);
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < NI_W_MAX; ++ii) {
+        const int j = wave_ + NW * ii;
+        if (j < NI) {
+          if (j < NI_A)
+            dma16(rsA_, st + 1024u * NW * ii, voff_[ii], koff);
+          else
+            dma16(rsB_, st + 1024u * NW * ii, voff_[ii], koff);
+        }
       }
     }
   }
@@ -316,10 +330,96 @@ struct AsyncGemm {
   }
 
   // Wait until this wave's DMA of stage s has landed, given that stages up
-  // to min(s + NST - 2, last) have been issued and nothing else is pending.
-  __device__ __forceinline__ void wait_for(int s) {
-    const int last = s + NST - 2 < nsteps_ - 1 ? s + NST - 2 : nsteps_ - 1;
-    const int after = last - s;
+  // to s + NST - 2 (clamped) have been issued and nothing else is pending.
+  __device__ __forceinline__ void wait_for(int s) { wait_until(s, s + NST - 2); }
+
+  // Fragments of stage s from LDS, then its MFMAs. All B fragments and the
+  // first two A fragments are read up front; A fragment i+2 is read while
+  // the MFMAs of row block i run, so most of the LDS reads overlap MFMAs.
+  __device__ __forceinline__ void compute(int s) {
+    const unsigned char* st = lds_ + (s % NST) * STAGE_BYTES;
+    bf16x8 af[MI], bfr[NJ];
+    constexpr int A0 = MI < 2 ? MI : 2;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      bfr[j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn_ * WTN + 16 * j) * ROWB + foff_));
+#pragma unroll
+    for (int i = 0; i < A0; ++i)
+      af[i] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * i) * ROWB + foff_));
+    __builtin_amdgcn_sched_group_barrier(0x100, NJ + A0, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (i + A0 < MI)
+        af[i + A0] = __builtin_bit_cast(
+            bf16x8,
+            *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * (i + A0)) * ROWB + foff_));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      if (i + A0 < MI) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // the next A read
+        __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);  // the rest of the row
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
+      }
+    }
+  }
+
+  // Fragments of stage s from LDS into registers (no wait).
+  __device__ __forceinline__ void read_frags(int s, bf16x8 (&af)[MI], bf16x8 (&bfr)[NJ]) const {
+    const unsigned char* st = lds_ + (s % NST) * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      af[i] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * i) * ROWB + foff_));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      bfr[j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn_ * WTN + 16 * j) * ROWB + foff_));
+  }
+
+  __device__ __forceinline__ void mfmas(const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+
+  // One workgroup of NW waves with fragment double-buffering: the fragments
+  // of stage s+1 are read from LDS while the MFMAs of stage s run. Before the
+  // barrier of step s every wave has its stage-s fragments in registers
+  // (lgkmcnt(0)), so after it slot s may be refilled: stage s+NST is issued
+  // there, NST-1 stages ahead of the one being read.
+  __device__ __forceinline__ void run_db(unsigned char* lds, const uint16_t* A, int64_t lda,
+                                         int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
+                                         int k_begin, int k_end) {
+    const int n = setup(lds, A, lda, a_rows, B, ldb, b_rows, k_begin, k_end, wave_id());
+    if (n <= 0) return;
+    prologue();
+    if (NST - 1 < n) issue(NST - 1);
+    wait_until(0, NST - 1);
+    barrier_only();
+    bf16x8 a0[MI], b0[NJ], a1[MI], b1[NJ];
+    read_frags(0, a0, b0);
+    int s = 0;
+    for (; s + 1 < n; s += 2) {
+      step_db(s, n, a0, b0, a1, b1);
+      step_db(s + 1, n, a1, b1, a0, b0);
+    }
+    if (s < n) step_db(s, n, a0, b0, a1, b1);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  // Wait for this wave's DMA of stage `want` when stages up to `last`
+  // (clamped to the final stage) have been issued and nothing else is pending.
+  __device__ __forceinline__ void wait_until(int want, int last) {
+    last = last < nsteps_ - 1 ? last : nsteps_ - 1;
+    const int after = last - want;
     if (after >= 3)
       wait_vmcnt<3 * NI_W_MIN>();
     else if (after == 2)
@@ -330,25 +430,18 @@ struct AsyncGemm {
       wait_vmcnt<0>();
   }
 
-  // Fragments of stage s from LDS, then its MFMAs.
-  __device__ __forceinline__ void compute(int s) {
-    const unsigned char* st = lds_ + (s % NST) * STAGE_BYTES;
-    bf16x8 af[MI], bfr[NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      af[i] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * i) * ROWB + foff_));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      bfr[j] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn_ * WTN + 16 * j) * ROWB + foff_));
-    // keep every fragment read ahead of the MFMAs (no load-wait-compute chains)
+  __device__ __forceinline__ void step_db(int s, int n, const bf16x8 (&ac)[MI],
+                                          const bf16x8 (&bc)[NJ], bf16x8 (&an)[MI],
+                                          bf16x8 (&bn)[NJ]) {
+    if (s + 1 < n) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): stage-s fragments are in registers
+      wait_until(s + 1, s + NST - 1);
+      barrier_only();
+      if (s + NST < n) issue(s + NST);
+      read_frags(s + 1, an, bn);
+    }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    mfmas(ac, bc);
   }
 
   // The whole loop for one workgroup of NW waves: a ring of NST slots,
@@ -439,7 +532,7 @@ struct AsyncGemmKN {
     const uint32_t lds0 = lds_addr(lds);
 
     const int drow = lane >> 2;
-    const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);
+    const int dpiece = (lane & 3) ^ row_swz(lane >> 2);
     const int brow = lane / PPR, bslot = lane % PPR;
     int voff[NI_W_MAX];
 #pragma unroll
@@ -473,7 +566,7 @@ struct AsyncGemmKN {
       }
     };
 
-    const int foff = (lane & 15) * ROWB_A + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
+    const int foff = (lane & 15) * ROWB_A + 16 * ((lane >> 4) ^ row_swz(lane & 15));
     // transposing reads: 16-lane group g, source lane sl; read q covers rows
     // 8 g + 4 q + sl / 4 at columns n0 + 4 (sl % 4) .. + 3
     const int g = lane >> 4, sl = lane & 15;
