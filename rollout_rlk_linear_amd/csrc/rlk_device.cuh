@@ -336,10 +336,18 @@ struct AsyncGemm {
   // Fragments of stage s from LDS, then its MFMAs. All B fragments and the
   // first two A fragments are read up front; A fragment i+2 is read while
   // the MFMAs of row block i run, so most of the LDS reads overlap MFMAs.
-  __device__ __forceinline__ void compute(int s) {
+  // If dma_stage >= 0 its DMA blocks are issued one per row block, between
+  // the MFMAs (its slot must already be free).
+  __device__ __forceinline__ void compute(int s, int dma_stage = -1) {
     const unsigned char* st = lds_ + (s % NST) * STAGE_BYTES;
     bf16x8 af[MI], bfr[NJ];
     constexpr int A0 = MI < 2 ? MI : 2;
+    constexpr bool SPLIT = NI_A % NW == 0 && NI % NW == 0 && NI / NW <= MI;
+    if constexpr (!SPLIT) {
+      if (dma_stage >= 0) issue(dma_stage);
+    }
+    const uint32_t dst = lds0_ + (uint32_t)((dma_stage % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave_;
+    const int koff = (k_begin_ + 32 * dma_stage) * 2;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       bfr[j] = __builtin_bit_cast(
@@ -364,6 +372,10 @@ struct AsyncGemm {
         __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);  // the rest of the row
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
+      }
+      if constexpr (SPLIT) {
+        if (i < NI / NW && dma_stage >= 0)
+          dma16(i < NI_A / NW ? rsA_ : rsB_, dst + 1024u * NW * i, voff_[i], koff);
       }
     }
   }
@@ -457,8 +469,7 @@ struct AsyncGemm {
     for (int s = 0; s < n; ++s) {
       wait_for(s);
       barrier_only();
-      if (s + NST - 1 < n) issue(s + NST - 1);
-      compute(s);
+      compute(s, s + NST - 1 < n ? s + NST - 1 : -1);
     }
     // all DMA done and every wave past its last fragment read: LDS is free
     wait_vmcnt<0>();
@@ -593,30 +604,66 @@ struct AsyncGemmKN {
     };
     auto last_of = [&](int s) { return s < nsteps - 1 ? s : nsteps - 1; };
 
-    // same 4-slot ring as AsyncGemm
+    // The DMA blocks of the stage being refilled go out one per MFMA row
+    // block when they divide evenly (which operand each is: compile time).
+    constexpr bool SPLIT = NI_A % NW == 0 && NI % NW == 0 && NI / NW <= MI;
+    auto issue_block = [&](int ii, uint32_t dst, int k0, const i32x4& rsB) {
+      if (ii < NI_A / NW)
+        dma16(rsA, dst + 1024u * NW * ii, voff[ii], k0 * 2);
+      else
+        dma16(rsB, dst + 1024u * NW * ii, voff[ii], 0);
+    };
+    auto stage_rsrc_b = [&](int k0) {
+      int brows = kb_valid - k0;
+      brows = brows < 0 ? 0 : (brows > 32 ? 32 : brows);
+      const uint32_t bbytes = brows > 0 ? (uint32_t)(((brows - 1) * ldb + nb_valid) * 2) : 0u;
+      return make_rsrc(B + (int64_t)k0 * ldb, bbytes);
+    };
+
+    // same 4-slot ring as AsyncGemm; A fragments read two row blocks ahead
     for (int s = 0; s < 3 && s < nsteps; ++s) issue(s);
     for (int s = 0; s < nsteps; ++s) {
       wait_stage(s, last_of(s + 2));
       barrier_only();
-      if (s + 3 < nsteps) issue(s + 3);
+      const bool refill = s + 3 < nsteps;
+      if (!SPLIT && refill) issue(s + 3);
+      const int k3 = k_begin + 32 * (s + 3);
+      const uint32_t dst = lds0 + (uint32_t)(((s + 3) % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave;
+      const i32x4 rsB3 = stage_rsrc_b(k3);
       unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+      constexpr int A0 = MI < 2 ? MI : 2;
       bf16x8 af[MI], bfr[NJ];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[i] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB_A + foff));
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[0][j]));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[1][j]));
         bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < A0; ++i)
+        af[i] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB_A + foff));
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + A0, 0);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        if (i + A0 < MI)
+          af[i + A0] = __builtin_bit_cast(
+              bf16x8,
+              *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * (i + A0)) * ROWB_A + foff));
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        if (i + A0 < MI) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
+        }
+        if constexpr (SPLIT) {
+          if (i < NI / NW && refill) issue_block(i, dst, k3, rsB3);
+        }
+      }
     }
     wait_vmcnt<0>();
     __syncthreads();
