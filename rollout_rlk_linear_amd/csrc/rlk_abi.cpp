@@ -85,7 +85,7 @@ namespace rlk {
 
 const char* const kKernelNames[K_COUNT] = {
     "fwd_tile", "fwd_combine", "bwd_rowprep", "bwd_recompute",
-    "bwd_dw",   "bwd_dh",      "bwd_dh_reduce", "fill_zero", "bwd_transpose"};
+    "bwd_dw",   "bwd_dh",      "bwd_dh_reduce", "fill_zero"};
 
 void prof_before(int id, hipStream_t st) {
   if (!g_prof.on.load(std::memory_order_relaxed)) return;
@@ -127,9 +127,8 @@ BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh) {
   if (S > kMaxSplits) S = kMaxSplits;
   p.split_w = (int)round_up(ceil_div(Vp, S), 256);
   p.nsplits = (int)ceil_div(Vp, p.split_w);
-  // dW walks K = Tp in steps of 32; the recompute tiles (32 rows for small
-  // batches, 256 otherwise) cover [0, Tp) so its zero rows are always written
-  p.Tp = round_up(T > 0 ? T : 1, T <= kSmallT ? 32 : 64);
+  // dW walks K = t over [0, Tp) in steps of 32 (rows t >= T read as zero)
+  p.Tp = round_up(T > 0 ? T : 1, 32);
   int64_t spc = kChunkElems / (p.Tp * p.split_w);
   if (spc < 1) spc = 1;
   if (spc > p.nsplits) spc = p.nsplits;
@@ -137,10 +136,8 @@ BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh) {
   p.nchunks = (int)ceil_div(p.nsplits, spc);
   p.ldg = spc * p.split_w;
   p.off_rowc = 0;
-  p.off_hT = align256(size_t(p.Tp) * 32);
-  p.off_gtv = align256(p.off_hT + size_t(H) * size_t(p.Tp) * 2);
-  p.off_gvt = align256(p.off_gtv + size_t(p.Tp) * size_t(p.ldg) * 2);
-  p.off_part = align256(p.off_gvt + size_t(p.ldg) * size_t(p.Tp) * 2);
+  p.off_gtv = align256(size_t(p.Tp) * 32);
+  p.off_part = align256(p.off_gtv + size_t(p.Tp) * size_t(p.ldg) * 2);
   p.total = align256(p.off_part + (want_dh ? size_t(p.nsplits) * size_t(T) * size_t(H) * 4 : 0));
   return p;
 }
@@ -256,9 +253,7 @@ RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
   a.dh_f32 = (flags & RLK_DH_F32) ? 1 : 0;
   a.dweight = dweight;
   a.rowc = reinterpret_cast<float4*>(ws + plan.off_rowc);
-  a.hT = reinterpret_cast<uint16_t*>(ws + plan.off_hT);
   a.gtv = reinterpret_cast<uint16_t*>(ws + plan.off_gtv);
-  a.gvt = reinterpret_cast<uint16_t*>(ws + plan.off_gvt);
   a.part = reinterpret_cast<float*>(ws + plan.off_part);
   if (rlk::launch_bwd(a, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return RLK_ERR_HIP;
   g_calls[1].fetch_add(1, std::memory_order_relaxed);

@@ -671,3 +671,174 @@ struct AsyncGemmKN {
 };
 
 }  // namespace rlk
+
+namespace rlk {
+
+// C[BM x BN] += A^T B with both operands K-major: element (k, m) of A at
+// A[k * lda + m] and element (k, n) of B at B[k * ldb + n] (e.g. dW = G^T h
+// with G stored [t][v] and h stored [t][h], contracting over t). Each stage is
+// 32 rows k of A (BM columns) and of B (BN columns), copied verbatim by
+// LDS-DMA with the 16-byte pieces of row k permuted as in AsyncGemmKN; both
+// MFMA fragments come from transposing reads (lane i of a 16-lane group
+// receives rows k0..k0+3 of column n0 + i). k runs over [k_begin, k_end) in
+// ascending MFMA steps of 32 (the span a multiple of 32). Rows at or past
+// ka_valid / kb_valid read as zero, and so do columns at or past na_valid /
+// nb_valid in the last valid row; other columns past them read what follows
+// in memory and only reach outputs the caller discards. WM x WN = 4 waves,
+// same accumulator layout as AsyncGemm (rows = A columns, cols = B columns).
+template <int BM, int BN, int WM, int WN, int NSTG>
+struct AsyncGemmKK {
+  static constexpr int NW = WM * WN;
+  static_assert(NW == 4, "4 waves per workgroup");
+  static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "rows of 256 or 512 bytes");
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int MI = WTM / 16, NJ = WTN / 16;
+  static constexpr int NST = NSTG;
+  static_assert(NST >= 2 && NST <= 4, "2- to 4-slot ring");
+  static constexpr int ROWB_A = BM * 2, ROWB_B = BN * 2;
+  static constexpr int PPR_A = BM / 8, RPB_A = 64 / PPR_A;  // pieces per row, rows per 1 KB block
+  static constexpr int PPR_B = BN / 8, RPB_B = 64 / PPR_B;
+  static constexpr int STAGE_A = 32 * ROWB_A, STAGE_B = 32 * ROWB_B;
+  static constexpr int STAGE_BYTES = STAGE_A + STAGE_B;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+  static constexpr int NI_A = STAGE_A / 1024, NI_B = STAGE_B / 1024, NI = NI_A + NI_B;
+  static_assert(NI_A % NW == 0 && NI % NW == 0, "DMA blocks divide among the waves");
+  static constexpr int NB = NI / NW;  // DMA blocks per wave per stage
+  static_assert(NB <= MI, "one DMA block per MFMA row block");
+
+  f32x4 acc[MI][NJ];
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  static __device__ __forceinline__ int bswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+  // Resource over rows [k0, k0 + 32) of a K-major operand: rows at or past
+  // k_valid, and columns at or past n_valid in the last valid row, read zero.
+  static __device__ __forceinline__ i32x4 stage_rsrc(const uint16_t* base, int64_t ld, int k0,
+                                                     int k_valid, int n_valid) {
+    int rows = k_valid - k0;
+    rows = rows < 0 ? 0 : (rows > 32 ? 32 : rows);
+    const uint32_t bytes = rows > 0 ? (uint32_t)(((rows - 1) * ld + n_valid) * 2) : 0u;
+    return make_rsrc(base + (int64_t)k0 * ld, bytes);
+  }
+
+  __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
+                                      int ka_valid, int na_valid, const uint16_t* B, int64_t ldb,
+                                      int kb_valid, int nb_valid, int k_begin, int k_end) {
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int wm = wave % WM, wn = wave / WM;
+    const int nsteps = (k_end - k_begin) / 32;
+    if (nsteps <= 0) return;
+    const uint32_t lds0 = lds_addr(lds);
+
+    // DMA: block j of a stage holds rows RPB j + lane / PPR, lane % PPR the
+    // physical piece slot, loading logical piece slot ^ bswz(row)
+    int voff[NB];
+#pragma unroll
+    for (int ii = 0; ii < NB; ++ii) {
+      const int j = wave + NW * ii;
+      if (ii < NI_A / NW) {
+        const int k = RPB_A * j + lane / PPR_A;
+        voff[ii] = (int)(k * lda * 2) + 16 * ((lane % PPR_A) ^ bswz(k));
+      } else {
+        const int k = RPB_B * (j - NI_A) + lane / PPR_B;
+        voff[ii] = (int)(k * ldb * 2) + 16 * ((lane % PPR_B) ^ bswz(k));
+      }
+    }
+    auto issue_block = [&](int ii, uint32_t dst, const i32x4& ra, const i32x4& rb) {
+      dma16(ii < NI_A / NW ? ra : rb, dst + 1024u * NW * ii, voff[ii], 0);
+    };
+    auto stage_dst = [&](int s) {
+      return lds0 + (uint32_t)((s % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave;
+    };
+    auto issue = [&](int s) {
+      const int k0 = k_begin + 32 * s;
+      const i32x4 ra = stage_rsrc(A, lda, k0, ka_valid, na_valid);
+      const i32x4 rb = stage_rsrc(B, ldb, k0, kb_valid, nb_valid);
+#pragma unroll
+      for (int ii = 0; ii < NB; ++ii) issue_block(ii, stage_dst(s), ra, rb);
+    };
+
+    // transposing reads: 16-lane group g, source lane sl; read q covers rows
+    // 8 g + 4 q + sl / 4 at columns c0 + 4 (sl % 4) .. + 3
+    const int g = lane >> 4, sl = lane & 15;
+    uint32_t aoff[2][MI], boff[2][NJ];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = 8 * g + 4 * q + (sl >> 2);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int col = wm * WTM + 16 * i + 4 * (sl & 3);
+        aoff[q][i] = (uint32_t)(k * ROWB_A + 16 * ((col >> 3) ^ bswz(k)) + 2 * (col & 7));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = wn * WTN + 16 * j + 4 * (sl & 3);
+        boff[q][j] = (uint32_t)(STAGE_A + k * ROWB_B + 16 * ((col >> 3) ^ bswz(k)) + 2 * (col & 7));
+      }
+    }
+    auto frag = [&](const unsigned char* st, uint32_t o0, uint32_t o1) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + o0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + o1));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto wait_stage = [&](int want, int last) {
+      last = last < nsteps - 1 ? last : nsteps - 1;
+      const int after = last - want;
+      if (after >= 3)
+        wait_vmcnt<3 * NB>();
+      else if (after == 2)
+        wait_vmcnt<2 * NB>();
+      else if (after == 1)
+        wait_vmcnt<NB>();
+      else
+        wait_vmcnt<0>();
+    };
+
+    for (int s = 0; s < NST - 1 && s < nsteps; ++s) issue(s);
+    for (int s = 0; s < nsteps; ++s) {
+      wait_stage(s, s + NST - 2);
+      barrier_only();
+      // refill the slot of stage s-1 (every wave is past its reads) with
+      // stage s+NST-1, one DMA block per MFMA row block
+      const bool refill = s + NST - 1 < nsteps;
+      const int kr = k_begin + 32 * (s + NST - 1);
+      const i32x4 ra = stage_rsrc(A, lda, kr, ka_valid, na_valid);
+      const i32x4 rb = stage_rsrc(B, ldb, kr, kb_valid, nb_valid);
+      const uint32_t dst = stage_dst(s + NST - 1);
+      const unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+      constexpr int A0 = MI < 2 ? MI : 2;
+      bf16x8 af[MI], bfr[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bfr[j] = frag(st, boff[0][j], boff[1][j]);
+#pragma unroll
+      for (int i = 0; i < A0; ++i) af[i] = frag(st, aoff[0][i], aoff[1][i]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (NJ + A0), 0);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        if (i + A0 < MI) af[i + A0] = frag(st, aoff[0][i + A0], aoff[1][i + A0]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        if (i + A0 < MI) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
+        }
+        if (i < NB && refill) issue_block(i, dst, ra, rb);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+};
+
+}  // namespace rlk

@@ -19,7 +19,7 @@ constexpr int kSmallT = 64;
 constexpr int kMaxSplits = 8;
 constexpr int kSplitCols = 16384;
 // Soft bound on the elements of one bf16 logit-gradient chunk (T x columns).
-constexpr int64_t kChunkElems = int64_t(1) << 27;
+constexpr int64_t kChunkElems = int64_t(1) << 28;
 // Columns h of one dW tile (the tile is 256 v x kDwBN h).
 constexpr int kDwBN = 128;
 
@@ -50,8 +50,8 @@ struct BwdPlan {
   int splits_per_chunk;
   int nchunks;
   int64_t ldg;          // row stride of the G chunk buffer (columns)
-  int64_t Tp;           // T rounded up to the dW k-step granularity (32 or 64)
-  size_t off_rowc, off_hT, off_gtv, off_gvt, off_part, total;
+  int64_t Tp;           // T rounded up to the dW k-step (32)
+  size_t off_rowc, off_gtv, off_part, total;
 };
 
 struct BwdArgs {
@@ -67,9 +67,7 @@ struct BwdArgs {
   int dh_f32;
   float* dweight;
   float4* rowc;
-  uint16_t* hT;   // [H][Tp] transposed hidden (dW operand)
-  uint16_t* gtv;  // [Tp][ldg] logit gradient, rows t (dH operand)
-  uint16_t* gvt;  // [ldg][Tp] logit gradient, rows v (dW operand)
+  uint16_t* gtv;  // [Tp][ldg] logit gradient of one chunk, rows t (dH and dW operand)
   float* part;
 };
 
@@ -83,7 +81,6 @@ enum KernelId {
   K_BWD_DH,
   K_BWD_DH_REDUCE,
   K_FILL_ZERO,
-  K_BWD_TRANSPOSE,
   K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];

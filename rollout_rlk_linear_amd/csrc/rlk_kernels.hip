@@ -3,10 +3,10 @@
 // Forward (per call):
 //   fwd_tile     one workgroup per (T-tile, vocabulary group of 256 columns):
 //                bf16 MFMA logits for the tile, kept in registers; per row and
-//                32-column chunk the statistics (m, R, B) by a fixed 16-lane
-//                DPP tree; the 8 chunks of the group folded left to right;
-//                one (m, R, B, zy) record per (row, group) written to the
-//                workspace. No T x V logits ever reach memory.
+//                128-column chunk the statistics (m, R, B) by a fixed in-lane
+//                and 16-lane DPP tree; the 2 chunks of the group folded left
+//                to right; one (m, R, B, zy) record per (row, group) written to
+//                the workspace. No T x V logits ever reach memory.
 //   fwd_combine  one wave per row: the row's group records folded in a fixed
 //                lane-strided order plus a fixed 64-lane tree; writes logp,
 //                entropy and the row's statistics record.
@@ -15,8 +15,9 @@
 //   bwd_recompute  logits of the chunk again (same MFMA chain as the forward,
 //                  so the same bits), the logit gradient G in fp32, RNE to
 //                  bf16, staged through LDS and stored [T][chunk] coalesced.
-//   bwd_dw         dW[v, :] = sum_t G[t, v] h[t, :]  (both operands K-strided,
-//                  transposed in registers), fp32, one owner per element.
+//   bwd_dw         dW[v, :] = sum_t G[t, v] h[t, :]  (both operands read
+//                  K-major through transposing LDS reads), fp32, one owner
+//                  per element.
 //   bwd_dh         dH partial of split s = sum_{v in s} G[t, v] W[v, :], one
 //                  MFMA chain over the split in ascending v; splits are set by
 //                  V alone.
@@ -214,14 +215,13 @@ __global__ __launch_bounds__(kThreads) void bwd_rowprep_kernel(
 }
 
 // G for one (T-tile, group) of the chunk, rounded to bf16 into an LDS tile
-// [t][v], then stored twice: gtv[t][lg*256 + c] (row t, for dH; 16-byte row
-// pieces) and gvt[lg*256 + c][t] (row v, for dW; 8 t gathered down a column
-// per 16-byte store). Rows t in [T, Tp) of gvt are zeros (dW reads K = Tp).
+// [t][v], then stored as gtv[t][lg*256 + c] (rows t < T, 16-byte row pieces;
+// the columns past V are zeros). Both dH and dW read G from there.
 template <int BM, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
     int V, int chunk_g0, int n_groups, int n_ttiles, const float4* __restrict__ rowc,
-    uint16_t* __restrict__ gtv, int64_t ldg, uint16_t* __restrict__ gvt, int Tp) {
+    uint16_t* __restrict__ gtv, int64_t ldg) {
   using Gm = AsyncGemm<BM, GROUP, WM, WN>;
   constexpr int LDG_S = GROUP + 8;  // [t][v] staging row (bf16), 528 B
   constexpr int STG = BM * LDG_S * 2;
@@ -289,62 +289,26 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
   }
   __syncthreads();
   // gtv rows: 32 threads per row, 16 B each
-  if (gtv) {
-    const int c8 = (tid & 31) * 8;
-    for (int rl = tid >> 5; rl < BM; rl += kThreads / 32) {
-      const int t = row0 + rl;
-      if (t >= T) break;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * LDG_S + c8);
-      *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * GROUP + c8) = v;
-    }
-  }
-  // gvt rows (one per vocabulary column): 8 consecutive t per 16-byte store,
-  // gathered down a column of the staging tile; rows t in [T, Tp) are zeros
-  if (gvt) {
-    constexpr int TPR = BM / 8;  // 16-byte pieces per gvt row segment
-#pragma unroll 1
-    for (int idx = tid; idx < GROUP * TPR; idx += kThreads) {
-      const int cl = idx / TPR;
-      const int tcol = (idx % TPR) * 8;
-      const int t = row0 + tcol;
-      if (t >= Tp) continue;
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[e] = (uint32_t)stg[(tcol + 2 * e) * LDG_S + cl] |
-               ((uint32_t)stg[(tcol + 2 * e + 1) * LDG_S + cl] << 16);
-      *reinterpret_cast<u32x4*>(gvt + ((int64_t)lg * GROUP + cl) * Tp + t) = v;
-    }
+  const int c8 = (tid & 31) * 8;
+  for (int rl = tid >> 5; rl < BM; rl += kThreads / 32) {
+    const int t = row0 + rl;
+    if (t >= T) break;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * LDG_S + c8);
+    *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * GROUP + c8) = v;
   }
 }
 
-// hT[h][t] = hidden[t][h] for t < T, 0 for T <= t < Tp (64 x 64 tiles via LDS).
-__global__ __launch_bounds__(kThreads) void transpose_hidden_kernel(
-    const uint16_t* __restrict__ hidden, int T, int H, int Tp, uint16_t* __restrict__ hT) {
-  __shared__ uint16_t tile[64][66];
-  const int t0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int t = t0 + r;
-    tile[r][tx] = (t < T) ? hidden[(int64_t)t * H + h0 + tx] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    const int t = t0 + tx;
-    if (t < Tp) hT[(int64_t)(h0 + r) * Tp + t] = tile[tx][r];
-  }
-}
-
-// dW[chunk_v0 + v, h] = sum_t G[t, v] h[t, h] = sum_t gvt[v][t] hT[h][t];
-// tile 256 (v) x kDwBN (h), K = Tp (rows t >= T are zeros in both operands).
+// dW[chunk_v0 + v, h] = sum_t G[t, v] h[t, h], read straight from gtv [t][v]
+// and hidden [t][h] (both K-major), tile 256 (v) x kDwBN (h), K = t over
+// [0, Tp) with rows t >= T reading as zero.
 // With K as short as one batch, the tile's fp32 output takes about as long
 // to write as its MFMAs take to run. The tile is sized for two workgroups
 // per CU (3-slot ring: 72 KB of LDS, 128 accumulators per lane) so that one
 // can compute while the other writes, and the stores are non-temporal. The
 // h-tiles are split into groups of at most 8, one group per set of XCDs,
-// and the XCDs of a set split the v-tiles: an XCD keeps its 8 h^T tiles in
-// L2 and its ~64 resident workgroups share 8 G^T tiles, so the operands stay
-// in L2 while the output streams past.
+// and the XCDs of a set split the v-tiles: an XCD keeps its 8 hidden column
+// slices in L2 and its ~64 resident workgroups share 8 G column slices, so
+// the operands stay in L2 while the output streams past.
 DwMap dw_map(int n_vtiles, int n_htiles) {
   DwMap m;
   const int need = (n_htiles + 7) / 8;
@@ -356,10 +320,10 @@ DwMap dw_map(int n_vtiles, int n_htiles) {
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-bwd_dw_kernel(const uint16_t* __restrict__ gvt, const uint16_t* __restrict__ hT, int Tp, int H,
-              int V, int chunk_v0, int chunk_w, int n_vtiles, int n_htiles, DwMap map,
-              float* __restrict__ dweight) {
-  using Gm = AsyncGemm<256, kDwBN, 2, 2, 3>;
+bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ hidden,
+              int T, int Tp, int H, int V, int chunk_v0, int chunk_w, int n_vtiles, int n_htiles,
+              DwMap map, float* __restrict__ dweight) {
+  using Gm = AsyncGemmKK<256, kDwBN, 2, 2, 3>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
   const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
   if (seq >= map.per_xcd) return;
@@ -370,7 +334,7 @@ bwd_dw_kernel(const uint16_t* __restrict__ gvt, const uint16_t* __restrict__ hT,
   const int v0 = vt * 256, h0 = ht * kDwBN;
   Gm gm;
   gm.zero();
-  gm.run(lds, gvt + (int64_t)v0 * Tp, Tp, chunk_w - v0, hT + (int64_t)h0 * Tp, Tp, H - h0, 0, Tp);
+  gm.run(lds, gtv + v0, ldg, T, 256, hidden + h0, H, T, min(kDwBN, H - h0), 0, Tp);
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % 2, wn = wave / 2;
@@ -477,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 #define RLK_RECOMPUTE(BM, WM, WN)                                                             \
   template __global__ void bwd_recompute_kernel<BM, WM, WN>(                                  \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
-      const float4* __restrict__, uint16_t* __restrict__, int64_t, uint16_t* __restrict__, int);
+      const float4* __restrict__, uint16_t* __restrict__, int64_t);
 #define RLK_DH(BM, BN, WM, WN)                                                             \
   template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                    \
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, int, \
@@ -523,14 +487,6 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
   const int Tp = (int)p.Tp;
   RLK_LAUNCH(K_BWD_ROWPREP, bwd_rowprep_kernel, cdiv(T, kThreads), st, a.stats, a.dlogp,
              a.dentropy, a.targets, T, a.vocab_start, a.rowc);
-  if (a.dweight) {
-    prof_before(K_BWD_TRANSPOSE, st);
-    hipLaunchKernelGGL(transpose_hidden_kernel, dim3(cdiv(Tp, 64), cdiv(H, 64)), dim3(kThreads), 0,
-                       st, a.hidden, T, H, Tp, a.hT);
-    prof_after(K_BWD_TRANSPOSE, st);
-  }
-  uint16_t* gtv = a.dhidden ? a.gtv : nullptr;
-  uint16_t* gvt = a.dweight ? a.gvt : nullptr;
   const bool small = T <= kSmallT;
   const int bm = small ? 32 : 256;
   const int nt = cdiv(T, bm);
@@ -546,16 +502,16 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
     const int ng8 = cdiv(ngroups, 8) * 8;
     if (small)
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, 2, 2>), ng8 * nt, st, a.hidden,
-                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, gtv, p.ldg, gvt, Tp);
+                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
     else
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 2, 2>), ng8 * nt, st, a.hidden,
-                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, gtv, p.ldg, gvt, Tp);
+                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
     if (a.dweight) {
       const int nvt = cdiv(width, 256);
       const int nhw = cdiv(H, kDwBN);
       const DwMap map = dw_map(nvt, nhw);
-      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, 8 * map.per_xcd, st, a.gvt, a.hT, Tp, H, V, v0,
-                 ngroups * GROUP, nvt, nhw, map, a.dweight);
+      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, 8 * map.per_xcd, st, a.gtv, p.ldg, a.hidden, T, Tp, H,
+                 V, v0, ngroups * GROUP, nvt, nhw, map, a.dweight);
     }
     if (a.dhidden) {
       const int nsp = s1 - s0;
