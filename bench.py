@@ -8,12 +8,17 @@ over one batch of synthetic Qwen3-8B LM-head inputs (T = 512 tokens, H = 4096,
 V = 151936; hidden RMS-normalised N(0,1), W N(0, 0.02^2), both bf16; uniform
 targets; dlogp N(0,1)). Inputs are resident in HBM before the timed region.
 
-Prints one JSON line: tokens/s, ms/step, TFLOP/s (8 T H V flops per step) and
-fraction of the bf16 dense MFMA peak, the roofline of the dominant kernel
-(per-launch duration measured with HIP events recorded by the library on the
-launch stream), and the float64 CPU oracle timed on a bounded sample.
+Prints one JSON line: tokens/s over the timed steps, ms/step (also median with
+a distribution-free 95% interval, and minimum, from per-step HIP events),
+TFLOP/s (8 T H V flops per step) and the fraction of the bf16 dense MFMA
+peak (published, and measured on the box by the library's microbenchmark);
+the roofline of the dominant kernel (per-launch duration from HIP events the
+library records on the launch stream); the other workloads (tiny, small-T
+forward against the HBM roofline with a bitwise check, the 5208-token step,
+one 37984-row vocabulary slice); and the float64 CPU oracle timed on the same
+batch.
 
-    python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-cpu-baseline] [--quick]
 """
 
 from __future__ import annotations
@@ -21,7 +26,9 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
+import subprocess
 import sys
 import time
 
@@ -31,7 +38,6 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 METRIC = "linear-logp fwd+bwd tokens/s and % bf16 MFMA peak at H4096 V151936 T512"
-MFMA_KERNELS = ("fwd_tile", "bwd_recompute", "bwd_dw", "bwd_dh")
 CSRC = os.path.join(ROOT, "rollout_rlk_linear_amd", "csrc")
 
 
@@ -44,7 +50,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, launch_bytes_alg: float):
+def load_traffic(kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -54,12 +60,10 @@ def load_traffic(kernel: str, launch_bytes_alg: float):
     if t.get("source_hash") != kernel_source_hash():
         return None
     k = t.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k.get("hbm_bytes_per_launch")
+    return None if not k else k.get("hbm_bytes_per_launch")
 
 
-def algorithmic_work(T, H, V, nchunks, nsplits):
+def algorithmic_work(T, H, V, nsplits):
     """Per-step algorithmic flops (MFMA kernels) and bytes (the others)."""
     G = -(-V // 256)
     f = 2.0 * T * H * V
@@ -74,9 +78,178 @@ def algorithmic_work(T, H, V, nchunks, nsplits):
     }
 
 
+def median_ci(xs):
+    """Median, distribution-free ~95% interval of the median, minimum (ms)."""
+    s = sorted(xs)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    half = 0.98 * math.sqrt(n)
+    lo = max(0, int(math.floor(n / 2 - half)) - 1)
+    hi = min(n - 1, int(math.ceil(n / 2 + half)))
+    return {"median": round(med, 4), "ci95": [round(s[lo], 4), round(s[hi], 4)],
+            "min": round(s[0], 4), "n": n}
+
+
+def timed(torch, fn, warmup, steps):
+    """Per-call HIP-event times (ms) on the current stream, and their total."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[steps])
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "cu_count": p.multi_processor_count,
+            "gcn_arch": getattr(p, "gcnArchName", None)}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        if r.returncode == 0:
+            d = json.loads(r.stdout)
+            card = d[sorted(d)[0]]
+            info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception as e:  # the clock readout is informative only
+        info["clocks_error"] = type(e).__name__
+    return info
+
+
+def microbench(torch, rlk):
+    """Measured denominators: HBM copy bandwidth and bf16 MFMA rate."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    per, _ = timed(torch, lambda: rlk.microbench_copy(dst, src), 2, 5)
+    copy_gbs = 2 * n / (min(per) * 1e-3) / 1e9
+    del src, dst
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    wg, iters = 8 * ncu, 4096
+    flops = [0.0]
+
+    def mfma():
+        flops[0] = rlk.microbench_mfma(sink, wg, iters)
+
+    per, _ = timed(torch, mfma, 2, 5)
+    return {"copy_GBps": round(copy_gbs, 1), "copy_bytes": n,
+            "mfma_bf16_TFLOPs": round(flops[0] / (min(per) * 1e-3) / 1e12, 1),
+            "mfma_workgroups": wg, "mfma_iters": iters}
+
+
+def to_dev(torch, c):
+    dev = torch.device("cuda:0")
+    return [x.to(dev).contiguous() for x in (c.hidden, c.weight, c.targets, c.dlogp)]
+
+
+def workload_runs(torch, rlk, wl, copy_gbs, steps):
+    """The tiny case, small-T forwards (+ bitwise check), the 5208-token step
+    and one vocabulary slice, timed on the GPU."""
+    res = {}
+    # tiny: launch-bound, for completeness
+    c = wl.tiny()
+    h, w, y, dl = to_dev(torch, c)
+    de = c.dentropy.to("cuda:0")
+    fo, bo = {}, {}
+
+    def step1():
+        o = rlk.fwd(h, w, y, out=fo)
+        rlk.bwd(h, w, y, o["stats"], dl, de, out=bo)
+
+    per, _ = timed(torch, step1, 3, steps)
+    res["tiny_T64_H256_V1024"] = {"fwd_bwd_ms": median_ci(per), "dentropy": "N(0,1)"}
+
+    # small T: the forward is a stream over W; bytes 2HV + 2TH + 16T per call.
+    # Bitwise check: every batch of T consecutive rows of the 64-row pool
+    # against the 64-row call (logp, entropy and stats bits).
+    c2w = wl.qwen512().weight.to("cuda:0")
+    pool = wl.pool64()
+    ph = pool["hidden"].to("cuda:0")
+    pt = pool["targets"].to("cuda:0")
+    H, V = c2w.shape[1], c2w.shape[0]
+    ref = rlk.fwd(ph, c2w, pt)
+    ref_bits = {k: ref[k].view(torch.int32).clone() for k in ("logp", "entropy", "stats")}
+    small = {}
+    mismatches, compared = 0, 0
+    for T in (1, 2, 3, 4, 64):
+        fo = {}
+        hh, tt = ph[:T].contiguous(), pt[:T].contiguous()
+        per, _ = timed(torch, lambda: rlk.fwd(hh, c2w, tt, out=fo), 3, steps)
+        ms = median_ci(per)
+        byts = 2 * H * V + 2 * T * H + 16 * T
+        gbs = byts / (ms["median"] * 1e-3) / 1e9
+        small[f"T{T}"] = {"fwd_ms": ms, "bytes": byts, "GBps": round(gbs, 1),
+                          "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                          "frac_measured_copy": round(gbs / copy_gbs, 4) if copy_gbs else None}
+        for s0 in range(0, 64 - T + 1, T):
+            o = rlk.fwd(ph[s0:s0 + T].contiguous(), c2w, pt[s0:s0 + T].contiguous())
+            for k in ("logp", "entropy", "stats"):
+                d = o[k].view(torch.int32) != ref_bits[k][s0:s0 + T]
+                mismatches += int(d.sum())
+                compared += d.numel()
+    small["bitwise"] = {"mismatched_words": mismatches, "compared_words": compared}
+    res["small_T_forward_H4096_V151936"] = small
+    del c2w, ref
+
+    # the 5208-token step (8 sequences), fwd+bwd
+    c = wl.step5208()
+    h, w, y, dl = to_dev(torch, c)
+    fo, bo = {}, {}
+
+    def step4():
+        o = rlk.fwd(h, w, y, out=fo)
+        rlk.bwd(h, w, y, o["stats"], dl, None, out=bo)
+
+    per, _ = timed(torch, step4, 2, max(3, steps // 4))
+    ms = median_ci(per)
+    fl = 8.0 * c.T * c.H * c.V
+    res["step_T5208_H4096_V151936"] = {
+        "seq_lengths": c.meta.get("seq_lengths"), "fwd_bwd_ms": ms,
+        "tokens_per_s": round(c.T / (ms["median"] * 1e-3), 1),
+        "TFLOPs": round(fl / (ms["median"] * 1e-3) / 1e12, 1),
+        "frac_bf16_peak": round(fl / (ms["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del h, w, y, dl, fo, bo
+    wl.clear_cache()
+
+    # one TP=4 rank's vocabulary slice (rows 0..37983 of a W scaled by 8):
+    # fwd (stats partials) + bwd with the global statistics, dH as fp32
+    c = wl.slice7168()
+    h, w, y, dl = to_dev(torch, c)
+    a, b = c.meta["slices"][0]
+    parts = [rlk.fwd(h, w[s0:s1].contiguous(), y, vocab_start=s0, vocab_total=c.V)["stats"]
+             for s0, s1 in c.meta["slices"]]
+    _, _, gstats = rlk.combine_host(parts)
+    gstats = gstats.to("cuda:0")
+    ws = w[a:b].contiguous()
+    del w, parts
+    fo, bo = {}, {}
+
+    def step5():
+        rlk.fwd(h, ws, y, vocab_start=a, vocab_total=c.V, out=fo)
+        rlk.bwd(h, ws, y, gstats, dl, None, vocab_start=a, vocab_total=c.V, dhidden_f32=True,
+                out=bo)
+
+    per, _ = timed(torch, step5, 2, max(3, steps // 4))
+    ms = median_ci(per)
+    Vs = b - a
+    fl = 8.0 * c.T * c.H * Vs
+    res["slice_T7168_H4096_V37984"] = {
+        "fwd_bwd_ms": ms, "tokens_per_s": round(c.T / (ms["median"] * 1e-3), 1),
+        "TFLOPs": round(fl / (ms["median"] * 1e-3) / 1e12, 1),
+        "frac_bf16_peak": round(fl / (ms["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    wl.clear_cache()
+    return res
+
+
 def cpu_baseline(case, rows: int):
     """The float64 oracle (unchanged) on the first ``rows`` tokens of the batch."""
-    import numpy as np  # noqa: F401
     from threadpoolctl import threadpool_info
 
     from oracle import backward, forward
@@ -89,9 +262,10 @@ def cpu_baseline(case, rows: int):
     backward(h, case.weight, y, dl, None)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    what = "the whole batch" if rows == case.T else f"the first {rows} of the {case.T} tokens"
     return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of the {case.T} tokens, full vocabulary, float64 forward + "
-                      f"backward (all of dH and dW for the sample); {dt:.1f} s wall"}
+            "sample": f"{what}, full vocabulary, float64 forward + backward (all of dH and dW); "
+                      f"{dt:.1f} s wall"}
 
 
 def main():
@@ -101,6 +275,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--quick", action="store_true",
+                    help="only the T=512 step (no microbenchmarks, other workloads or clocks)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times), the reference "
@@ -133,9 +309,7 @@ def main():
     rlk.load_library()
     c = wl.qwen512()
     T, H, V = c.T, c.H, c.V
-    dev = torch.device("cuda:0")
-    hidden, weight, targets = (x.to(dev).contiguous() for x in (c.hidden, c.weight, c.targets))
-    dlogp = c.dlogp.to(dev).contiguous()
+    hidden, weight, targets, dlogp = to_dev(torch, c)
     fo, bo = {}, {}
 
     def step():
@@ -145,28 +319,27 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     rlk.profile_begin()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     prof = rlk.profile_end()
-    ms_total = e0.elapsed_time(e1)
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms_total = ev[0].elapsed_time(ev[args.steps])
     ms_step = ms_total / args.steps
     tokens_s = T * args.steps / (ms_total / 1e3)
     flops_step = 8.0 * T * H * V
     tflops = flops_step / (ms_step / 1e3) / 1e12
 
-    # plan figures for the per-launch work
     nsplits = max(1, min(8, V // 16384))
     launches = {k: n // args.steps for k, (_, n) in prof.items() if n}
-    work = algorithmic_work(T, H, V, launches.get("bwd_recompute", 1), nsplits)
+    work = algorithmic_work(T, H, V, nsplits)
     kernels = {}
     for k, (ms, n) in prof.items():
         if n == 0:
@@ -188,7 +361,7 @@ def main():
                 "unit": "GB/s", "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4)}
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(dk["avg_launch_ms"], 4)
-    roof["traffic"] = load_traffic(dom, dk["work_per_launch"])
+    roof["traffic"] = load_traffic(dom)
 
     result = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -199,7 +372,9 @@ def main():
                    "T": T, "H": H, "V": V, "seed": 1, "dlogp": "N(0,1)", "dentropy": None,
                    "parallelism": "none (1 GPU)",
                    "inputs_sha256": wl.digest(c.hidden, c.weight, c.targets)[:16]},
+        "step_ms": median_ci(per),
         "tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "model_tflops_6thv": round(0.75 * tflops, 2),
         "wall_s_timed": round(wall, 4),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
@@ -207,8 +382,15 @@ def main():
         "backend": rlk.backend_id(),
         "kernel_source": kernel_source_hash(),
     }
+    del fo, bo
+    if not args.quick:
+        result["device"] = device_info(torch)
+        mb = microbench(torch, rlk)
+        result["microbench"] = mb
+        result["frac_measured_mfma"] = round(tflops / mb["mfma_bf16_TFLOPs"], 4)
+        result["workloads"] = workload_runs(torch, rlk, wl, mb["copy_GBps"], args.steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(c, min(args.cpu_rows, T))
+        result["cpu_baseline"] = cpu_baseline(wl.qwen512(), min(args.cpu_rows, T))
     else:
         result["cpu_baseline"] = None
     line = json.dumps(result)

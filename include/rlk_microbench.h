@@ -1,0 +1,39 @@
+/* rlk_microbench.h — on-device microbenchmarks that give the measured
+ * denominators of the roofline figures: sustained HBM copy bandwidth and the
+ * sustained dense bf16 MFMA rate of the same v_mfma_f32_16x16x32_bf16
+ * instruction the GEMM kernels use. They are measurement tools, not part of
+ * the linear log-prob path.
+ *
+ * Both calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ * stream) and return immediately; the caller times them with events on that
+ * stream. They allocate nothing. Errors: RLK_ERR_INVALID_ARG for NULL or
+ * misaligned pointers or sizes out of range, RLK_ERR_UNSUPPORTED_DEVICE when
+ * the current device is not gfx950, RLK_ERR_HIP when the launch fails.
+ */
+#ifndef RLK_MICROBENCH_H
+#define RLK_MICROBENCH_H
+
+#include "rlk_linear.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dst[i] = src[i] for `bytes` bytes (a multiple of 16, at most 2^40), both
+ * device pointers 16-byte aligned, not overlapping. One read and one write
+ * of every byte: count 2 * bytes of HBM traffic. */
+RLK_API rlk_status rlk_microbench_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Back-to-back independent bf16 MFMAs (16x16x32, fp32 accumulate) on every
+ * SIMD: `workgroups` workgroups of 4 waves, each wave `iters` rounds of 32
+ * MFMAs (1 <= iters <= 2^24, 1 <= workgroups <= 2^20). Flops performed:
+ * workgroups * 4 * iters * 32 * 16384. `sink` (device, 16-byte aligned,
+ * >= 16 bytes) receives a value derived from the accumulators so the work
+ * cannot be elided. */
+RLK_API rlk_status rlk_microbench_mfma(float* sink, int64_t workgroups, int64_t iters, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_MICROBENCH_H */

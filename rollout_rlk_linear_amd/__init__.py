@@ -84,6 +84,10 @@ def load_library(path: str | None = None):
     lib.rlk_profile_kernel_count.restype = ctypes.c_int
     lib.rlk_profile_kernel_name.argtypes = [ctypes.c_int]
     lib.rlk_profile_kernel_name.restype = ctypes.c_char_p
+    lib.rlk_microbench_copy.argtypes = [vp, vp, sz, vp]
+    lib.rlk_microbench_copy.restype = ctypes.c_int
+    lib.rlk_microbench_mfma.argtypes = [vp, i64, i64, vp]
+    lib.rlk_microbench_mfma.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -124,6 +128,22 @@ def profile_end() -> dict:
     cnt = (ctypes.c_uint64 * n)()
     _check(lib.rlk_profile_end(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(cnt, ctypes.c_void_p), n))
     return {lib.rlk_profile_kernel_name(i).decode(): (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+def microbench_copy(dst: torch.Tensor, src: torch.Tensor):
+    """Enqueue one copy of src's bytes into dst (``rlk_microbench_copy``)."""
+    if dst.nbytes != src.nbytes or not (dst.is_cuda and src.is_cuda and dst.is_contiguous()
+                                        and src.is_contiguous()):
+        raise ValueError("dst and src must be contiguous device tensors of equal size")
+    _check(load_library().rlk_microbench_copy(_ptr(dst), _ptr(src), src.nbytes, _stream(src.device)))
+
+
+def microbench_mfma(sink: torch.Tensor, workgroups: int, iters: int) -> float:
+    """Enqueue the MFMA-rate kernel; returns the flops it performs."""
+    if not (sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= 4):
+        raise ValueError("sink must be a device fp32 tensor of at least 4 elements")
+    _check(load_library().rlk_microbench_mfma(_ptr(sink), workgroups, iters, _stream(sink.device)))
+    return float(workgroups) * 4 * iters * 32 * 16384
 
 
 def fwd_workspace_bytes(T: int, H: int, V: int) -> int:

@@ -83,6 +83,8 @@ Profiler g_prof;
 
 namespace rlk {
 
+int check_device_status() { return (int)check_device(); }
+
 const char* const kKernelNames[K_COUNT] = {
     "fwd_tile", "fwd_combine", "bwd_rowprep", "bwd_recompute",
     "bwd_dw",   "bwd_dh",      "bwd_dh_reduce", "fill_zero"};

@@ -90,6 +90,8 @@ void prof_before(int id, hipStream_t st);
 void prof_after(int id, hipStream_t st);
 
 size_t fwd_workspace(int64_t T, int64_t H, int64_t V);
+// RLK_OK when the current device is gfx950, else the rlk_status error.
+int check_device_status();
 BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);

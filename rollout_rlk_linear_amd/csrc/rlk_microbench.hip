@@ -1,0 +1,89 @@
+// rlk_microbench.hip — measured denominators for the roofline figures: a
+// streaming copy (HBM bandwidth) and back-to-back independent bf16 MFMAs
+// (matrix-core rate), declared in rlk_microbench.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rlk_device.cuh"
+#include "rlk_internal.h"
+#include "../../include/rlk_microbench.h"
+
+namespace rlk {
+namespace {
+
+// 4 float4 per thread, strided by the grid so every load instruction of a
+// wave covers 1 KB of consecutive bytes.
+__global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ dst,
+                                                        const u32x4* __restrict__ src, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  u32x4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = i0 + k * stride;
+    if (i < n16) v[k] = src[i];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = i0 + k * stride;
+    if (i < n16) dst[i] = v[k];
+  }
+}
+
+// Every wave: 32 independent accumulators, `iters` rounds of one MFMA each;
+// operands vary per lane so the data is not trivially constant.
+__global__ __launch_bounds__(kThreads) void mfma_kernel(float* __restrict__ sink, int iters) {
+  const int lane = threadIdx.x & 63;
+  u32x4 ra, rb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ra[e] = 0x3c003c00u ^ (uint32_t)((lane * 2654435761u + e) & 0x007f007fu);
+    rb[e] = 0x3c803c80u ^ (uint32_t)((lane * 40503u + 3 * e) & 0x007f007fu);
+  }
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ra), b = __builtin_bit_cast(bf16x8, rb);
+  f32x4 acc[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  // a value the compiler cannot predict decides the store
+  if (s == -1.2345e-30f) sink[threadIdx.x & 3] = s;
+}
+
+}  // namespace
+}  // namespace rlk
+
+extern "C" {
+
+RLK_API rlk_status rlk_microbench_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes == 0 || (bytes % 16) != 0 || bytes > (size_t(1) << 40))
+    return RLK_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16) return RLK_ERR_INVALID_ARG;
+  const int s = rlk::check_device_status();
+  if (s != RLK_OK) return (rlk_status)s;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t per_block = (int64_t)rlk::kThreads * 4;
+  const int64_t grid = (n16 + per_block - 1) / per_block;
+  hipLaunchKernelGGL(rlk::copy_kernel, dim3((unsigned)grid), dim3(rlk::kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<rlk::u32x4*>(dst),
+                     static_cast<const rlk::u32x4*>(src), n16);
+  return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
+RLK_API rlk_status rlk_microbench_mfma(float* sink, int64_t workgroups, int64_t iters, void* stream) {
+  if (!sink || (reinterpret_cast<uintptr_t>(sink) % 16) || workgroups < 1 || workgroups > (1 << 20) ||
+      iters < 1 || iters > (1 << 24))
+    return RLK_ERR_INVALID_ARG;
+  const int s = rlk::check_device_status();
+  if (s != RLK_OK) return (rlk_status)s;
+  hipLaunchKernelGGL(rlk::mfma_kernel, dim3((unsigned)workgroups), dim3(rlk::kThreads), 0,
+                     static_cast<hipStream_t>(stream), sink, (int)iters);
+  return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
+}  // extern "C"

@@ -8,6 +8,7 @@
 """
 
 import ctypes
+import glob
 import math
 import os
 import re
@@ -20,7 +21,7 @@ import rollout_rlk_linear_amd as rlk
 from oracle import finalize_partials, forward_f64, merge_partials, slice_partials_f64
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rlk_linear.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, INVALID, SHAPE, WS_SMALL, DEVICE, HIPERR = 0, 1, 2, 3, 4, 5
 P = ctypes.c_void_p(1 << 20)  # aligned fake device pointer, never dereferenced on the host
@@ -28,15 +29,18 @@ NULL = None
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    return re.findall(r"RLK_API\s+[\w\s\*]+?\b(rlk_\w+)\s*\(", text)
+    names = []
+    for h in HEADERS:
+        names += re.findall(r"RLK_API\s+[\w\s\*]+?\b(rlk_\w+)\s*\(", open(h).read())
+    return names
 
 
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ["rlk_linear_logp_fwd", "rlk_linear_logp_bwd", "rlk_linear_logp_fwd_workspace_bytes",
               "rlk_linear_logp_bwd_workspace_bytes", "rlk_linear_logp_combine_host",
-              "rlk_status_string", "rlk_backend_id", "rlk_call_count", "rlk_abi_version"]:
+              "rlk_status_string", "rlk_backend_id", "rlk_call_count", "rlk_abi_version",
+              "rlk_microbench_copy", "rlk_microbench_mfma"]:
         assert n in names
 
 
@@ -44,6 +48,21 @@ def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(rlk.LIB_PATH)
     for n in declared_symbols():
         assert hasattr(raw, n), n
+
+
+def test_microbench_argument_errors():
+    raw = ctypes.CDLL(rlk.LIB_PATH)
+    raw.rlk_microbench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    raw.rlk_microbench_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    Q = ctypes.c_void_p(1 << 21)
+    assert raw.rlk_microbench_copy(NULL, Q, 1024, NULL) == INVALID
+    assert raw.rlk_microbench_copy(P, Q, 1000, NULL) == INVALID             # not a multiple of 16
+    assert raw.rlk_microbench_copy(ctypes.c_void_p((1 << 20) + 8), Q, 1024, NULL) == INVALID
+    assert raw.rlk_microbench_copy(P, Q, 0, NULL) == INVALID
+    assert raw.rlk_microbench_mfma(NULL, 256, 10, NULL) == INVALID
+    assert raw.rlk_microbench_mfma(P, 0, 10, NULL) == INVALID
+    assert raw.rlk_microbench_mfma(P, 256, 0, NULL) == INVALID
+    assert raw.rlk_microbench_mfma(P, 256, (1 << 24) + 1, NULL) == INVALID
 
 
 def test_provenance(lib):
