@@ -278,6 +278,9 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="only the T=512 step (no microbenchmarks, other workloads or clocks)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--profile-case", choices=["fwd_t1"], default=None,
+                    help="run only this case's calls (warmup + steps), for profilers: fwd_t1 = "
+                         "the T=1 forward over the full vocabulary")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -308,6 +311,14 @@ def main():
         return
     rlk.load_library()
     c = wl.qwen512()
+    if args.profile_case == "fwd_t1":
+        w = c.weight.to("cuda:0")
+        pool = wl.pool64()
+        h1, y1 = pool["hidden"][:1].to("cuda:0"), pool["targets"][:1].to("cuda:0")
+        fo1 = {}
+        per, _ = timed(torch, lambda: rlk.fwd(h1, w, y1, out=fo1), args.warmup, args.steps)
+        print(json.dumps({"profile_case": "fwd_t1", "fwd_ms": median_ci(per)}), flush=True)
+        return
     T, H, V = c.T, c.H, c.V
     hidden, weight, targets, dlogp = to_dev(torch, c)
     fo, bo = {}, {}
