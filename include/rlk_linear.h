@@ -21,7 +21,7 @@
  * its target, its upstream gradients and W: not on T, on the other rows, on
  * the row's position in the batch, or on the repeat. dweight is a sum over
  * rows and is only repeat-deterministic. Nothing uses atomics; every
- * reduction runs in a fixed order set by V alone.
+ * reduction runs in a fixed order set by the vocabulary layout alone.
  *
  * Memory. All tensor pointers are device pointers owned by the caller,
  * row-major, 16-byte aligned; inputs and outputs must not alias. The library
@@ -41,8 +41,19 @@
  * a vocabulary of vocab_total rows (one GPU's share of a tensor-parallel LM
  * head; the pages' actor runs at TP=4). `weight` then points at the slice's
  * first row. The forward returns the slice's partial statistics, which
- * rlk_linear_logp_combine_host merges across slices; the backward takes the
- * merged (whole-vocabulary) statistics.
+ * rlk_linear_logp_combine (on the device) or rlk_linear_logp_combine_host
+ * merges across slices; the backward takes the merged (whole-vocabulary)
+ * statistics.
+ *
+ * Tensor-parallel invariance. When vocab_total is a multiple of 4 the
+ * vocabulary is cut into 4 virtual slices of vocab_total / 4 rows. The
+ * forward reduces each virtual slice on its own (groups of 256 columns from
+ * the slice's first row) and merges the virtual slices with a fixed balanced
+ * tree, ((s0 + s1) + (s2 + s3)). A call that covers 1, 2 or all 4 virtual
+ * slices, aligned to its own size (TP = 4, 2 or 1 with equal shares), computes
+ * exactly its subtree, and rlk_linear_logp_combine merges call records with
+ * the same tree: so TP = 1, 2 and 4 give identical bits for logp, entropy and
+ * stats. Any other call covers one segment starting at its first row.
  */
 #ifndef RLK_LINEAR_H
 #define RLK_LINEAR_H
@@ -87,7 +98,9 @@ typedef enum rlk_status {
 #define RLK_MAX_V (1LL << 24)
 #define RLK_MAX_VOCAB ((1LL << 31) - 1)
 
-/* Bytes of device workspace the forward needs for (T, H, V). 0 when T == 0. */
+/* Bytes of device workspace the forward needs for (T, H, V): one 16-byte
+ * record per row and group of 256 columns, (ceil(V/256) + 3) groups at most,
+ * rounded up to 256 bytes. 0 when T == 0. */
 RLK_API size_t rlk_linear_logp_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V);
 
 /* Bytes of device workspace the backward needs for (T, H, V, flags, whether
@@ -133,18 +146,33 @@ RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
                                        uint32_t flags, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
-/* Host-side merge of S slice records in the fixed order s = 0, 1, ..., S-1.
- *   partials  host fp32 [S][T][4] (slice s's forward `stats`)
- *   logp, entropy  host fp32 [T] or NULL
- *   stats     host fp32 [T,4] or NULL: the merged whole-vocabulary record
- * Runs on the CPU, touches no device. */
+/* Merge of S slice records (slices in vocabulary order) by the fixed merge
+ * tree: adjacent pairs first, (r0 + r1), (r2 + r3), ..., an odd last record
+ * carried up unchanged, repeated until one record is left; so S = 2 gives
+ * r0 + r1 and S = 4 gives (r0 + r1) + (r2 + r3).
+ *   partials  fp32 [S][T][4] (slice s's forward `stats`), 1 <= S <= 1024
+ *   logp, entropy  fp32 [T] or NULL (a row whose target lies in no slice
+ *            gets logp = -inf)
+ *   stats     fp32 [T,4] or NULL: the merged whole-vocabulary record
+ * rlk_linear_logp_combine takes device pointers and runs on `stream` with the
+ * arithmetic of the forward kernels, so its bits equal those of a call that
+ * covers the same slices (see "Tensor-parallel invariance"); at least one
+ * output must be non-NULL, T == 0 is a no-op.
+ * rlk_linear_logp_combine_host takes host pointers and runs on the CPU
+ * (touches no device); its exp and log1p are the host library's, so its
+ * values agree with the device's to rounding but not necessarily in every
+ * bit. */
+RLK_API rlk_status rlk_linear_logp_combine(const float* partials, int64_t S, int64_t T,
+                                           float* logp, float* entropy, float* stats,
+                                           void* stream);
 RLK_API rlk_status rlk_linear_logp_combine_host(const float* partials, int64_t S, int64_t T,
                                                 float* logp, float* entropy, float* stats);
 
 /* Provenance. */
 RLK_API const char* rlk_status_string(int status);
 RLK_API const char* rlk_backend_id(void);
-/* Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host. */
+/* Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host,
+ * 3 combine. */
 RLK_API uint64_t rlk_call_count(int which);
 RLK_API int rlk_abi_version(void);
 

@@ -68,6 +68,8 @@ def load_library(path: str | None = None):
     lib.rlk_linear_logp_bwd.restype = ctypes.c_int
     lib.rlk_linear_logp_combine_host.argtypes = [f32p, i64, i64, f32p, f32p, f32p]
     lib.rlk_linear_logp_combine_host.restype = ctypes.c_int
+    lib.rlk_linear_logp_combine.argtypes = [f32p, i64, i64, f32p, f32p, f32p, vp]
+    lib.rlk_linear_logp_combine.restype = ctypes.c_int
     lib.rlk_status_string.argtypes = [ctypes.c_int]
     lib.rlk_status_string.restype = ctypes.c_char_p
     lib.rlk_backend_id.argtypes = []
@@ -252,7 +254,8 @@ def bwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, stats
 
 
 def combine_host(partials):
-    """Merge per-slice stats (list of [T,4] fp32, CPU or device) in list order.
+    """Merge per-slice stats (list of [T,4] fp32, CPU or device, slices in
+    vocabulary order) by the library's fixed merge tree.
 
     Runs ``rlk_linear_logp_combine_host`` on the CPU. Returns (logp, entropy,
     stats) as CPU fp32 tensors.
@@ -265,6 +268,36 @@ def combine_host(partials):
     stats = torch.empty(T, 4, dtype=torch.float32)
     _check(lib.rlk_linear_logp_combine_host(_ptr(parts), S, T, _ptr(logp), _ptr(ent), _ptr(stats)))
     return logp, ent, stats
+
+
+def combine(partials, out: dict | None = None):
+    """Merge per-slice stats on the device (``rlk_linear_logp_combine``).
+
+    ``partials``: list of [T,4] fp32 device tensors, or one [S,T,4] tensor,
+    slices in vocabulary order. Returns dict(logp, entropy, stats) on the
+    same device; the bits equal those of a forward call covering the same
+    aligned virtual slices.
+    """
+    lib = load_library()
+    parts = partials if isinstance(partials, torch.Tensor) else torch.stack(list(partials))
+    parts = parts.contiguous()
+    if parts.dim() != 3 or parts.shape[2] != 4 or parts.dtype != torch.float32 or not parts.is_cuda:
+        raise ValueError("partials must be device fp32 [S,T,4] (or a list of [T,4])")
+    S, T = parts.shape[0], parts.shape[1]
+    out = {} if out is None else out
+    logp = _reuse(out, "logp", (T,), torch.float32)
+    ent = _reuse(out, "entropy", (T,), torch.float32)
+    stats = _reuse(out, "stats", (T, 4), torch.float32)
+    if logp is None:
+        logp = torch.empty(T, dtype=torch.float32, device=parts.device)
+    if ent is None:
+        ent = torch.empty(T, dtype=torch.float32, device=parts.device)
+    if stats is None:
+        stats = torch.empty(T, 4, dtype=torch.float32, device=parts.device)
+    out.update({"logp": logp, "entropy": ent, "stats": stats})
+    _check(lib.rlk_linear_logp_combine(_ptr(parts), S, T, _ptr(logp), _ptr(ent), _ptr(stats),
+                                       _stream(parts.device)))
+    return {"logp": logp, "entropy": ent, "stats": stats}
 
 
 class LinearLogp(torch.autograd.Function):

@@ -17,7 +17,7 @@ namespace {
 constexpr int kAbiVersion = 1;
 const char kBackendId[] = "rlk.linear_logp.bitwise.gfx950.v1";
 
-std::atomic<uint64_t> g_calls[3];
+std::atomic<uint64_t> g_calls[4];
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -87,7 +87,7 @@ int check_device_status() { return (int)check_device(); }
 
 const char* const kKernelNames[K_COUNT] = {
     "fwd_tile", "fwd_combine", "bwd_rowprep", "bwd_recompute",
-    "bwd_dw",   "bwd_dh",      "bwd_dh_reduce", "fill_zero"};
+    "bwd_dw",   "bwd_dh",      "bwd_dh_reduce", "fill_zero", "combine"};
 
 void prof_before(int id, hipStream_t st) {
   if (!g_prof.on.load(std::memory_order_relaxed)) return;
@@ -117,8 +117,26 @@ void prof_after(int id, hipStream_t st) {
 size_t fwd_workspace(int64_t T, int64_t H, int64_t V) {
   (void)H;
   if (T <= 0) return 0;
-  const int64_t G = ceil_div(V, 256);
+  // P virtual slices of V / P rows take at most ceil(V/256) + P - 1 groups
+  const int64_t G = ceil_div(V, 256) + kVirtualSlices - 1;
   return align256(size_t(T) * size_t(G) * 16);
+}
+
+FwdSlicing fwd_slicing(int64_t V, int64_t vocab_start, int64_t vocab_total) {
+  FwdSlicing f{1, (int)V, 0, 0};
+  if (vocab_total % kVirtualSlices == 0) {
+    const int64_t vs = vocab_total / kVirtualSlices;
+    if (vocab_start % vs == 0 && V % vs == 0) {
+      const int64_t p = V / vs, first = vocab_start / vs;
+      if ((p == 1 || p == 2 || p == 4) && first % p == 0) {
+        f.P = (int)p;
+        f.Vs = (int)vs;
+      }
+    }
+  }
+  f.Gs = (int)ceil_div(f.Vs, 256);
+  f.G = f.P * f.Gs;
+  return f;
 }
 
 BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh) {
@@ -195,6 +213,7 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
   a.vocab_start = vocab_start;
   a.vocab_total = vocab_total;
   a.full = full ? 1 : 0;
+  a.slicing = rlk::fwd_slicing(V, vocab_start, vocab_total);
   a.logp = logp;
   a.entropy = entropy;
   a.stats = reinterpret_cast<float4*>(stats);
@@ -268,40 +287,76 @@ RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
 // B = B_b + e^d (B_o + (1 + R_o) d), zy = max(zy_1, zy_2).
 RLK_API rlk_status rlk_linear_logp_combine_host(const float* partials, int64_t S, int64_t T,
                                                 float* logp, float* entropy, float* stats) {
-  if (S < 1 || T < 0) return RLK_ERR_INVALID_ARG;
+  if (S < 1 || S > rlk::kMaxCombine || T < 0) return RLK_ERR_INVALID_ARG;
   if (T > 0 && !partials) return RLK_ERR_INVALID_ARG;
+  struct Rec {
+    float m, R, B, zy;
+  };
+  auto merge = [](const Rec& l, const Rec& r) {
+    const bool left_base = !(r.m > l.m);
+    const Rec& b = left_base ? l : r;
+    const Rec& o = left_base ? r : l;
+    Rec out{b.m, b.R, b.B, std::fmax(l.zy, r.zy)};
+    if (o.m == -INFINITY) return out;
+    const float d = o.m - b.m;
+    const float e = std::exp(d);
+    const float one_r = 1.f + o.R;
+    out.R = b.R + e * one_r;
+    out.B = b.B + e * (o.B + one_r * d);
+    return out;
+  };
   for (int64_t t = 0; t < T; ++t) {
-    float m = partials[t * 4 + 0], R = partials[t * 4 + 1], B = partials[t * 4 + 2],
-          zy = partials[t * 4 + 3];
-    for (int64_t s = 1; s < S; ++s) {
+    // the merge tree as a binary counter: a stack of subtrees whose sizes are
+    // decreasing powers of two; equal neighbours merge (left + right), and
+    // what remains at the end is folded from the right
+    Rec st[rlk::kCombineDepth];
+    int lvl[rlk::kCombineDepth];
+    int n = 0;
+    for (int64_t s = 0; s < S; ++s) {
       const float* q = partials + (s * T + t) * 4;
-      const bool left_base = !(q[0] > m);
-      const float mb = left_base ? m : q[0], Rb = left_base ? R : q[1], Bb = left_base ? B : q[2];
-      const float mo = left_base ? q[0] : m, Ro = left_base ? q[1] : R, Bo = left_base ? q[2] : B;
-      zy = std::fmax(zy, q[3]);
-      m = mb;
-      if (mo == -INFINITY) {
-        R = Rb;
-        B = Bb;
-        continue;
+      st[n] = Rec{q[0], q[1], q[2], q[3]};
+      lvl[n++] = 0;
+      while (n >= 2 && lvl[n - 2] == lvl[n - 1]) {
+        st[n - 2] = merge(st[n - 2], st[n - 1]);
+        ++lvl[n - 2];
+        --n;
       }
-      const float d = mo - mb;
-      const float e = std::exp(d);
-      const float one_r = 1.f + Ro;
-      R = Rb + e * one_r;
-      B = Bb + e * (Bo + one_r * d);
     }
-    const float L = std::log1p(R);
+    Rec acc = st[n - 1];
+    for (int i = n - 2; i >= 0; --i) acc = merge(st[i], acc);
+    const float L = std::log1p(acc.R);
     if (stats) {
-      stats[t * 4 + 0] = m;
-      stats[t * 4 + 1] = R;
-      stats[t * 4 + 2] = B;
-      stats[t * 4 + 3] = zy;
+      stats[t * 4 + 0] = acc.m;
+      stats[t * 4 + 1] = acc.R;
+      stats[t * 4 + 2] = acc.B;
+      stats[t * 4 + 3] = acc.zy;
     }
-    if (logp) logp[t] = (zy - m) - L;
-    if (entropy) entropy[t] = L - B / (1.f + R);
+    if (logp) logp[t] = (acc.zy - acc.m) - L;
+    if (entropy) entropy[t] = L - acc.B / (1.f + acc.R);
   }
   g_calls[2].fetch_add(1, std::memory_order_relaxed);
+  return RLK_OK;
+}
+
+RLK_API rlk_status rlk_linear_logp_combine(const float* partials, int64_t S, int64_t T,
+                                           float* logp, float* entropy, float* stats,
+                                           void* stream) {
+  if (S < 1 || S > rlk::kMaxCombine || T < 0 || T > RLK_MAX_T) return RLK_ERR_INVALID_ARG;
+  if (!logp && !entropy && !stats) return RLK_ERR_INVALID_ARG;
+  if (T == 0) {
+    g_calls[3].fetch_add(1, std::memory_order_relaxed);
+    return RLK_OK;
+  }
+  if (!partials || !aligned(partials, 16) || (logp && !aligned(logp, 4)) ||
+      (entropy && !aligned(entropy, 4)) || (stats && !aligned(stats, 16)))
+    return RLK_ERR_INVALID_ARG;
+  const rlk_status s = check_device();
+  if (s != RLK_OK) return s;
+  if (rlk::launch_combine(reinterpret_cast<const float4*>(partials), (int)S, (int)T, logp, entropy,
+                          reinterpret_cast<float4*>(stats),
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return RLK_ERR_HIP;
+  g_calls[3].fetch_add(1, std::memory_order_relaxed);
   return RLK_OK;
 }
 
@@ -320,7 +375,7 @@ RLK_API const char* rlk_status_string(int status) {
 RLK_API const char* rlk_backend_id(void) { return kBackendId; }
 
 RLK_API uint64_t rlk_call_count(int which) {
-  if (which < 0 || which > 2) return 0;
+  if (which < 0 || which > 3) return 0;
   return g_calls[which].load(std::memory_order_relaxed);
 }
 

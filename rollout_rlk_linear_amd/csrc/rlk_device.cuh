@@ -497,7 +497,7 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 // Rows of B at or past kb_valid, and columns at or past nb_valid in its last
 // valid row, read as zero; other columns past nb_valid read whatever follows
 // in memory and only reach output columns the caller discards.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NSTG = 4>
 struct AsyncGemmKN {
   static constexpr int NW = WM * WN;
   static_assert(NW == 4, "4 waves per workgroup");
@@ -505,7 +505,8 @@ struct AsyncGemmKN {
   static_assert(BM % 16 == 0, "16-row A blocks");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NJ = WTN / 16;
-  static constexpr int NST = 4;
+  static constexpr int NST = NSTG;
+  static_assert(NST == 3 || NST == 4, "3- or 4-slot ring");
   static constexpr int ROWB_A = 64;
   static constexpr int ROWB_B = BN * 2;
   static constexpr int PPR = BN / 8;    // 16-byte pieces per B row
@@ -620,15 +621,16 @@ struct AsyncGemmKN {
       return make_rsrc(B + (int64_t)k0 * ldb, bbytes);
     };
 
-    // same 4-slot ring as AsyncGemm; A fragments read two row blocks ahead
-    for (int s = 0; s < 3 && s < nsteps; ++s) issue(s);
+    // same ring as AsyncGemm; A fragments read two row blocks ahead
+    for (int s = 0; s < NST - 1 && s < nsteps; ++s) issue(s);
     for (int s = 0; s < nsteps; ++s) {
-      wait_stage(s, last_of(s + 2));
+      wait_stage(s, last_of(s + NST - 2));
       barrier_only();
-      const bool refill = s + 3 < nsteps;
-      if (!SPLIT && refill) issue(s + 3);
-      const int k3 = k_begin + 32 * (s + 3);
-      const uint32_t dst = lds0 + (uint32_t)(((s + 3) % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave;
+      const bool refill = s + NST - 1 < nsteps;
+      if (!SPLIT && refill) issue(s + NST - 1);
+      const int k3 = k_begin + 32 * (s + NST - 1);
+      const uint32_t dst =
+          lds0 + (uint32_t)(((s + NST - 1) % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave;
       const i32x4 rsB3 = stage_rsrc_b(k3);
       unsigned char* st = lds + (s % NST) * STAGE_BYTES;
       constexpr int A0 = MI < 2 ? MI : 2;

@@ -31,6 +31,23 @@ struct DwMap {
 };
 DwMap dw_map(int n_vtiles, int n_htiles);
 
+// Forward reduction layout. With P > 1 the call covers P of the 4 virtual
+// slices (vocab_total / 4 rows each) of the vocabulary: groups of 256
+// columns restart at each slice's first row (Gs groups per slice, the last
+// one short), each slice is reduced on its own, and the slice records merge
+// by the fixed tree. Otherwise P = 1 and the one segment is the call.
+constexpr int kVirtualSlices = 4;
+struct FwdSlicing {
+  int P;   // virtual slices covered by the call (1, 2 or 4)
+  int Vs;  // rows per slice
+  int Gs;  // groups per slice
+  int G;   // P * Gs
+};
+FwdSlicing fwd_slicing(int64_t V, int64_t vocab_start, int64_t vocab_total);
+// Records merged by one combine call, and the depth of its merge stack.
+constexpr int kMaxCombine = 1024;
+constexpr int kCombineDepth = 12;
+
 struct FwdArgs {
   const uint16_t* hidden;
   const uint16_t* weight;
@@ -38,6 +55,7 @@ struct FwdArgs {
   int T, H, V;
   int64_t vocab_start, vocab_total;
   int full;
+  FwdSlicing slicing;
   float* logp;
   float* entropy;
   float4* stats;
@@ -81,6 +99,7 @@ enum KernelId {
   K_BWD_DH,
   K_BWD_DH_REDUCE,
   K_FILL_ZERO,
+  K_COMBINE,
   K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];
@@ -96,6 +115,8 @@ BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st);
+hipError_t launch_combine(const float4* partials, int S, int T, float* logp, float* entropy,
+                          float4* stats, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 }  // namespace rlk

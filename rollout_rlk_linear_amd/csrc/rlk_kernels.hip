@@ -74,10 +74,12 @@ __device__ __forceinline__ ChunkStats chunk_stats(const float (&z)[8]) {
   return c;
 }
 
+// Group g of the call is group g % Gs of virtual slice g / Gs: columns
+// (g / Gs) Vs + 256 (g % Gs) onward, at most 256 and not past the slice.
 template <int BM, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
-    const int32_t* __restrict__ targets, int T, int H, int V, int64_t vocab_start, int G,
+    const int32_t* __restrict__ targets, int T, int H, int Vs, int Gs, int64_t vocab_start, int G,
     int n_ttiles, float4* __restrict__ part) {
   using Gm = AsyncGemm<BM, GROUP, WM, WN>;
   static_assert(WN == 2 && Gm::WTN == 128 && Gm::NJ == 8, "one 128-column chunk per wave");
@@ -89,22 +91,23 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
   xcd_decode(blockIdx.x, n_ttiles, g, tt);
   if (g >= G) return;
   const int row0 = tt * BM;
-  const int col0 = g * GROUP;
+  const int lg = g % Gs;
+  const int col0 = (g / Gs) * Vs + lg * GROUP;
+  const int vlim = min(GROUP, Vs - lg * GROUP);  // valid columns of the group
   const int tid = threadIdx.x;
   if (tid < BM) {
     const int t = row0 + tid;
     int yc = -1;
     if (t < T) {
       const int64_t y = (int64_t)targets[t] - vocab_start - col0;
-      if (y >= 0 && y < GROUP && y < (int64_t)(V - col0)) yc = (int)y;
+      if (y >= 0 && y < vlim) yc = (int)y;
     }
     ycol[tid] = yc;
   }
 
   Gm gm;
   gm.zero();
-  gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, V - col0, 0,
-         H);
+  gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, vlim, 0, H);
   // run() ends on a barrier: the LDS stages are free and ycol is visible.
 
   float4* rec = reinterpret_cast<float4*>(lds);  // [BM][2 chunks] {m, R, B, zy}
@@ -112,7 +115,6 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
   const int cbase = wn * 128;  // this wave's chunk within the group
-  const int vlim = V - col0;
   if (cbase < vlim) {
     bool cvalid[8];
 #pragma unroll
@@ -163,34 +165,82 @@ __device__ __forceinline__ Part shfl_xor_part(const Part& p, int s) {
   return Part{__shfl_xor(p.m, s), __shfl_xor(p.R, s), __shfl_xor(p.B, s), __shfl_xor(p.zy, s)};
 }
 
+// Final outputs of one row from its whole-vocabulary record.
+__device__ __forceinline__ void finalize_row(const Part& acc, bool target_ok, float* logp,
+                                             float* entropy) {
+  const float L = log1pf(acc.R);
+  if (logp) *logp = target_ok ? (acc.zy - acc.m) - L : __builtin_nanf("");
+  if (entropy) *entropy = L - acc.B / (1.f + acc.R);
+}
+
+// One wave per row. Each virtual slice's groups: lane j folds groups j,
+// j + 64, ... of the slice in order, then a 64-lane xor tree (lower lane
+// left); the P slice records then merge by the fixed tree (P = 1, 2 or 4).
 __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(
-    const float4* __restrict__ part, const int32_t* __restrict__ targets, int T, int G,
-    int64_t vocab_total, int full, float* __restrict__ logp, float* __restrict__ entropy,
+    const float4* __restrict__ part, const int32_t* __restrict__ targets, int T, int G, int P,
+    int Gs, int64_t vocab_total, int full, float* __restrict__ logp, float* __restrict__ entropy,
     float4* __restrict__ stats) {
   const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= T) return;
-  Part acc = part_empty();
   const float4* pr = part + (int64_t)row * G;
-  for (int g = lane; g < G; g += 64) {
-    const float4 q = pr[g];
-    acc = part_merge(acc, Part{q.x, q.y, q.z, q.w});
-  }
+  Part rs[kVirtualSlices];
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const Part o = shfl_xor_part(acc, s);
-    acc = (lane & s) ? part_merge(o, acc) : part_merge(acc, o);
+  for (int p = 0; p < kVirtualSlices; ++p) {
+    if (p < P) {
+      Part acc = part_empty();
+      for (int g = lane; g < Gs; g += 64) {
+        const float4 q = pr[p * Gs + g];
+        acc = part_merge(acc, Part{q.x, q.y, q.z, q.w});
+      }
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) {
+        const Part o = shfl_xor_part(acc, s);
+        acc = (lane & s) ? part_merge(o, acc) : part_merge(acc, o);
+      }
+      rs[p] = acc;
+    }
   }
+  Part acc = rs[0];
+  if (P == 2) acc = part_merge(rs[0], rs[1]);
+  if (P == 4) acc = part_merge(part_merge(rs[0], rs[1]), part_merge(rs[2], rs[3]));
   if (lane == 0) {
     if (stats) stats[row] = make_float4(acc.m, acc.R, acc.B, acc.zy);
     if (full) {
-      const float L = log1pf(acc.R);
       const int32_t y = targets[row];
-      const bool ok = y >= 0 && (int64_t)y < vocab_total;
-      if (logp) logp[row] = ok ? (acc.zy - acc.m) - L : __builtin_nanf("");
-      if (entropy) entropy[row] = L - acc.B / (1.f + acc.R);
+      finalize_row(acc, y >= 0 && (int64_t)y < vocab_total, logp ? logp + row : nullptr,
+                   entropy ? entropy + row : nullptr);
     }
   }
+}
+
+// Merge of S slice records per row (slices in vocabulary order) by the fixed
+// tree: a stack of subtrees of decreasing power-of-two sizes, equal
+// neighbours merged left + right as records arrive, the rest folded from the
+// right. One thread per row.
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restrict__ partials,
+                                                           int S, int T, float* __restrict__ logp,
+                                                           float* __restrict__ entropy,
+                                                           float4* __restrict__ stats) {
+  const int row = blockIdx.x * kThreads + threadIdx.x;
+  if (row >= T) return;
+  Part st[kCombineDepth];
+  int lvl[kCombineDepth];
+  int n = 0;
+  for (int s = 0; s < S; ++s) {
+    const float4 q = partials[(int64_t)s * T + row];
+    st[n] = Part{q.x, q.y, q.z, q.w};
+    lvl[n++] = 0;
+    while (n >= 2 && lvl[n - 2] == lvl[n - 1]) {
+      st[n - 2] = part_merge(st[n - 2], st[n - 1]);
+      ++lvl[n - 2];
+      --n;
+    }
+  }
+  Part acc = st[n - 1];
+  for (int i = n - 2; i >= 0; --i) acc = part_merge(st[i], acc);
+  if (stats) stats[row] = make_float4(acc.m, acc.R, acc.B, acc.zy);
+  finalize_row(acc, true, logp ? logp + row : nullptr, entropy ? entropy + row : nullptr);
 }
 
 // ======================================================== backward =======
@@ -319,18 +369,13 @@ DwMap dw_map(int n_vtiles, int n_htiles) {
   return m;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ hidden,
-              int T, int Tp, int H, int V, int chunk_v0, int chunk_w, int n_vtiles, int n_htiles,
-              DwMap map, float* __restrict__ dweight) {
-  using Gm = AsyncGemmKK<256, kDwBN, 2, 2, 3>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
-  const int xcd = blockIdx.x & 7, seq = blockIdx.x >> 3;
-  if (seq >= map.per_xcd) return;
-  const int ht = (xcd % map.groups) * map.h_per_group + seq % map.h_per_group;
-  const int vt = (xcd / map.groups) * map.v_per_xcd + seq / map.h_per_group;
-  if (ht >= n_htiles) return;
-  if (vt >= n_vtiles) return;
+// One dW tile (v-tile vt, h-tile ht) of the chunk; lds holds DwGemm::LDS_BYTES.
+using DwGemm = AsyncGemmKK<256, kDwBN, 2, 2, 3>;
+__device__ __forceinline__ void dw_tile(unsigned char* lds, const uint16_t* __restrict__ gtv,
+                                        int64_t ldg, const uint16_t* __restrict__ hidden, int T,
+                                        int Tp, int H, int V, int chunk_v0, int chunk_w, int vt,
+                                        int ht, float* __restrict__ dweight) {
+  using Gm = DwGemm;
   const int v0 = vt * 256, h0 = ht * kDwBN;
   Gm gm;
   gm.zero();
@@ -357,26 +402,38 @@ bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __r
   }
 }
 
+// (v-tile, h-tile) of the seq-th tile of XCD xcd under `map` (ht >= n_htiles
+// or vt >= n_vtiles: no tile).
+__device__ __forceinline__ void dw_tile_of(const DwMap& map, int xcd, int seq, int& vt, int& ht) {
+  ht = (xcd % map.groups) * map.h_per_group + seq % map.h_per_group;
+  vt = (xcd / map.groups) * map.v_per_xcd + seq / map.h_per_group;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ hidden,
+              int T, int Tp, int H, int V, int chunk_v0, int chunk_w, int n_vtiles, int n_htiles,
+              DwMap map, float* __restrict__ dweight) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[DwGemm::LDS_BYTES];
+  const int seq = blockIdx.x >> 3;
+  if (seq >= map.per_xcd) return;
+  int vt, ht;
+  dw_tile_of(map, blockIdx.x & 7, seq, vt, ht);
+  if (ht >= n_htiles || vt >= n_vtiles) return;
+  dw_tile(lds, gtv, ldg, hidden, T, Tp, H, V, chunk_v0, chunk_w, vt, ht, dweight);
+}
+
 // dH partial of split (split_base + si): rows t of the T-tile, columns h of
 // the H-tile, v over [s_begin, s_end) of the chunk in ascending order (the
 // G columns past V are zeros and the W rows past V read as zero, so the span
 // is rounded up to whole MFMA steps). Work items (t-tile fastest, then
 // h-tile, then split) are dealt to the 8 XCDs in contiguous runs, so one
 // split's G rows and W rows are fetched into one XCD's L2 and reused there.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
-    const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ weight, int T,
-    int H, int V, int chunk_v0, int split_w, int n_splits, int split_base, int n_ttiles,
-    int n_htiles, int per_xcd, float* __restrict__ part) {
-  using Gm = AsyncGemmKN<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
-  const int seq = blockIdx.x >> 3;
-  if (seq >= per_xcd) return;
-  const int w = (blockIdx.x & 7) * per_xcd + seq;
-  if (w >= n_ttiles * n_htiles * n_splits) return;
-  const int tt = w % n_ttiles;
-  const int ht = (w / n_ttiles) % n_htiles;
-  const int si = w / (n_ttiles * n_htiles);
+template <int BM, int BN, int WM, int WN, int NSTG>
+__device__ __forceinline__ void dh_item(unsigned char* lds, const uint16_t* __restrict__ gtv,
+                                        int64_t ldg, const uint16_t* __restrict__ weight, int T,
+                                        int H, int V, int chunk_v0, int split_w, int split_base,
+                                        int tt, int ht, int si, float* __restrict__ part) {
+  using Gm = AsyncGemmKN<BM, BN, WM, WN, NSTG>;
   const int row0 = tt * BM, h0 = ht * BN;
   const int s_begin = si * split_w;
   const int s_end = min(s_begin + split_w, V - chunk_v0);
@@ -403,6 +460,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
         if (hb + 16 * j < H) rowp[16 * j] = gm.acc[i][j][r];
     }
   }
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
+    const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ weight, int T,
+    int H, int V, int chunk_v0, int split_w, int n_splits, int split_base, int n_ttiles,
+    int n_htiles, int per_xcd, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[AsyncGemmKN<BM, BN, WM, WN>::LDS_BYTES];
+  const int seq = blockIdx.x >> 3;
+  if (seq >= per_xcd) return;
+  const int w = (blockIdx.x & 7) * per_xcd + seq;
+  if (w >= n_ttiles * n_htiles * n_splits) return;
+  const int tt = w % n_ttiles;
+  const int ht = (w / n_ttiles) % n_htiles;
+  const int si = w / (n_ttiles * n_htiles);
+  dh_item<BM, BN, WM, WN, 4>(lds, gtv, ldg, weight, T, H, V, chunk_v0, split_w, split_base, tt, ht,
+                             si, part);
 }
 
 // dH = sum_{s=0}^{S-1} part[s] in order; 4 elements per thread.
@@ -437,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 #define RLK_FWD_TILE(BM, WM, WN)                                                              \
   template __global__ void fwd_tile_kernel<BM, WM, WN>(                                       \
       const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__, \
-      int, int, int, int64_t, int, int, float4* __restrict__);
+      int, int, int, int, int64_t, int, int, float4* __restrict__);
 #define RLK_RECOMPUTE(BM, WM, WN)                                                             \
   template __global__ void bwd_recompute_kernel<BM, WM, WN>(                                  \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
@@ -466,19 +540,27 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
   } while (0)
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
-  const int G = cdiv(a.V, GROUP);
+  const FwdSlicing& sl = a.slicing;
+  const int G = sl.G;
   const int G8 = cdiv(G, 8) * 8;
   if (a.T <= kSmallT) {
     const int nt = cdiv(a.T, 32);
     RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<32, 2, 2>), G8 * nt, st, a.hidden, a.weight, a.targets,
-               a.T, a.H, a.V, a.vocab_start, G, nt, a.part);
+               a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, a.part);
   } else {
     const int nt = cdiv(a.T, 256);
     RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2>), G8 * nt, st, a.hidden, a.weight,
-               a.targets, a.T, a.H, a.V, a.vocab_start, G, nt, a.part);
+               a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, a.part);
   }
   RLK_LAUNCH(K_FWD_COMBINE, fwd_combine_kernel, cdiv(a.T, kThreads / 64), st, a.part, a.targets,
-             a.T, G, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
+             a.T, G, sl.P, sl.Gs, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float4* partials, int S, int T, float* logp, float* entropy,
+                          float4* stats, hipStream_t st) {
+  RLK_LAUNCH(K_COMBINE, combine_kernel, cdiv(T, kThreads), st, partials, S, T, logp, entropy,
+             stats);
   return hipGetLastError();
 }
 
@@ -506,15 +588,15 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
     else
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 2, 2>), ng8 * nt, st, a.hidden,
                  a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
+    const int nvt = cdiv(width, 256);
+    const int nhw = cdiv(H, kDwBN);
+    const int nsp = s1 - s0;
     if (a.dweight) {
-      const int nvt = cdiv(width, 256);
-      const int nhw = cdiv(H, kDwBN);
       const DwMap map = dw_map(nvt, nhw);
       RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, 8 * map.per_xcd, st, a.gtv, p.ldg, a.hidden, T, Tp, H,
                  V, v0, ngroups * GROUP, nvt, nhw, map, a.dweight);
     }
     if (a.dhidden) {
-      const int nsp = s1 - s0;
       if (small) {
         const int nh = cdiv(H, 128);
         const int per = cdiv(nt * nh * nsp, 8);

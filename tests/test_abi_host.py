@@ -50,6 +50,56 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(raw, n), n
 
 
+def test_combine_argument_errors(lib):
+    raw = ctypes.CDLL(rlk.LIB_PATH)
+    raw.rlk_linear_logp_combine.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    c = raw.rlk_linear_logp_combine
+    assert c(P, 0, 4, P, P, P, NULL) == INVALID                    # no slices
+    assert c(P, 1025, 4, P, P, P, NULL) == INVALID                 # too many slices
+    assert c(P, 4, -1, P, P, P, NULL) == INVALID
+    assert c(P, 4, 4, NULL, NULL, NULL, NULL) == INVALID           # nothing requested
+    assert c(NULL, 4, 4, P, P, P, NULL) == INVALID
+    assert c(ctypes.c_void_p((1 << 20) + 4), 4, 4, P, P, P, NULL) == INVALID  # misaligned
+    assert c(P, 4, 4, P, P, ctypes.c_void_p((1 << 20) + 4), NULL) == INVALID
+    assert c(P, 4, 0, P, P, P, NULL) == OK                         # T == 0: no-op
+    assert lib.rlk_call_count(3) >= 1
+
+
+def test_combine_host_tree_order():
+    # three records whose merge order is visible in fp32: the tree merges
+    # (r0 + r1) first and then r2, which equals a left fold for S = 3 but
+    # not for S = 4 where (r0 + r1) + (r2 + r3) is the defined order
+    raw = ctypes.CDLL(rlk.LIB_PATH)
+    raw.rlk_linear_logp_combine_host.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    r = np.random.default_rng(11)
+    S, T = 4, 512
+    parts = np.zeros((S, T, 4), dtype=np.float32)
+    parts[..., 0] = r.normal(0, 3, (S, T))
+    parts[..., 1] = r.uniform(0, 50, (S, T))
+    parts[..., 2] = -r.uniform(0, 80, (S, T))
+    parts[..., 3] = -np.inf
+    out = np.zeros((T, 4), dtype=np.float32)
+    raw.rlk_linear_logp_combine_host(parts.ctypes.data, S, T, None, None, out.ctypes.data)
+
+    def merge(a, b):
+        base_left = not (b[0] > a[0])
+        bb, oo = (a, b) if base_left else (b, a)
+        if oo[0] == -np.inf:
+            return bb.copy()
+        d = np.float32(oo[0] - bb[0])
+        e = np.float32(np.exp(np.float64(d)))
+        one_r = np.float32(1) + oo[1]
+        return np.array([bb[0], bb[1] + e * one_r, bb[2] + e * (oo[2] + one_r * d), -np.inf],
+                        dtype=np.float32)
+
+    for t in range(0, T, 37):
+        want = merge(merge(parts[0, t], parts[1, t]), merge(parts[2, t], parts[3, t]))
+        np.testing.assert_allclose(out[t, :3], want[:3], rtol=2e-6)
+
+
 def test_microbench_argument_errors():
     raw = ctypes.CDLL(rlk.LIB_PATH)
     raw.rlk_microbench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -144,8 +194,8 @@ def test_workspace_sizes(lib):
     f = lib.rlk_linear_logp_fwd_workspace_bytes
     assert f(0, 4096, 151936) == 0
     # one 16-byte record per (row, group of 256 columns), rounded to 256 B
-    assert f(512, 4096, 151936) == 512 * 594 * 16
-    assert f(3, 256, 1024) == 256
+    assert f(512, 4096, 151936) == 512 * (594 + 3) * 16  # virtual slices add <= 3 short groups
+    assert f(3, 256, 1024) == 512
     b = lib.rlk_linear_logp_bwd_workspace_bytes
     sizes = [b(T, 4096, 151936, 0, 1) for T in (1, 4, 64, 512, 5208)]
     assert all(x < y for x, y in zip(sizes, sizes[1:]))
