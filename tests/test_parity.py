@@ -202,6 +202,24 @@ def test_qwen512_backward_sampled(qwen):
     check_column_sum(dw, "qwen512")
 
 
+def test_qwen512_backward_entropy_sampled(qwen):
+    # the entropy-regularised objective: dlogp and dentropy both N(0,1)
+    c, d = qwen
+    dent_cpu = torch.randn(c.T, generator=torch.Generator().manual_seed(14), dtype=torch.float32)
+    o = run_fwd(d)
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"],
+                     dent_cpu.cuda())
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(15)
+    rows = torch.randperm(c.T, generator=g)[:48].sort().values.numpy()
+    vrows = np.unique(np.concatenate([torch.randperm(c.V, generator=g)[:128].numpy(),
+                                      c.targets[:48].numpy()]))
+    ref = backward(c.hidden, c.weight, c.targets, c.dlogp, dent_cpu, dh_rows=rows, dw_rows=vrows)
+    check_grad(f64(dh[torch.from_numpy(rows).cuda()]), ref["dH"], "qwen512 dH rows (entropy term)")
+    check_grad(f64(dw[torch.from_numpy(vrows).cuda()]), ref["dW"], "qwen512 dW rows (entropy term)")
+    check_column_sum(dw, "qwen512 (entropy term)")
+
+
 # ------------------------------------------ full size: T = 5208 (full step)
 
 @pytest.mark.slow
