@@ -139,8 +139,14 @@ def microbench(torch, rlk):
         flops[0] = rlk.microbench_mfma(sink, wg, iters)
 
     per, _ = timed(torch, mfma, 2, 5)
-    return {"copy_GBps": round(copy_gbs, 1), "copy_bytes": n,
-            "mfma_bf16_TFLOPs": round(flops[0] / (min(per) * 1e-3) / 1e12, 1),
+    mf = flops[0] / (min(per) * 1e-3) / 1e12
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    per_r, _ = timed(torch, lambda: rlk.microbench_read(src, sink, ncu), 2, 5)
+    read_gbs = n / (min(per_r) * 1e-3) / 1e9
+    del src
+    return {"copy_GBps": round(copy_gbs, 1), "copy_bytes": n, "read_GBps": round(read_gbs, 1),
+            "read_bytes": n,
+            "mfma_bf16_TFLOPs": round(mf, 1),
             "mfma_workgroups": wg, "mfma_iters": iters}
 
 
@@ -149,7 +155,7 @@ def to_dev(torch, c):
     return [x.to(dev).contiguous() for x in (c.hidden, c.weight, c.targets, c.dlogp)]
 
 
-def workload_runs(torch, rlk, wl, copy_gbs, steps):
+def workload_runs(torch, rlk, wl, read_gbs, steps):
     """The tiny case, small-T forwards (+ bitwise check), the 5208-token step
     and one vocabulary slice, timed on the GPU."""
     res = {}
@@ -166,37 +172,69 @@ def workload_runs(torch, rlk, wl, copy_gbs, steps):
     per, _ = timed(torch, step1, 3, steps)
     res["tiny_T64_H256_V1024"] = {"fwd_bwd_ms": median_ci(per), "dentropy": "N(0,1)"}
 
-    # small T: the forward is a stream over W; bytes 2HV + 2TH + 16T per call.
-    # Bitwise check: every batch of T consecutive rows of the 64-row pool
-    # against the 64-row call (logp, entropy and stats bits).
+    # small T (rollout decode batches): the forward is a stream over W; bytes
+    # 2HV + 2TH + 4T + 16T per call (W, hidden, targets, logp+entropy+stats).
+    # Timed over W in its natural layout and over the packed copy (packed
+    # once, its time reported apart). Bitwise check: every batch of T
+    # consecutive rows of the 64-row pool, both layouts, against the same rows
+    # inside the 512-row training batch (the tile path).
     c2w = wl.qwen512().weight.to("cuda:0")
     pool = wl.pool64()
     ph = pool["hidden"].to("cuda:0")
     pt = pool["targets"].to("cuda:0")
+    emb = pool["embed"]
+    pos = emb["positions"].to("cuda:0")
     H, V = c2w.shape[1], c2w.shape[0]
-    ref = rlk.fwd(ph, c2w, pt)
-    ref_bits = {k: ref[k].view(torch.int32).clone() for k in ("logp", "entropy", "stats")}
-    small = {}
+    train = rlk.fwd(emb["hidden"].to("cuda:0"), c2w, emb["targets"].to("cuda:0"))
+    ref_bits = {k: train[k][pos].contiguous().view(torch.int32).clone()
+                for k in ("logp", "entropy", "stats")}
+    pw = rlk.pack_weight(c2w)
+    per, _ = timed(torch, lambda: rlk.pack_weight(c2w, out=pw), 1, 5)
+    small = {"pack_weight_ms": median_ci(per), "packed_bytes": int(pw.data.numel())}
     mismatches, compared = 0, 0
-    for T in (1, 2, 3, 4, 64):
-        fo = {}
+    for T in (1, 2, 3, 4, 16, 64):
         hh, tt = ph[:T].contiguous(), pt[:T].contiguous()
-        per, _ = timed(torch, lambda: rlk.fwd(hh, c2w, tt, out=fo), 3, steps)
-        ms = median_ci(per)
-        byts = 2 * H * V + 2 * T * H + 16 * T
-        gbs = byts / (ms["median"] * 1e-3) / 1e9
-        small[f"T{T}"] = {"fwd_ms": ms, "bytes": byts, "GBps": round(gbs, 1),
-                          "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                          "frac_measured_copy": round(gbs / copy_gbs, 4) if copy_gbs else None}
+        byts = 2 * H * V + 2 * T * H + 20 * T + 8 * T
+        row = {"bytes": byts}
+        for name, fn in (("natural", lambda o: rlk.fwd(hh, c2w, tt, out=o)),
+                         ("packed", lambda o: rlk.fwd_packed(hh, pw, tt, out=o))):
+            fo = {}
+            per, _ = timed(torch, lambda: fn(fo), 3, steps)
+            ms = median_ci(per)
+            gbs = byts / (ms["median"] * 1e-3) / 1e9
+            row[name] = {"fwd_ms": ms, "GBps": round(gbs, 1),
+                         "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                         "frac_measured_read": round(gbs / read_gbs, 4) if read_gbs else None}
+        small[f"T{T}"] = row
         for s0 in range(0, 64 - T + 1, T):
-            o = rlk.fwd(ph[s0:s0 + T].contiguous(), c2w, pt[s0:s0 + T].contiguous())
-            for k in ("logp", "entropy", "stats"):
-                d = o[k].view(torch.int32) != ref_bits[k][s0:s0 + T]
-                mismatches += int(d.sum())
-                compared += d.numel()
-    small["bitwise"] = {"mismatched_words": mismatches, "compared_words": compared}
+            hs, ts = ph[s0:s0 + T].contiguous(), pt[s0:s0 + T].contiguous()
+            for o in (rlk.fwd(hs, c2w, ts), rlk.fwd_packed(hs, pw, ts)):
+                for k in ("logp", "entropy", "stats"):
+                    d = o[k].view(torch.int32) != ref_bits[k][s0:s0 + T]
+                    mismatches += int(d.sum())
+                    compared += d.numel()
+    small["bitwise_vs_training_batch"] = {"mismatched_words": mismatches,
+                                          "compared_words": compared}
     res["small_T_forward_H4096_V151936"] = small
-    del c2w, ref
+    del c2w, pw, train
+
+    # the entropy-regularised objective at T = 512: dlogp and dentropy both N(0,1)
+    c = wl.qwen512()
+    h, w, y, dl = to_dev(torch, c)
+    de = torch.randn(c.T, generator=torch.Generator().manual_seed(14)).to("cuda:0")
+    fo, bo = {}, {}
+
+    def step_ent():
+        o = rlk.fwd(h, w, y, out=fo)
+        rlk.bwd(h, w, y, o["stats"], dl, de, out=bo)
+
+    per, _ = timed(torch, step_ent, 3, steps)
+    ms = median_ci(per)
+    fl = 8.0 * c.T * c.H * c.V
+    res["entropy_regularised_T512_H4096_V151936"] = {
+        "fwd_bwd_ms": ms, "tokens_per_s": round(c.T / (ms["median"] * 1e-3), 1),
+        "TFLOPs": round(fl / (ms["median"] * 1e-3) / 1e12, 1), "dentropy": "N(0,1), seed 14"}
+    del h, w, y, dl, de, fo, bo
 
     # the 5208-token step (8 sequences), fwd+bwd
     c = wl.step5208()
@@ -278,9 +316,12 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="only the T=512 step (no microbenchmarks, other workloads or clocks)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
-    ap.add_argument("--profile-case", choices=["fwd_t1"], default=None,
+    ap.add_argument("--profile-case", choices=["fwd_t1", "fwd_packed_t1", "fwd_packed_t64", "read"],
+                    default=None,
                     help="run only this case's calls (warmup + steps), for profilers: fwd_t1 = "
-                         "the T=1 forward over the full vocabulary")
+                         "the T=1 forward over the full vocabulary (natural layout), "
+                         "fwd_packed_t1 / _t64 = the same over the packed weight with 1 / 64 rows, "
+                         "read = the 1 GiB streaming-read microbenchmark")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -311,13 +352,26 @@ def main():
         return
     rlk.load_library()
     c = wl.qwen512()
-    if args.profile_case == "fwd_t1":
+    if args.profile_case == "read":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        sink = torch.zeros(4, dtype=torch.float32, device="cuda:0")
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        per, _ = timed(torch, lambda: rlk.microbench_read(src, sink, ncu), args.warmup, args.steps)
+        print(json.dumps({"profile_case": "read", "ms": median_ci(per)}), flush=True)
+        return
+    if args.profile_case is not None:
         w = c.weight.to("cuda:0")
         pool = wl.pool64()
-        h1, y1 = pool["hidden"][:1].to("cuda:0"), pool["targets"][:1].to("cuda:0")
+        nrow = 64 if args.profile_case.endswith("t64") else 1
+        h1, y1 = pool["hidden"][:nrow].to("cuda:0"), pool["targets"][:nrow].to("cuda:0")
         fo1 = {}
-        per, _ = timed(torch, lambda: rlk.fwd(h1, w, y1, out=fo1), args.warmup, args.steps)
-        print(json.dumps({"profile_case": "fwd_t1", "fwd_ms": median_ci(per)}), flush=True)
+        if args.profile_case == "fwd_t1":
+            fn = lambda: rlk.fwd(h1, w, y1, out=fo1)  # noqa: E731
+        else:
+            pw = rlk.pack_weight(w)
+            fn = lambda: rlk.fwd_packed(h1, pw, y1, out=fo1)  # noqa: E731
+        per, _ = timed(torch, fn, args.warmup, args.steps)
+        print(json.dumps({"profile_case": args.profile_case, "fwd_ms": median_ci(per)}), flush=True)
         return
     T, H, V = c.T, c.H, c.V
     hidden, weight, targets, dlogp = to_dev(torch, c)
@@ -399,7 +453,7 @@ def main():
         mb = microbench(torch, rlk)
         result["microbench"] = mb
         result["frac_measured_mfma"] = round(tflops / mb["mfma_bf16_TFLOPs"], 4)
-        result["workloads"] = workload_runs(torch, rlk, wl, mb["copy_GBps"], args.steps)
+        result["workloads"] = workload_runs(torch, rlk, wl, mb["read_GBps"], args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl.qwen512(), min(args.cpu_rows, T))
     else:

@@ -100,7 +100,8 @@ typedef enum rlk_status {
 
 /* Bytes of device workspace the forward needs for (T, H, V): one 16-byte
  * record per row and group of 256 columns, (ceil(V/256) + 3) groups at most,
- * rounded up to 256 bytes. 0 when T == 0. */
+ * two records per group (one per 128-column half) when T <= 64, rounded up
+ * to 256 bytes. 0 when T == 0. */
 RLK_API size_t rlk_linear_logp_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V);
 
 /* Bytes of device workspace the backward needs for (T, H, V, flags, whether
@@ -123,6 +124,52 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
                                        int64_t vocab_start, int64_t vocab_total, float* logp,
                                        float* entropy, float* stats, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/* Packed weight for the streaming forward.
+ *
+ * Rollout calls the forward with a few rows at a time (the decode batch) and
+ * a weight that stays fixed for the whole rollout, so the forward is a read
+ * of W at the HBM rate. In its natural [V,H] layout the library reads W as
+ * 64-byte pieces of 128 rows at a time (one MFMA k-step of one 128-row unit);
+ * the packed copy holds the same elements in the order the stream consumes
+ * them, so each step reads 8 KB that are contiguous, a pattern HBM serves
+ * markedly faster. Values, arithmetic and results are identical: the forward
+ * over the packed copy returns the same bits as rlk_linear_logp_fwd over W.
+ *
+ * Layout (for the slicing the forward derives from V, vocab_start and
+ * vocab_total: see tensor-parallel invariance above): the call's rows form P
+ * slices of Vs rows; unit iu of slice p is slice rows 128 iu .. 128 iu + 127,
+ * units numbered pu = p * ceil(Vs/128) + iu, each 128 * H bf16 at offset
+ * pu * 128 * H. Inside a unit, k-step s (elements 32 s .. 32 s + 31 of each
+ * row) is 4096 bf16 at offset 4096 s; inside a step, 16-byte piece i of
+ * 1 KB block b holds row 16 b + i / 4 and 8-element piece
+ * (i % 4) XOR (((r >> 1) XOR (r >> 3)) & 3) with r = i / 4. Rows past the
+ * slice are zero. The layout is tied to (H, V, vocab_start, vocab_total):
+ * pack and use with the same four values. */
+RLK_API size_t rlk_linear_pack_weight_bytes(int64_t H, int64_t V, int64_t vocab_start,
+                                            int64_t vocab_total);
+/* weight bf16 [V,H] (16-byte aligned); packed: device buffer of packed_bytes >=
+ * rlk_linear_pack_weight_bytes(...), 16-byte aligned, written on `stream`.
+ * Errors as the forward's shape and argument checks;
+ * RLK_ERR_WORKSPACE_TOO_SMALL if packed_bytes is short. */
+RLK_API rlk_status rlk_linear_pack_weight(const void* weight, int64_t H, int64_t V,
+                                          int64_t vocab_start, int64_t vocab_total, void* packed,
+                                          size_t packed_bytes, void* stream);
+/* Workspace of the packed forward: two 16-byte records per row and group. */
+RLK_API size_t rlk_linear_logp_fwd_packed_workspace_bytes(int64_t T, int64_t H, int64_t V);
+/* The forward over a packed weight: arguments and results as
+ * rlk_linear_logp_fwd, with packed_weight/packed_bytes from
+ * rlk_linear_pack_weight for the same (H, V, vocab_start, vocab_total)
+ * (RLK_ERR_INVALID_ARG if packed_bytes is short) and the workspace from
+ * rlk_linear_logp_fwd_packed_workspace_bytes. Any T works; W is streamed once
+ * per 64 rows, so it is meant for T <= 64 (decode batches). */
+RLK_API rlk_status rlk_linear_logp_fwd_packed(const void* hidden, const void* packed_weight,
+                                              size_t packed_bytes, const int32_t* targets,
+                                              int64_t T, int64_t H, int64_t V,
+                                              int64_t vocab_start, int64_t vocab_total,
+                                              float* logp, float* entropy, float* stats,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream);
 
 /* Backward.
  *   hidden, weight, targets, T, H, V, vocab_start, vocab_total: as in the forward
@@ -172,7 +219,7 @@ RLK_API rlk_status rlk_linear_logp_combine_host(const float* partials, int64_t S
 RLK_API const char* rlk_status_string(int status);
 RLK_API const char* rlk_backend_id(void);
 /* Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host,
- * 3 combine. */
+ * 3 combine, 4 pack_weight, 5 fwd_packed. */
 RLK_API uint64_t rlk_call_count(int which);
 RLK_API int rlk_abi_version(void);
 

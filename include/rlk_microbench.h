@@ -1,5 +1,5 @@
 /* rlk_microbench.h — on-device microbenchmarks that give the measured
- * denominators of the roofline figures: sustained HBM copy bandwidth and the
+ * denominators of the roofline figures: sustained HBM copy and read bandwidth and the
  * sustained dense bf16 MFMA rate of the same v_mfma_f32_16x16x32_bf16
  * instruction the GEMM kernels use. They are measurement tools, not part of
  * the linear log-prob path.
@@ -23,6 +23,14 @@ extern "C" {
  * device pointers 16-byte aligned, not overlapping. One read and one write
  * of every byte: count 2 * bytes of HBM traffic. */
 RLK_API rlk_status rlk_microbench_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Reads `bytes` bytes of src (device, 16-byte aligned; a multiple of 8192, at
+ * most 2^40) once, linearly, into LDS through LDS-DMA and discards them:
+ * `workgroups` workgroups (1 .. 2^20; one per compute unit is the intended
+ * use) each stream 1 MB runs over a ring of eight 8 KB stages. Counts
+ * `bytes` of HBM traffic. sink as for rlk_microbench_mfma. */
+RLK_API rlk_status rlk_microbench_read(const void* src, size_t bytes, float* sink, int64_t workgroups,
+                                       void* stream);
 
 /* Back-to-back independent bf16 MFMAs (16x16x32, fp32 accumulate) on every
  * SIMD: `workgroups` workgroups of 4 waves, each wave `iters` rounds of 32

@@ -11,6 +11,7 @@ calls raise.
     dH, dW = bwd(hidden, weight, targets, out["stats"], dlogp)      # gradients
     parts = fwd(hidden, W_slice, targets, vocab_start=a, vocab_total=V)["stats"]
     logp, entropy, stats = combine_host([parts_0, parts_1, ...])    # fixed-order merge
+    pw = pack_weight(W); out = fwd_packed(hidden, pw, targets)       # rollout: same bits as fwd
 
 The operator is the linear-logp provider of the pages on RL-Kernel (page
 "VIME Qwen3-8B TP4/CP2 200-round consistency experiment", section
@@ -63,6 +64,15 @@ def load_library(path: str | None = None):
     lib.rlk_linear_logp_fwd.argtypes = [vp, vp, i32p, i64, i64, i64, i64, i64, f32p, f32p, f32p,
                                         vp, sz, vp]
     lib.rlk_linear_logp_fwd.restype = ctypes.c_int
+    lib.rlk_linear_logp_fwd_packed_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.rlk_linear_logp_fwd_packed_workspace_bytes.restype = sz
+    lib.rlk_linear_pack_weight_bytes.argtypes = [i64, i64, i64, i64]
+    lib.rlk_linear_pack_weight_bytes.restype = sz
+    lib.rlk_linear_pack_weight.argtypes = [vp, i64, i64, i64, i64, vp, sz, vp]
+    lib.rlk_linear_pack_weight.restype = ctypes.c_int
+    lib.rlk_linear_logp_fwd_packed.argtypes = [vp, vp, sz, i32p, i64, i64, i64, i64, i64, f32p,
+                                               f32p, f32p, vp, sz, vp]
+    lib.rlk_linear_logp_fwd_packed.restype = ctypes.c_int
     lib.rlk_linear_logp_bwd.argtypes = [vp, vp, i32p, i64, i64, i64, i64, i64, f32p, f32p, f32p,
                                         vp, f32p, u32, vp, sz, vp]
     lib.rlk_linear_logp_bwd.restype = ctypes.c_int
@@ -88,6 +98,8 @@ def load_library(path: str | None = None):
     lib.rlk_profile_kernel_name.restype = ctypes.c_char_p
     lib.rlk_microbench_copy.argtypes = [vp, vp, sz, vp]
     lib.rlk_microbench_copy.restype = ctypes.c_int
+    lib.rlk_microbench_read.argtypes = [vp, sz, vp, i64, vp]
+    lib.rlk_microbench_read.restype = ctypes.c_int
     lib.rlk_microbench_mfma.argtypes = [vp, i64, i64, vp]
     lib.rlk_microbench_mfma.restype = ctypes.c_int
     if path is None:
@@ -140,6 +152,12 @@ def microbench_copy(dst: torch.Tensor, src: torch.Tensor):
     _check(load_library().rlk_microbench_copy(_ptr(dst), _ptr(src), src.nbytes, _stream(src.device)))
 
 
+def microbench_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int):
+    """Linear LDS-DMA read of src (a multiple of 8 KB); see rlk_microbench.h."""
+    _check(load_library().rlk_microbench_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                              workgroups, _stream(src.device)))
+
+
 def microbench_mfma(sink: torch.Tensor, workgroups: int, iters: int) -> float:
     """Enqueue the MFMA-rate kernel; returns the flops it performs."""
     if not (sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= 4):
@@ -178,6 +196,28 @@ def _check_inputs(hidden, weight, targets):
             raise ValueError(f"{name} must be a contiguous device tensor")
 
 
+def _outputs(out: dict, T: int, full: bool, want_logp: bool, want_entropy: bool,
+             want_stats: bool, dev):
+    logp = _reuse(out, "logp", (T,), torch.float32) if full and want_logp else None
+    ent = _reuse(out, "entropy", (T,), torch.float32) if full and want_entropy else None
+    stats = _reuse(out, "stats", (T, 4), torch.float32) if want_stats or not full else None
+    if full and want_logp and logp is None:
+        logp = torch.empty(T, dtype=torch.float32, device=dev)
+    if full and want_entropy and ent is None:
+        ent = torch.empty(T, dtype=torch.float32, device=dev)
+    if (want_stats or not full) and stats is None:
+        stats = torch.empty(T, 4, dtype=torch.float32, device=dev)
+    return logp, ent, stats
+
+
+def _fwd_workspace(out: dict, key: str, nws: int, dev) -> torch.Tensor:
+    ws = out.get(key)
+    if ws is None or ws.numel() < nws:
+        ws = _workspace(nws, dev)
+    out[key] = ws
+    return ws
+
+
 def fwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, *,
         vocab_start: int = 0, vocab_total: int | None = None, want_logp: bool = True,
         want_entropy: bool = True, want_stats: bool = True, out: dict | None = None):
@@ -194,23 +234,71 @@ def fwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, *,
     full = vocab_start == 0 and V == vt
     dev = hidden.device
     out = {} if out is None else out
-    logp = _reuse(out, "logp", (T,), torch.float32) if full and want_logp else None
-    ent = _reuse(out, "entropy", (T,), torch.float32) if full and want_entropy else None
-    stats = _reuse(out, "stats", (T, 4), torch.float32) if want_stats or not full else None
-    if full and want_logp and logp is None:
-        logp = torch.empty(T, dtype=torch.float32, device=dev)
-    if full and want_entropy and ent is None:
-        ent = torch.empty(T, dtype=torch.float32, device=dev)
-    if (want_stats or not full) and stats is None:
-        stats = torch.empty(T, 4, dtype=torch.float32, device=dev)
-    nws = lib.rlk_linear_logp_fwd_workspace_bytes(T, H, V)
-    ws = out.get("_ws_fwd")
-    if ws is None or ws.numel() < nws:
-        ws = _workspace(nws, dev)
-    out.update({"logp": logp, "entropy": ent, "stats": stats, "_ws_fwd": ws})
+    logp, ent, stats = _outputs(out, T, full, want_logp, want_entropy, want_stats, dev)
+    ws = _fwd_workspace(out, "_ws_fwd", lib.rlk_linear_logp_fwd_workspace_bytes(T, H, V), dev)
+    out.update({"logp": logp, "entropy": ent, "stats": stats})
     _check(lib.rlk_linear_logp_fwd(_ptr(hidden), _ptr(weight), _ptr(targets), T, H, V,
                                    vocab_start, vt, _ptr(logp), _ptr(ent), _ptr(stats),
                                    _ptr(ws), ws.numel(), _stream(dev)))
+    return {"logp": logp, "entropy": ent, "stats": stats}
+
+
+class PackedWeight:
+    """W rearranged by ``rlk_linear_pack_weight`` for (H, V, vocab_start, vocab_total)."""
+
+    def __init__(self, data: torch.Tensor, H: int, V: int, vocab_start: int, vocab_total: int):
+        self.data, self.H, self.V = data, H, V
+        self.vocab_start, self.vocab_total = vocab_start, vocab_total
+
+
+def pack_weight_bytes(H: int, V: int, vocab_start: int = 0, vocab_total: int | None = None) -> int:
+    vt = V if vocab_total is None else vocab_total
+    return int(load_library().rlk_linear_pack_weight_bytes(H, V, vocab_start, vt))
+
+
+def pack_weight(weight: torch.Tensor, *, vocab_start: int = 0, vocab_total: int | None = None,
+                out: PackedWeight | None = None) -> PackedWeight:
+    """Packed copy of ``weight`` for ``fwd_packed`` (same slicing arguments)."""
+    lib = load_library()
+    if weight.dtype != torch.bfloat16 or not weight.is_cuda or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous bfloat16 device tensor")
+    V, H = weight.shape
+    vt = V if vocab_total is None else vocab_total
+    nbytes = lib.rlk_linear_pack_weight_bytes(H, V, vocab_start, vt)
+    if nbytes == 0:
+        raise RlkError(1, "pack_weight: unsupported shape or slicing")
+    data = out.data if out is not None and out.data.numel() >= nbytes else None
+    if data is None:
+        data = torch.empty(nbytes, dtype=torch.uint8, device=weight.device)
+    _check(lib.rlk_linear_pack_weight(_ptr(weight), H, V, vocab_start, vt, _ptr(data), data.numel(),
+                                      _stream(weight.device)))
+    return PackedWeight(data, H, V, vocab_start, vt)
+
+
+def fwd_packed(hidden: torch.Tensor, packed: PackedWeight, targets: torch.Tensor, *,
+               want_logp: bool = True, want_entropy: bool = True, want_stats: bool = True,
+               out: dict | None = None):
+    """Forward through ``rlk_linear_logp_fwd_packed``: same results, bit for bit, as
+    ``fwd`` over the weight ``packed`` was made from."""
+    lib = load_library()
+    if hidden.dtype != torch.bfloat16 or targets.dtype != torch.int32:
+        raise TypeError("hidden must be bfloat16 and targets int32")
+    for name, t in (("hidden", hidden), ("targets", targets)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    T, H = hidden.shape
+    if H != packed.H:
+        raise ValueError(f"hidden has H={H}, the packed weight H={packed.H}")
+    V, vs0, vt = packed.V, packed.vocab_start, packed.vocab_total
+    full = vs0 == 0 and V == vt
+    dev = hidden.device
+    out = {} if out is None else out
+    logp, ent, stats = _outputs(out, T, full, want_logp, want_entropy, want_stats, dev)
+    ws = _fwd_workspace(out, "_ws_fwdp", lib.rlk_linear_logp_fwd_packed_workspace_bytes(T, H, V), dev)
+    out.update({"logp": logp, "entropy": ent, "stats": stats})
+    _check(lib.rlk_linear_logp_fwd_packed(_ptr(hidden), _ptr(packed.data), packed.data.numel(),
+                                          _ptr(targets), T, H, V, vs0, vt, _ptr(logp), _ptr(ent),
+                                          _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
     return {"logp": logp, "entropy": ent, "stats": stats}
 
 

@@ -17,7 +17,7 @@ namespace {
 constexpr int kAbiVersion = 1;
 const char kBackendId[] = "rlk.linear_logp.bitwise.gfx950.v1";
 
-std::atomic<uint64_t> g_calls[4];
+std::atomic<uint64_t> g_calls[6];
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -34,20 +34,30 @@ rlk_status check_shape(int64_t T, int64_t H, int64_t V, int64_t vocab_start, int
   return RLK_OK;
 }
 
-// The kernels are built for gfx950 only; refuse anything else.
-rlk_status check_device() {
+// The kernels are built for gfx950 only; refuse anything else. On success
+// *n_cu (if given) receives the current device's compute-unit count.
+rlk_status check_device(int* n_cu = nullptr) {
   static std::atomic<int> cache[256];  // 0 unknown, 1 gfx950, 2 other
+  static std::atomic<int> cus[256];
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return RLK_ERR_HIP;
   if (dev < 256) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c == 1) return RLK_OK;
+    const int c = cache[dev].load(std::memory_order_acquire);
     if (c == 2) return RLK_ERR_UNSUPPORTED_DEVICE;
+    if (c == 1) {
+      if (n_cu) *n_cu = cus[dev].load(std::memory_order_relaxed);
+      return RLK_OK;
+    }
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return RLK_ERR_HIP;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 256) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  const int ncu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 0;
+  if (dev < 256) {
+    cus[dev].store(ncu, std::memory_order_relaxed);
+    cache[dev].store(ok ? 1 : 2, std::memory_order_release);
+  }
+  if (ok && n_cu) *n_cu = ncu;
   return ok ? RLK_OK : RLK_ERR_UNSUPPORTED_DEVICE;
 }
 
@@ -86,8 +96,8 @@ namespace rlk {
 int check_device_status() { return (int)check_device(); }
 
 const char* const kKernelNames[K_COUNT] = {
-    "fwd_tile", "fwd_combine", "bwd_rowprep", "bwd_recompute",
-    "bwd_dw",   "bwd_dh",      "bwd_dh_reduce", "fill_zero", "combine"};
+    "fwd_tile",  "fwd_combine", "bwd_rowprep", "bwd_recompute", "bwd_dw",     "bwd_dh",
+    "bwd_dh_reduce", "fill_zero", "combine",   "fwd_stream",    "pack_weight"};
 
 void prof_before(int id, hipStream_t st) {
   if (!g_prof.on.load(std::memory_order_relaxed)) return;
@@ -114,12 +124,17 @@ void prof_after(int id, hipStream_t st) {
   g_prof.recs.back().b = e;
 }
 
-size_t fwd_workspace(int64_t T, int64_t H, int64_t V) {
+size_t fwd_workspace(int64_t T, int64_t H, int64_t V, bool packed) {
   (void)H;
   if (T <= 0) return 0;
-  // P virtual slices of V / P rows take at most ceil(V/256) + P - 1 groups
+  // P virtual slices of V / P rows take at most ceil(V/256) + P - 1 groups;
+  // the stream path keeps one record per 128-column half of a group
   const int64_t G = ceil_div(V, 256) + kVirtualSlices - 1;
-  return align256(size_t(T) * size_t(G) * 16);
+  return align256(size_t(T) * size_t(G) * (packed || T <= kSmallT ? 2 : 1) * 16);
+}
+
+size_t packed_weight_bytes(int64_t H, const FwdSlicing& sl) {
+  return size_t(sl.P) * size_t(ceil_div(sl.Vs, 128)) * 128 * size_t(H) * 2;
 }
 
 FwdSlicing fwd_slicing(int64_t V, int64_t vocab_start, int64_t vocab_total) {
@@ -168,7 +183,35 @@ extern "C" {
 
 RLK_API size_t rlk_linear_logp_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V) {
   if (T <= 0 || H <= 0 || V <= 0) return 0;
-  return rlk::fwd_workspace(T, H, V);
+  return rlk::fwd_workspace(T, H, V, false);
+}
+
+RLK_API size_t rlk_linear_logp_fwd_packed_workspace_bytes(int64_t T, int64_t H, int64_t V) {
+  if (T <= 0 || H <= 0 || V <= 0) return 0;
+  return rlk::fwd_workspace(T, H, V, true);
+}
+
+RLK_API size_t rlk_linear_pack_weight_bytes(int64_t H, int64_t V, int64_t vocab_start,
+                                            int64_t vocab_total) {
+  if (check_shape(0, H, V, vocab_start, vocab_total) != RLK_OK) return 0;
+  return rlk::packed_weight_bytes(H, rlk::fwd_slicing(V, vocab_start, vocab_total));
+}
+
+RLK_API rlk_status rlk_linear_pack_weight(const void* weight, int64_t H, int64_t V,
+                                          int64_t vocab_start, int64_t vocab_total, void* packed,
+                                          size_t packed_bytes, void* stream) {
+  rlk_status s = check_shape(0, H, V, vocab_start, vocab_total);
+  if (s != RLK_OK) return s;
+  if (!weight || !aligned(weight, 16) || !packed || !aligned(packed, 16)) return RLK_ERR_INVALID_ARG;
+  const rlk::FwdSlicing sl = rlk::fwd_slicing(V, vocab_start, vocab_total);
+  if (packed_bytes < rlk::packed_weight_bytes(H, sl)) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  s = check_device();
+  if (s != RLK_OK) return s;
+  if (rlk::launch_pack(static_cast<const uint16_t*>(weight), (int)H, sl,
+                       static_cast<uint16_t*>(packed), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return RLK_ERR_HIP;
+  g_calls[4].fetch_add(1, std::memory_order_relaxed);
+  return RLK_OK;
 }
 
 RLK_API size_t rlk_linear_logp_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V,
@@ -178,11 +221,14 @@ RLK_API size_t rlk_linear_logp_bwd_workspace_bytes(int64_t T, int64_t H, int64_t
   return rlk::bwd_plan(T, H, V, want_dhidden != 0).total;
 }
 
-RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
-                                       const int32_t* targets, int64_t T, int64_t H, int64_t V,
-                                       int64_t vocab_start, int64_t vocab_total, float* logp,
-                                       float* entropy, float* stats, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+namespace {
+// The forward for the natural layout (packed_bytes == 0) or the packed one.
+rlk_status fwd_call(const void* hidden, const void* weight, bool packed, size_t packed_bytes,
+                    const int32_t* targets, int64_t T, int64_t H, int64_t V, int64_t vocab_start,
+                    int64_t vocab_total, float* logp, float* entropy, float* stats,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const int counter = packed ? 5 : 0;
+
   rlk_status s = check_shape(T, H, V, vocab_start, vocab_total);
   if (s != RLK_OK) return s;
   const bool full = vocab_start == 0 && V == vocab_total;
@@ -190,20 +236,26 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
   if (!logp && !entropy && !stats) return RLK_ERR_INVALID_ARG;
   if (!weight || !aligned(weight, 16)) return RLK_ERR_INVALID_ARG;
   if (T == 0) {
-    g_calls[0].fetch_add(1, std::memory_order_relaxed);
+    g_calls[counter].fetch_add(1, std::memory_order_relaxed);
     return RLK_OK;
   }
   if (!hidden || !aligned(hidden, 16) || !targets || !aligned(targets, 4)) return RLK_ERR_INVALID_ARG;
   if ((logp && !aligned(logp, 4)) || (entropy && !aligned(entropy, 4)) ||
       (stats && !aligned(stats, 16)))
     return RLK_ERR_INVALID_ARG;
-  const size_t need = rlk::fwd_workspace(T, H, V);
+  if (packed &&
+      packed_bytes < rlk::packed_weight_bytes(H, rlk::fwd_slicing(V, vocab_start, vocab_total)))
+    return RLK_ERR_INVALID_ARG;
+  const size_t need = rlk::fwd_workspace(T, H, V, packed);
   if (workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 16)) return RLK_ERR_INVALID_ARG;
-  s = check_device();
+  int n_cu = 0;
+  s = check_device(&n_cu);
   if (s != RLK_OK) return s;
 
   rlk::FwdArgs a{};
+  a.n_cu = n_cu;
+  a.packed = packed ? 1 : 0;
   a.hidden = static_cast<const uint16_t*>(hidden);
   a.weight = static_cast<const uint16_t*>(weight);
   a.targets = targets;
@@ -219,9 +271,32 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
   a.stats = reinterpret_cast<float4*>(stats);
   a.part = static_cast<float4*>(workspace);
   if (rlk::launch_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return RLK_ERR_HIP;
-  g_calls[0].fetch_add(1, std::memory_order_relaxed);
+  g_calls[counter].fetch_add(1, std::memory_order_relaxed);
   return RLK_OK;
 }
+}  // namespace
+
+RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
+                                       const int32_t* targets, int64_t T, int64_t H, int64_t V,
+                                       int64_t vocab_start, int64_t vocab_total, float* logp,
+                                       float* entropy, float* stats, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return fwd_call(hidden, weight, false, 0, targets, T, H, V, vocab_start, vocab_total, logp,
+                  entropy, stats, workspace, workspace_bytes, stream);
+}
+
+RLK_API rlk_status rlk_linear_logp_fwd_packed(const void* hidden, const void* packed_weight,
+                                              size_t packed_bytes, const int32_t* targets,
+                                              int64_t T, int64_t H, int64_t V,
+                                              int64_t vocab_start, int64_t vocab_total,
+                                              float* logp, float* entropy, float* stats,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  return fwd_call(hidden, packed_weight, true, packed_bytes, targets, T, H, V, vocab_start,
+                  vocab_total, logp, entropy, stats, workspace, workspace_bytes, stream);
+}
+
+
 
 RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
                                        const int32_t* targets, int64_t T, int64_t H, int64_t V,
@@ -375,7 +450,7 @@ RLK_API const char* rlk_status_string(int status) {
 RLK_API const char* rlk_backend_id(void) { return kBackendId; }
 
 RLK_API uint64_t rlk_call_count(int which) {
-  if (which < 0 || which > 3) return 0;
+  if (which < 0 || which > 5) return 0;
   return g_calls[which].load(std::memory_order_relaxed);
 }
 

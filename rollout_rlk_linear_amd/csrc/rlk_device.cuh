@@ -225,7 +225,7 @@ __device__ __forceinline__ void barrier_only() {
 // start. WM x WN waves (4 or 8); wave (wm, wn) owns rows wm*WTM.. and
 // columns wn*WTN.. of the tile, and acc[i][j][r] is element
 // (row wm*WTM + 16 i + 4 (lane / 16) + r, col wn*WTN + 16 j + lane % 16).
-// NSTG slots (3 or 4) of LDS ring.
+// NSTG slots (3 to 8) of LDS ring.
 //
 // run() is the whole loop for a workgroup of WM x WN waves. setup(),
 // issue(), wait_for() and compute() are its steps, for kernels that drive
@@ -236,7 +236,7 @@ struct AsyncGemm {
   static constexpr int NW = WM * WN;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per tile");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row DMA blocks");
-  static_assert(NSTG == 3 || NSTG == 4, "3- or 4-slot ring");
+  static_assert(NSTG >= 3 && NSTG <= 8, "3- to 8-slot ring");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NJ = WTN / 16;
   static constexpr int NST = NSTG;
@@ -380,80 +380,19 @@ struct AsyncGemm {
     }
   }
 
-  // Fragments of stage s from LDS into registers (no wait).
-  __device__ __forceinline__ void read_frags(int s, bf16x8 (&af)[MI], bf16x8 (&bfr)[NJ]) const {
-    const unsigned char* st = lds_ + (s % NST) * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      af[i] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * i) * ROWB + foff_));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      bfr[j] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn_ * WTN + 16 * j) * ROWB + foff_));
-  }
-
-  __device__ __forceinline__ void mfmas(const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ]) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  }
-
-  // One workgroup of NW waves with fragment double-buffering: the fragments
-  // of stage s+1 are read from LDS while the MFMAs of stage s run. Before the
-  // barrier of step s every wave has its stage-s fragments in registers
-  // (lgkmcnt(0)), so after it slot s may be refilled: stage s+NST is issued
-  // there, NST-1 stages ahead of the one being read.
-  __device__ __forceinline__ void run_db(unsigned char* lds, const uint16_t* A, int64_t lda,
-                                         int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
-                                         int k_begin, int k_end) {
-    const int n = setup(lds, A, lda, a_rows, B, ldb, b_rows, k_begin, k_end, wave_id());
-    if (n <= 0) return;
-    prologue();
-    if (NST - 1 < n) issue(NST - 1);
-    wait_until(0, NST - 1);
-    barrier_only();
-    bf16x8 a0[MI], b0[NJ], a1[MI], b1[NJ];
-    read_frags(0, a0, b0);
-    int s = 0;
-    for (; s + 1 < n; s += 2) {
-      step_db(s, n, a0, b0, a1, b1);
-      step_db(s + 1, n, a1, b1, a0, b0);
-    }
-    if (s < n) step_db(s, n, a0, b0, a1, b1);
-    wait_vmcnt<0>();
-    __syncthreads();
-  }
-
   // Wait for this wave's DMA of stage `want` when stages up to `last`
   // (clamped to the final stage) have been issued and nothing else is pending.
   __device__ __forceinline__ void wait_until(int want, int last) {
     last = last < nsteps_ - 1 ? last : nsteps_ - 1;
-    const int after = last - want;
-    if (after >= 3)
-      wait_vmcnt<3 * NI_W_MIN>();
-    else if (after == 2)
-      wait_vmcnt<2 * NI_W_MIN>();
-    else if (after == 1)
-      wait_vmcnt<NI_W_MIN>();
-    else
-      wait_vmcnt<0>();
-  }
-
-  __device__ __forceinline__ void step_db(int s, int n, const bf16x8 (&ac)[MI],
-                                          const bf16x8 (&bc)[NJ], bf16x8 (&an)[MI],
-                                          bf16x8 (&bn)[NJ]) {
-    if (s + 1 < n) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): stage-s fragments are in registers
-      wait_until(s + 1, s + NST - 1);
-      barrier_only();
-      if (s + NST < n) issue(s + NST);
-      read_frags(s + 1, an, bn);
+    switch (last - want) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<NI_W_MIN>(); break;
+      case 2: wait_vmcnt<2 * NI_W_MIN>(); break;
+      case 3: wait_vmcnt<3 * NI_W_MIN>(); break;
+      case 4: wait_vmcnt<(NST > 5 ? 4 : 3) * NI_W_MIN>(); break;
+      case 5: wait_vmcnt<(NST > 6 ? 5 : 3) * NI_W_MIN>(); break;
+      default: wait_vmcnt<(NST > 7 ? 6 : 3) * NI_W_MIN>(); break;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(ac, bc);
   }
 
   // The whole loop for one workgroup of NW waves: a ring of NST slots,

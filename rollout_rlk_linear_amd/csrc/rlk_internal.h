@@ -56,6 +56,8 @@ struct FwdArgs {
   int64_t vocab_start, vocab_total;
   int full;
   FwdSlicing slicing;
+  int n_cu;    // compute units of the device (persistent small-batch grid)
+  int packed;  // weight is the pack_weight layout (fwd_stream only)
   float* logp;
   float* entropy;
   float4* stats;
@@ -100,6 +102,8 @@ enum KernelId {
   K_BWD_DH_REDUCE,
   K_FILL_ZERO,
   K_COMBINE,
+  K_FWD_STREAM,
+  K_PACK,
   K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];
@@ -108,7 +112,10 @@ extern const char* const kKernelNames[K_COUNT];
 void prof_before(int id, hipStream_t st);
 void prof_after(int id, hipStream_t st);
 
-size_t fwd_workspace(int64_t T, int64_t H, int64_t V);
+size_t fwd_workspace(int64_t T, int64_t H, int64_t V, bool packed);
+size_t packed_weight_bytes(int64_t H, const FwdSlicing& sl);
+hipError_t launch_pack(const uint16_t* weight, int H, const FwdSlicing& sl, uint16_t* packed,
+                       hipStream_t st);
 // RLK_OK when the current device is gfx950, else the rlk_status error.
 int check_device_status();
 BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh);

@@ -159,6 +159,197 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
   }
 }
 
+// ------------------------------------------------- small-batch stream ----
+//
+// For T <= 64 the forward is a stream over W. A unit is 128 consecutive rows
+// of one virtual slice: unit iu of slice p holds slice rows 128 iu .. (the
+// half iu % 2 of group iu / 2), i.e. one wave-chunk of fwd_tile's 256-column
+// group. A persistent grid of n_wg workgroups (one per CU) takes units
+// b, b + n_wg, ... and runs them as ONE pipeline of 32-k stages: the ring of
+// NST slots keeps NST - 1 stages in flight across unit boundaries, and a
+// unit's epilogue runs while the next unit's first stages land.
+//
+// Wave w multiplies the MI 16-row blocks of hidden by column blocks 2w and
+// 2w + 1 of the unit (so a stage costs each wave 2 + MI fragment reads and
+// 2 MI MFMAs, whatever T), every logit from the same MFMA chain as in
+// fwd_tile (k ascending in steps of 32 from zero). At the end of a unit the
+// logits pass through LDS so that each 16-lane group holds one row's 128
+// columns in fwd_tile's arrangement (lane l: columns 16 j + l), and the
+// record comes from the same chunk tree; the combine merges a group's two
+// halves as fwd_tile does, so the bits match the large-batch path.
+//
+// W is read either in its natural [V, H] layout (a stage holds 64 bytes of
+// each of the unit's 128 rows) or packed by pack_weight_kernel (a stage is
+// 8 KB contiguous, already in the slot's LDS order), which streams from HBM
+// at a markedly higher rate than 128 strided 64-byte pieces.
+constexpr int kStreamStages = 10;
+constexpr int kStreamRows = 64;                // rows of hidden per launch
+constexpr int kStreamStage = (64 + 128) * 64;  // A: 64 rows, B: 128 rows, 64 B each
+constexpr int kZStride = 68;                   // floats per logit column in LDS (conflict-free)
+
+template <int NST, int MI, bool PACKED>
+__global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
+    const int32_t* __restrict__ targets, int T, int H, int Vs, int Us, int P, int Gs,
+    int64_t vocab_start, int n_wg, int ldp, float4* __restrict__ part) {
+  static_assert(MI == 1 || MI == 2 || MI == 4, "16, 32 or 64 rows");
+  static_assert(NST >= 3 && NST * kStreamStage + 128 * kZStride * 4 <= 160 * 1024,
+                "ring and logit buffer fit the LDS");
+  static_assert(3 * (NST - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NST * kStreamStage];
+  __shared__ __attribute__((aligned(16))) float zbuf[128 * kZStride];  // [column][row]
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n_units = P * Us;
+  const int my_units = (int)blockIdx.x < n_units ? (n_units - 1 - (int)blockIdx.x) / n_wg + 1 : 0;
+  const int nsteps = H / 32;
+  const int Q = my_units * nsteps;  // stages of this workgroup, all units in a row
+
+  // targets of this lane's epilogue rows 16 i + 4 wave + lane / 16
+  int yv[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = 16 * i + 4 * wave + (lane >> 4);
+    yv[i] = targets[row < T ? row : 0];  // T >= 1: the loads are in flight together
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) asm volatile("" ::"v"(yv[i]) : "memory");  // landed before any DMA
+
+  const uint32_t lds0 = lds_addr(lds);
+  const int drow = lane >> 2;
+  const int dpiece = (lane & 3) ^ row_swz(drow);
+  const i32x4 rsA = make_rsrc(hidden, (uint32_t)((T < 64 ? T : 64) * H * 2));
+  const int voffA = (16 * wave + drow) * H * 2 + 16 * dpiece;
+  const int voffB0 = PACKED ? 1024 * wave + 16 * lane : (16 * wave + drow) * H * 2 + 16 * dpiece;
+  const int voffB1 = PACKED ? 1024 * (wave + 4) + 16 * lane
+                            : (16 * (wave + 4) + drow) * H * 2 + 16 * dpiece;
+  const int sB = PACKED ? 8192 : 64;  // bytes between consecutive stages of a unit's B
+
+  // issue state: the next stage to issue is stage iss_s of this workgroup's unit iss_u
+  int iss_u = 0, iss_s = 0;
+  i32x4 rsB;
+  auto set_unit = [&](int i) {
+    const int pu = (int)blockIdx.x + i * n_wg;
+    const int p = pu / Us, iu = pu - p * Us;
+    if constexpr (PACKED)
+      rsB = make_rsrc(weight + (int64_t)pu * 128 * H, (uint32_t)(128 * H * 2));
+    else
+      rsB = make_rsrc(weight + ((int64_t)p * Vs + 128 * iu) * H,
+                      (uint32_t)(min(128, Vs - 128 * iu) * H * 2));
+  };
+  auto issue = [&](int slot) {
+    const uint32_t st = lds0 + (uint32_t)(slot * kStreamStage);
+    dma16(rsA, st + 1024u * wave, voffA, 64 * iss_s);
+    dma16(rsB, st + 4096u + 1024u * wave, voffB0, sB * iss_s);
+    dma16(rsB, st + 4096u + 1024u * (wave + 4), voffB1, sB * iss_s);
+    if (++iss_s == nsteps) {
+      iss_s = 0;
+      if (++iss_u < my_units) set_unit(iss_u);
+    }
+  };
+
+  if (Q > 0) set_unit(0);
+  for (int q = 0; q < NST - 1 && q < Q; ++q) issue(q);
+
+  const int foff = (lane & 15) * 64 + 16 * ((lane >> 4) ^ row_swz(lane & 15));
+  f32x4 acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int unit = 0, s = 0;
+  for (int q = 0; q < Q; ++q) {
+    // this wave's DMA of stage q has landed once at most NST - 2 later stages are pending
+    if (q + NST - 2 < Q)
+      wait_vmcnt<3 * (NST - 2)>();
+    else
+      wait_vmcnt<0>();
+    barrier_only();  // every wave's part of stage q is in; slot (q - 1) % NST is free
+    if (q + NST - 1 < Q) issue((q + NST - 1) % NST);
+    const unsigned char* st = lds + (q % NST) * kStreamStage;
+    const bf16x8 b0 = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(st + (64 + 32 * wave) * 64 + foff));
+    const bf16x8 b1 = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(st + (64 + 32 * wave + 16) * 64 + foff));
+    bf16x8 af[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + 16 * i * 64 + foff));
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[i][1], 0, 0, 0);
+    }
+    if (++s < nsteps) continue;
+
+    // ---- unit epilogue: logits to LDS, column-major ([col][row], 68 floats a column)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        *reinterpret_cast<f32x4*>(&zbuf[(32 * wave + 16 * jj + (lane & 15)) * kZStride + 16 * i +
+                                        4 * (lane >> 4)]) = acc[i][jj];
+    __syncthreads();
+    const int pu = (int)blockIdx.x + unit * n_wg;
+    const int p = pu / Us, iu = pu - p * Us;
+    const int vlim = min(128, Vs - 128 * iu);
+    const int64_t col0 = (int64_t)p * Vs + 128 * iu;  // call-relative first column
+    const int u = p * 2 * Gs + iu;                   // record index (group iu / 2, half iu % 2)
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      // one row per 16-lane group: the 128 columns as fwd_tile's wave holds them
+      const int row = 16 * i + 4 * wave + (lane >> 4);
+      float z[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = zbuf[(16 * j + (lane & 15)) * kZStride + row];
+        z[j] = 16 * j + (lane & 15) < vlim ? v : neg_inf();
+      }
+      const ChunkStats c = chunk_stats(z);
+      const int64_t yc = (int64_t)yv[i] - vocab_start - col0;
+      const bool yin = row < T && yc >= 0 && yc < vlim;
+      const int ycl = yin ? (int)yc : 0;
+      const int jt = ycl >> 4;
+      float zl = neg_inf();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) zl = (j == jt) ? z[j] : zl;
+      zl = (yin && (ycl & 15) == (lane & 15)) ? zl : neg_inf();
+      const float zy = row16_max(zl);
+      if ((lane & 15) == 0 && row < T) part[(int64_t)row * ldp + u] = make_float4(c.m, c.R, c.B, zy);
+    }
+    // zbuf is rewritten only after at least one more stage barrier (nsteps >= 2),
+    // which every wave reaches after its reads above have returned
+#pragma unroll
+    for (int i = 0; i < MI; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s = 0;
+    ++unit;
+  }
+  wait_vmcnt<0>();
+}
+
+// W rearranged for fwd_stream_kernel<PACKED>: unit pu = p Us + iu (slice p,
+// slice rows 128 iu .. + 127) is 128 H elements at pu 128 H; its stage s
+// (k = 32 s .. + 31) is 8 KB at s 4096 inside it, laid out exactly as a B
+// slot of the ring: 16-byte piece i of 1 KB block jb holds row 16 jb + i / 4,
+// k piece (i % 4) ^ row_swz(i / 4). Rows past the slice are zero.
+__global__ __launch_bounds__(kThreads) void pack_weight_kernel(
+    const uint16_t* __restrict__ weight, int H, int Vs, int Us, int64_t n_pieces,
+    uint16_t* __restrict__ packed) {
+  const int64_t per_unit = (int64_t)16 * H;  // 16-byte pieces per unit
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n_pieces;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t pu = idx / per_unit;
+    const int rem = (int)(idx - pu * per_unit);
+    const int s = rem >> 9, q = rem & 511;
+    const int i = q & 63, r = 16 * (q >> 6) + (i >> 2);
+    const int piece = (i & 3) ^ row_swz(i >> 2);
+    const int p = (int)(pu / Us), iu = (int)(pu - (int64_t)p * Us);
+    const int srow = 128 * iu + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (srow < Vs)
+      v = *reinterpret_cast<const u32x4*>(weight + ((int64_t)p * Vs + srow) * H + 32 * s + 8 * piece);
+    *reinterpret_cast<u32x4*>(packed + idx * 8) = v;
+  }
+}
+
 // ==================================================== forward combine ====
 
 __device__ __forceinline__ Part shfl_xor_part(const Part& p, int s) {
@@ -176,22 +367,35 @@ __device__ __forceinline__ void finalize_row(const Part& acc, bool target_ok, fl
 // One wave per row. Each virtual slice's groups: lane j folds groups j,
 // j + 64, ... of the slice in order, then a 64-lane xor tree (lower lane
 // left); the P slice records then merge by the fixed tree (P = 1, 2 or 4).
+// With units = 2 the records are per 128-column half (fwd_chunk_kernel) and
+// a group's record is merged from its halves here, as fwd_tile merges them.
 __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(
     const float4* __restrict__ part, const int32_t* __restrict__ targets, int T, int G, int P,
-    int Gs, int64_t vocab_total, int full, float* __restrict__ logp, float* __restrict__ entropy,
-    float4* __restrict__ stats) {
+    int Gs, int Vs, int units, int64_t vocab_total, int full, float* __restrict__ logp,
+    float* __restrict__ entropy, float4* __restrict__ stats) {
   const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= T) return;
-  const float4* pr = part + (int64_t)row * G;
+  const float4* pr = part + (int64_t)row * G * units;
   Part rs[kVirtualSlices];
 #pragma unroll
   for (int p = 0; p < kVirtualSlices; ++p) {
     if (p < P) {
       Part acc = part_empty();
       for (int g = lane; g < Gs; g += 64) {
-        const float4 q = pr[p * Gs + g];
-        acc = part_merge(acc, Part{q.x, q.y, q.z, q.w});
+        Part q;
+        if (units == 1) {
+          const float4 a = pr[p * Gs + g];
+          q = Part{a.x, a.y, a.z, a.w};
+        } else {
+          const float4 a = pr[2 * (p * Gs + g)];
+          q = Part{a.x, a.y, a.z, a.w};
+          if (128 < min(GROUP, Vs - g * GROUP)) {
+            const float4 b = pr[2 * (p * Gs + g) + 1];
+            q = part_merge(q, Part{b.x, b.y, b.z, b.w});
+          }
+        }
+        acc = part_merge(acc, q);
       }
 #pragma unroll
       for (int s = 1; s < 64; s <<= 1) {
@@ -520,7 +724,6 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                    \
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, int, \
       int, int, int, int, int, int, float* __restrict__);
-RLK_FWD_TILE(32, 2, 2)
 RLK_FWD_TILE(256, 2, 2)
 RLK_RECOMPUTE(32, 2, 2)
 RLK_RECOMPUTE(256, 2, 2)
@@ -542,18 +745,51 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   const FwdSlicing& sl = a.slicing;
   const int G = sl.G;
-  const int G8 = cdiv(G, 8) * 8;
-  if (a.T <= kSmallT) {
-    const int nt = cdiv(a.T, 32);
-    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<32, 2, 2>), G8 * nt, st, a.hidden, a.weight, a.targets,
-               a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, a.part);
+  int units = 1;
+  if (a.packed || a.T <= kSmallT) {
+    // persistent stream over 128-row units, 64 rows of hidden per launch
+    units = 2;
+    const int Us = cdiv(sl.Vs, 128);
+    const int n_units = sl.P * Us;
+    const int n_cu = a.n_cu > 0 ? a.n_cu : 256;
+    const int grid = n_cu < n_units ? n_cu : n_units;
+    for (int r0 = 0; r0 < a.T; r0 += kStreamRows) {
+      const int rows = a.T - r0 < kStreamRows ? a.T - r0 : kStreamRows;
+      const uint16_t* h = a.hidden + (int64_t)r0 * a.H;
+      const int32_t* y = a.targets + r0;
+      float4* pr = a.part + (int64_t)r0 * 2 * G;
+#define RLK_STREAM(MI, PK)                                                                     \
+  RLK_LAUNCH(K_FWD_STREAM, (fwd_stream_kernel<kStreamStages, MI, PK>), grid, st, h, a.weight, y, \
+             rows, a.H, sl.Vs, Us, sl.P, sl.Gs, a.vocab_start, grid, 2 * G, pr)
+      if (a.packed) {
+        if (rows <= 16) RLK_STREAM(1, true);
+        else if (rows <= 32) RLK_STREAM(2, true);
+        else RLK_STREAM(4, true);
+      } else {
+        if (rows <= 16) RLK_STREAM(1, false);
+        else if (rows <= 32) RLK_STREAM(2, false);
+        else RLK_STREAM(4, false);
+      }
+#undef RLK_STREAM
+    }
   } else {
     const int nt = cdiv(a.T, 256);
+    const int G8 = cdiv(G, 8) * 8;
     RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2>), G8 * nt, st, a.hidden, a.weight,
                a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, a.part);
   }
   RLK_LAUNCH(K_FWD_COMBINE, fwd_combine_kernel, cdiv(a.T, kThreads / 64), st, a.part, a.targets,
-             a.T, G, sl.P, sl.Gs, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
+             a.T, G, sl.P, sl.Gs, sl.Vs, units, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint16_t* weight, int H, const FwdSlicing& sl, uint16_t* packed,
+                       hipStream_t st) {
+  const int Us = cdiv(sl.Vs, 128);
+  const int64_t n_pieces = (int64_t)sl.P * Us * 16 * H;
+  const int64_t want = (n_pieces + kThreads - 1) / kThreads;
+  const int grid = (int)(want < 8192 ? want : 8192);
+  RLK_LAUNCH(K_PACK, pack_weight_kernel, grid, st, weight, H, sl.Vs, Us, n_pieces, packed);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 // rlk_microbench.hip — measured denominators for the roofline figures: a
-// streaming copy (HBM bandwidth) and back-to-back independent bf16 MFMAs
-// (matrix-core rate), declared in rlk_microbench.h.
+// streaming copy and a streaming read (HBM bandwidth) and back-to-back
+// independent bf16 MFMAs (matrix-core rate), declared in rlk_microbench.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,6 +28,47 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ dst,
     const int64_t i = i0 + k * stride;
     if (i < n16) dst[i] = v[k];
   }
+}
+
+// Linear read of `n_stages` 8 KB stages through LDS-DMA: workgroup b streams
+// 1 MB runs (128 stages) b, b + grid, ... as one pipeline over a ring of 8
+// slots, each wave moving two 1 KB blocks per stage. Nothing but the loads:
+// the read rate HBM gives a consumer of contiguous bytes.
+constexpr int kReadStages = 8;
+__global__ __launch_bounds__(kThreads) void read_kernel(const unsigned char* __restrict__ src,
+                                                        int64_t n_stages, float* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kReadStages * 8192];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const uint32_t lds0 = lds_addr(lds);
+  const int64_t runs = (n_stages + 127) / 128;
+  const int64_t my_runs = (int64_t)blockIdx.x < runs ? (runs - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  // stage j of this workgroup: run blockIdx.x + (j / 128) gridDim.x, stage j % 128 of it
+  int64_t Q = 0;
+  if (my_runs > 0) {
+    const int64_t last_run = blockIdx.x + (my_runs - 1) * (int64_t)gridDim.x;
+    const int64_t last_len = n_stages - 128 * last_run < 128 ? n_stages - 128 * last_run : 128;
+    Q = (my_runs - 1) * 128 + last_len;
+  }
+  auto issue = [&](int64_t j) {
+    const int64_t stage = 128 * ((int64_t)blockIdx.x + (j >> 7) * gridDim.x) + (j & 127);
+    const i32x4 rs = make_rsrc(src + stage * 8192, 8192u);
+    const uint32_t st = lds0 + (uint32_t)((j % kReadStages) * 8192);
+    dma16(rs, st + 1024u * wave, 1024 * wave + 16 * lane, 0);
+    dma16(rs, st + 1024u * (wave + 4), 1024 * (wave + 4) + 16 * lane, 0);
+  };
+  for (int64_t j = 0; j < kReadStages - 1 && j < Q; ++j) issue(j);
+  for (int64_t j = 0; j < Q; ++j) {
+    if (j + kReadStages - 2 < Q)
+      wait_vmcnt<2 * (kReadStages - 2)>();
+    else
+      wait_vmcnt<0>();
+    barrier_only();
+    if (j + kReadStages - 1 < Q) issue(j + kReadStages - 1);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  const float v = reinterpret_cast<const float*>(lds)[threadIdx.x];
+  if (v == -1.2345e-30f) sink[threadIdx.x & 3] = v;
 }
 
 // Every wave: 32 independent accumulators, `iters` rounds of one MFMA each;
@@ -72,6 +113,20 @@ RLK_API rlk_status rlk_microbench_copy(void* dst, const void* src, size_t bytes,
   hipLaunchKernelGGL(rlk::copy_kernel, dim3((unsigned)grid), dim3(rlk::kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<rlk::u32x4*>(dst),
                      static_cast<const rlk::u32x4*>(src), n16);
+  return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
+RLK_API rlk_status rlk_microbench_read(const void* src, size_t bytes, float* sink, int64_t workgroups,
+                                       void* stream) {
+  if (!src || !sink || bytes == 0 || (bytes % 8192) != 0 || bytes > (size_t(1) << 40) ||
+      workgroups < 1 || workgroups > (1 << 20))
+    return RLK_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(sink)) % 16) return RLK_ERR_INVALID_ARG;
+  const int s = rlk::check_device_status();
+  if (s != RLK_OK) return (rlk_status)s;
+  hipLaunchKernelGGL(rlk::read_kernel, dim3((unsigned)workgroups), dim3(rlk::kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const unsigned char*>(src),
+                     (int64_t)(bytes / 8192), sink);
   return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 

@@ -113,6 +113,13 @@ def test_microbench_argument_errors():
     assert raw.rlk_microbench_mfma(P, 0, 10, NULL) == INVALID
     assert raw.rlk_microbench_mfma(P, 256, 0, NULL) == INVALID
     assert raw.rlk_microbench_mfma(P, 256, (1 << 24) + 1, NULL) == INVALID
+    raw.rlk_microbench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    assert raw.rlk_microbench_read(NULL, 8192, P, 256, NULL) == INVALID
+    assert raw.rlk_microbench_read(Q, 8192 + 16, P, 256, NULL) == INVALID   # not whole 8 KB stages
+    assert raw.rlk_microbench_read(Q, 8192, NULL, 256, NULL) == INVALID
+    assert raw.rlk_microbench_read(Q, 8192, P, 0, NULL) == INVALID
+    assert raw.rlk_microbench_read(ctypes.c_void_p((1 << 21) + 8), 8192, P, 256, NULL) == INVALID
 
 
 def test_provenance(lib):
@@ -190,12 +197,67 @@ def test_bwd_T0_without_dweight_is_noop(lib):
     assert bwd(lib, T=0, hidden=NULL, targets=NULL, stats=NULL, dw=NULL, ws=NULL, nws=0) == OK
 
 
+def fwdp(lib, hidden=P, packed=P, npk=1 << 40, targets=P, T=4, H=64, V=100, vs=0, vt=None,
+         logp=P, ent=P, stats=P, ws=P, nws=1 << 30):
+    vt = V if vt is None else vt
+    return lib.rlk_linear_logp_fwd_packed(hidden, packed, npk, targets, T, H, V, vs, vt, logp, ent,
+                                          stats, ws, nws, NULL)
+
+
+def test_pack_weight_bytes(lib):
+    f = lib.rlk_linear_pack_weight_bytes
+    # whole vocabulary 151936 = 4 virtual slices of 37984 rows = 297 units of 128 rows each
+    assert f(4096, 151936, 0, 151936) == 4 * 297 * 128 * 4096 * 2
+    # half of a 303872-row vocabulary: 2 slices of 75968 rows, 594 units each
+    assert f(4096, 151936, 151936, 303872) == 2 * 594 * 128 * 4096 * 2
+    # no virtual slicing (vocab_total not a multiple of 4): one slice of V rows
+    assert f(64, 1001, 0, 1001) == 8 * 128 * 64 * 2
+    assert f(96, 1000, 0, 1000) == 0        # H not a multiple of 64
+    assert f(64, 0, 0, 1000) == 0
+    assert f(64, 100, 950, 1000) == 0       # slice past the vocabulary
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(weight=NULL), INVALID), (dict(packed=NULL), INVALID),
+    (dict(packed=ctypes.c_void_p((1 << 20) + 8)), INVALID), (dict(H=96), SHAPE),
+    (dict(npk=1000), WS_SMALL), (dict(vs=10, vt=105), INVALID),
+])
+def test_pack_weight_argument_errors(lib, kw, code):
+    a = dict(weight=P, H=64, V=100, vs=0, vt=100, packed=P, npk=1 << 30)
+    a.update(kw)
+    assert lib.rlk_linear_pack_weight(a["weight"], a["H"], a["V"], a["vs"], a["vt"], a["packed"],
+                                      a["npk"], NULL) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(npk=4 * 128 * 64 * 2 - 2), INVALID),   # (64, 100): 4 virtual slices, one unit each
+    (dict(packed=NULL), INVALID), (dict(T=-1), INVALID), (dict(H=96), SHAPE),
+    (dict(vs=5, vt=200, stats=P), INVALID), (dict(nws=0), WS_SMALL),
+    (dict(hidden=ctypes.c_void_p((1 << 20) + 2)), INVALID),
+])
+def test_fwd_packed_argument_errors(lib, kw, code):
+    assert fwdp(lib, **kw) == code
+
+
+def test_fwd_packed_T0_is_noop(lib):
+    before = lib.rlk_call_count(5)
+    assert fwdp(lib, T=0, hidden=NULL, targets=NULL, ws=NULL, nws=0) == OK
+    assert lib.rlk_call_count(5) == before + 1
+
+
 def test_workspace_sizes(lib):
     f = lib.rlk_linear_logp_fwd_workspace_bytes
     assert f(0, 4096, 151936) == 0
     # one 16-byte record per (row, group of 256 columns), rounded to 256 B
     assert f(512, 4096, 151936) == 512 * (594 + 3) * 16  # virtual slices add <= 3 short groups
-    assert f(3, 256, 1024) == 512
+    # batches of at most 64 rows keep one record per 128-column half of a group
+    assert f(3, 256, 1024) == 768  # 3 * (4 + 3) * 2 * 16 = 672, rounded up
+    assert f(64, 4096, 151936) == 64 * 597 * 2 * 16
+    assert f(65, 4096, 151936) == (65 * 597 * 16 + 255) // 256 * 256
+    # the packed forward keeps two records per group for every T
+    fp = lib.rlk_linear_logp_fwd_packed_workspace_bytes
+    assert fp(512, 4096, 151936) == 512 * 597 * 2 * 16
+    assert fp(3, 256, 1024) == f(3, 256, 1024)
     b = lib.rlk_linear_logp_bwd_workspace_bytes
     sizes = [b(T, 4096, 151936, 0, 1) for T in (1, 4, 64, 512, 5208)]
     assert all(x < y for x, y in zip(sizes, sizes[1:]))

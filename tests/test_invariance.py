@@ -7,7 +7,8 @@ h100-cp-gradient.json", validation.train_rollout_logprob and
 validation.cuda_graph.expected_capture_sizes). Here a fixed pool of 64
 Qwen3-8B-shaped rows (H = 4096, V = 151936) is scored in batches of 1, 2, 3,
 4 and 64, under 3 row permutations, embedded in a batch of 512 other rows,
-and repeated; every row's logp, entropy and statistics record must be
+and repeated, and scored through the packed-weight rollout path in batches
+of 1 to 4 and 64; every row's logp, entropy and statistics record must be
 bit-identical across all of them. The same holds for each row of dhidden.
 """
 
@@ -86,6 +87,26 @@ def test_composition_bitwise(setup):
         torch.cuda.synchronize()
         assert mismatch(got[pos], ref) == 0
         assert mismatch(st[pos], ref_st) == 0
+
+
+def test_rollout_packed_batches_match_training_batch(setup):
+    # the rollout engine's path (packed W, decode batches of 1 to 4 and 64)
+    # against the trainer's: the pool's rows inside a 512-row batch
+    W, h, y = setup["W"], setup["h"], setup["y"]
+    emb = setup["pool"]["embed"]
+    pos = emb["positions"].cuda()
+    train, train_st = score(W, dev(emb["hidden"]), dev(emb["targets"]))
+    pw = rlk.pack_weight(W)
+    for bs in (1, 2, 3, 4, 64):
+        outs, stats = [], []
+        for r0 in range(0, 64, bs):
+            o = rlk.fwd_packed(h[r0:r0 + bs].contiguous(), pw, y[r0:r0 + bs].contiguous())
+            outs.append(torch.stack([o["logp"], o["entropy"]], dim=1))
+            stats.append(o["stats"])
+        torch.cuda.synchronize()
+        assert mismatch(torch.cat(outs), train[pos]) == 0, f"rollout batch {bs}"
+        assert mismatch(torch.cat(stats), train_st[pos]) == 0, f"rollout stats, batch {bs}"
+    del pw
 
 
 def test_dhidden_rows_bitwise(setup):
