@@ -27,9 +27,13 @@ Modules:
   and their merge; every function names the definition it writes out.
 * ``brute`` — exact rational logits plus 50-digit decimal exp/ln for tiny
   vocabularies; pins ``linear_logp`` from outside float64.
+* ``lora_linear`` — numpy float64 forward and backward of the LoRA linear of
+  the page "RL-Kernel h3-runtime-integration-b200 report.json" (key
+  ``lora_gate``) and that page's norm-wise relative error.
 
-Every function here is pinned by ``tests/test_oracle.py`` against closed
-forms, brute force, finite differences and invariants. No function here is
+Every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_lora.py`` against closed forms, brute force, finite
+differences and invariants. No function here is
 "parity unpinned".
 """
 
@@ -44,3 +48,4 @@ from .linear_logp import (  # noqa: F401
     merge_partials,
     finalize_partials,
 )
+from .lora_linear import lora_backward, lora_forward, rel_err  # noqa: F401

@@ -21,6 +21,11 @@ Cases:
   step5208  T=5208 from 8 sequences of length U[256,1024] (seed 7)
   slice7168 T=7168, full W as qwen512 then x8 (exact: power of two), cut into
             4 slices of 37984 rows; targets over the full vocabulary; seed 8
+
+LoRA linear (the page "RL-Kernel h3-runtime-integration-b200 report.json",
+key ``lora_gate``: shapes N512 K384 T70, N2048 K1024 T257, N5120 K5120 T33;
+rank 16 here, the page gives none): x N(0,1), W N(0,1/K), A N(0,1/K),
+B N(0,1/r), dy N(0,1), all bf16; draw order x, W, A, B, dy; seeds 40, 41, 42.
 """
 
 from __future__ import annotations
@@ -197,3 +202,50 @@ def digest(*tensors) -> str:
 
 def clear_cache():
     _cache.clear()
+
+
+# ------------------------------------------------------------ LoRA linear ----
+
+LORA_SHAPES = ((512, 384, 70), (2048, 1024, 257), (5120, 5120, 33))  # (N, K, T)
+LORA_RANK = 16
+
+
+@dataclass
+class LoraCase:
+    name: str
+    x: torch.Tensor    # bf16 [T,K]
+    W: torch.Tensor    # bf16 [N,K]
+    A: torch.Tensor    # bf16 [r,K]
+    B: torch.Tensor    # bf16 [N,r]
+    dy: torch.Tensor   # bf16 [T,N]
+
+    @property
+    def T(self):
+        return self.x.shape[0]
+
+    @property
+    def K(self):
+        return self.x.shape[1]
+
+    @property
+    def N(self):
+        return self.W.shape[0]
+
+    @property
+    def r(self):
+        return self.A.shape[0]
+
+
+def lora_case(N: int, K: int, T: int, seed: int, r: int = LORA_RANK) -> LoraCase:
+    g = _gen(seed)
+    x = to_bf16(torch.randn(T, K, generator=g))
+    W = to_bf16(torch.randn(N, K, generator=g) / K ** 0.5)
+    A = to_bf16(torch.randn(r, K, generator=g) / K ** 0.5)
+    B = to_bf16(torch.randn(N, r, generator=g) / r ** 0.5)
+    dy = to_bf16(torch.randn(T, N, generator=g))
+    return LoraCase(f"lora_N{N}_K{K}_T{T}", x, W, A, B, dy)
+
+
+def lora_page_cases():
+    """The three shapes of the page's gate, seeds 40, 41, 42."""
+    return [lora_case(N, K, T, 40 + i) for i, (N, K, T) in enumerate(LORA_SHAPES)]
