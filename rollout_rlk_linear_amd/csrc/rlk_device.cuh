@@ -194,12 +194,16 @@ __device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3
 // LDS read) would drain the prefetch pipeline. Ordering is the caller's:
 // explicit vmcnt waits and barriers (all with memory clobbers).
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t addr, int voff, int soff) {
+  // the descriptor is wave-uniform; readfirstlane keeps it in SGPRs where the
+  // compiler cannot prove that itself (a no-op where it can)
+  const i32x4 rs = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
-      : "s"(__builtin_amdgcn_readfirstlane((int)addr)), "v"(voff), "s"(rsrc),
+      : "s"(__builtin_amdgcn_readfirstlane((int)addr)), "v"(voff), "s"(rs),
         "s"(__builtin_amdgcn_readfirstlane(soff))
       : "memory", "m0");
 }
@@ -505,14 +509,25 @@ struct AsyncGemmKN {
       // the resource ends at column nb_valid of the stage's last valid row
       const uint32_t bbytes = brows > 0 ? (uint32_t)(((brows - 1) * ldb + nb_valid) * 2) : 0u;
       const i32x4 rsB = make_rsrc(B + (int64_t)k0 * ldb, bbytes);
+      if constexpr (NI_A % NW == 0 && NI % NW == 0) {
+        // block wave + NW ii is an A block iff ii < NI_A / NW (known at compile time)
 #pragma unroll
-      for (int ii = 0; ii < NI_W_MAX; ++ii) {
-        const int j = wave + NW * ii;
-        if (j < NI) {
-          if (j < NI_A)
-            dma16(rsA, st + j * 1024, voff[ii], k0 * 2);
+        for (int ii = 0; ii < NI / NW; ++ii) {
+          if (ii < NI_A / NW)
+            dma16(rsA, st + (wave + NW * ii) * 1024, voff[ii], k0 * 2);
           else
-            dma16(rsB, st + j * 1024, voff[ii], 0);
+            dma16(rsB, st + (wave + NW * ii) * 1024, voff[ii], 0);
+        }
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < NI_W_MAX; ++ii) {
+          const int j = wave + NW * ii;
+          if (j < NI) {
+            if (j < NI_A)
+              dma16(rsA, st + j * 1024, voff[ii], k0 * 2);
+            else
+              dma16(rsB, st + j * 1024, voff[ii], 0);
+          }
         }
       }
     };

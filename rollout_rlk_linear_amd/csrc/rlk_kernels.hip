@@ -182,22 +182,32 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
 // each of the unit's 128 rows) or packed by pack_weight_kernel (a stage is
 // 8 KB contiguous, already in the slot's LDS order), which streams from HBM
 // at a markedly higher rate than 128 strided 64-byte pieces.
-constexpr int kStreamStages = 10;
-constexpr int kStreamRows = 64;                // rows of hidden per launch
-constexpr int kStreamStage = (64 + 128) * 64;  // A: 64 rows, B: 128 rows, 64 B each
-constexpr int kZStride = 68;                   // floats per logit column in LDS (conflict-free)
+constexpr int kStreamRows = 64;  // rows of hidden per launch
+// Per row count (MI 16-row blocks): a stage holds 16 MI rows of hidden and the
+// unit's 128 W rows, 64 bytes each; the logit buffer holds 128 columns of
+// 16 MI rows at a stride of ZS floats (ZS = 4 mod 64 keeps the epilogue's
+// reads and writes free of bank conflicts); the ring takes what remains.
+template <int MI>
+struct StreamCfg {
+  static constexpr int STAGE = (16 * MI + 128) * 64;
+  static constexpr int ZS = 16 * MI + 4;
+  static constexpr int ZBYTES = 128 * ZS * 4;
+  static constexpr int NST = (160 * 1024 - ZBYTES) / STAGE;
+};
 
-template <int NST, int MI, bool PACKED>
+template <int MI, bool PACKED>
 __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int Vs, int Us, int P, int Gs,
     int64_t vocab_start, int n_wg, int ldp, float4* __restrict__ part) {
   static_assert(MI == 1 || MI == 2 || MI == 4, "16, 32 or 64 rows");
-  static_assert(NST >= 3 && NST * kStreamStage + 128 * kZStride * 4 <= 160 * 1024,
-                "ring and logit buffer fit the LDS");
+  using C = StreamCfg<MI>;
+  constexpr int NST = C::NST, STAGE = C::STAGE, ZS = C::ZS;
+  constexpr int A_BYTES = 16 * MI * 64;
+  static_assert(NST >= 3 && NST * STAGE + C::ZBYTES <= 160 * 1024, "ring and logits fit the LDS");
   static_assert(3 * (NST - 2) < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NST * kStreamStage];
-  __shared__ __attribute__((aligned(16))) float zbuf[128 * kZStride];  // [column][row]
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STAGE];
+  __shared__ __attribute__((aligned(16))) float zbuf[128 * ZS];  // [column][row]
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int n_units = P * Us;
@@ -218,7 +228,8 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
   const uint32_t lds0 = lds_addr(lds);
   const int drow = lane >> 2;
   const int dpiece = (lane & 3) ^ row_swz(drow);
-  const i32x4 rsA = make_rsrc(hidden, (uint32_t)((T < 64 ? T : 64) * H * 2));
+  const i32x4 rsA = make_rsrc(hidden, (uint32_t)((T < 16 * MI ? T : 16 * MI) * H * 2));
+  const bool loads_a = wave < MI;  // waves 0 .. MI-1 move one 16-row block of hidden each
   const int voffA = (16 * wave + drow) * H * 2 + 16 * dpiece;
   const int voffB0 = PACKED ? 1024 * wave + 16 * lane : (16 * wave + drow) * H * 2 + 16 * dpiece;
   const int voffB1 = PACKED ? 1024 * (wave + 4) + 16 * lane
@@ -238,10 +249,10 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
                       (uint32_t)(min(128, Vs - 128 * iu) * H * 2));
   };
   auto issue = [&](int slot) {
-    const uint32_t st = lds0 + (uint32_t)(slot * kStreamStage);
-    dma16(rsA, st + 1024u * wave, voffA, 64 * iss_s);
-    dma16(rsB, st + 4096u + 1024u * wave, voffB0, sB * iss_s);
-    dma16(rsB, st + 4096u + 1024u * (wave + 4), voffB1, sB * iss_s);
+    const uint32_t st = lds0 + (uint32_t)(slot * STAGE);
+    if (loads_a) dma16(rsA, st + 1024u * wave, voffA, 64 * iss_s);
+    dma16(rsB, st + A_BYTES + 1024u * wave, voffB0, sB * iss_s);
+    dma16(rsB, st + A_BYTES + 1024u * (wave + 4), voffB1, sB * iss_s);
     if (++iss_s == nsteps) {
       iss_s = 0;
       if (++iss_u < my_units) set_unit(iss_u);
@@ -257,18 +268,21 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
   for (int i = 0; i < MI; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   int unit = 0, s = 0;
   for (int q = 0; q < Q; ++q) {
-    // this wave's DMA of stage q has landed once at most NST - 2 later stages are pending
-    if (q + NST - 2 < Q)
+    // this wave's DMA of stage q has landed once at most NST - 2 later stages are
+    // pending (3 blocks a stage for the waves that move hidden, else 2)
+    if (q + NST - 2 >= Q)
+      wait_vmcnt<0>();
+    else if (loads_a)
       wait_vmcnt<3 * (NST - 2)>();
     else
-      wait_vmcnt<0>();
+      wait_vmcnt<2 * (NST - 2)>();
     barrier_only();  // every wave's part of stage q is in; slot (q - 1) % NST is free
     if (q + NST - 1 < Q) issue((q + NST - 1) % NST);
-    const unsigned char* st = lds + (q % NST) * kStreamStage;
+    const unsigned char* st = lds + (q % NST) * STAGE;
     const bf16x8 b0 = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(st + (64 + 32 * wave) * 64 + foff));
+        bf16x8, *reinterpret_cast<const u32x4*>(st + A_BYTES + 32 * wave * 64 + foff));
     const bf16x8 b1 = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(st + (64 + 32 * wave + 16) * 64 + foff));
+        bf16x8, *reinterpret_cast<const u32x4*>(st + A_BYTES + (32 * wave + 16) * 64 + foff));
     bf16x8 af[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -280,12 +294,12 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
     }
     if (++s < nsteps) continue;
 
-    // ---- unit epilogue: logits to LDS, column-major ([col][row], 68 floats a column)
+    // ---- unit epilogue: logits to LDS, column-major ([col][row], ZS floats a column)
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
-        *reinterpret_cast<f32x4*>(&zbuf[(32 * wave + 16 * jj + (lane & 15)) * kZStride + 16 * i +
+        *reinterpret_cast<f32x4*>(&zbuf[(32 * wave + 16 * jj + (lane & 15)) * ZS + 16 * i +
                                         4 * (lane >> 4)]) = acc[i][jj];
     __syncthreads();
     const int pu = (int)blockIdx.x + unit * n_wg;
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
       float z[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float v = zbuf[(16 * j + (lane & 15)) * kZStride + row];
+        const float v = zbuf[(16 * j + (lane & 15)) * ZS + row];
         z[j] = 16 * j + (lane & 15) < vlim ? v : neg_inf();
       }
       const ChunkStats c = chunk_stats(z);
@@ -330,23 +344,37 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
 // (k = 32 s .. + 31) is 8 KB at s 4096 inside it, laid out exactly as a B
 // slot of the ring: 16-byte piece i of 1 KB block jb holds row 16 jb + i / 4,
 // k piece (i % 4) ^ row_swz(i / 4). Rows past the slice are zero.
+// One thread moves one 128-byte line of a W row (two stages' worth of that
+// row: each line is read once) to its two 64-byte slots; consecutive threads
+// take consecutive rows, so the slots they write are contiguous.
 __global__ __launch_bounds__(kThreads) void pack_weight_kernel(
-    const uint16_t* __restrict__ weight, int H, int Vs, int Us, int64_t n_pieces,
+    const uint16_t* __restrict__ weight, int H, int Vs, int Us, int64_t n_lines,
     uint16_t* __restrict__ packed) {
-  const int64_t per_unit = (int64_t)16 * H;  // 16-byte pieces per unit
-  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n_pieces;
+  const int pairs = H / 64;  // 128-byte lines per W row
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n_lines;
        idx += (int64_t)gridDim.x * kThreads) {
-    const int64_t pu = idx / per_unit;
-    const int rem = (int)(idx - pu * per_unit);
-    const int s = rem >> 9, q = rem & 511;
-    const int i = q & 63, r = 16 * (q >> 6) + (i >> 2);
-    const int piece = (i & 3) ^ row_swz(i >> 2);
+    const int r = (int)(idx & 127);
+    const int64_t rest = idx >> 7;
+    const int s2 = (int)(rest % pairs);
+    const int64_t pu = rest / pairs;
     const int p = (int)(pu / Us), iu = (int)(pu - (int64_t)p * Us);
     const int srow = 128 * iu + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (srow < Vs)
-      v = *reinterpret_cast<const u32x4*>(weight + ((int64_t)p * Vs + srow) * H + 32 * s + 8 * piece);
-    *reinterpret_cast<u32x4*>(packed + idx * 8) = v;
+    u32x4 v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = u32x4{0u, 0u, 0u, 0u};
+    if (srow < Vs) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(weight + ((int64_t)p * Vs + srow) * H + 64 * s2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = src[e];
+    }
+    const int sw = row_swz(r & 15);
+    uint16_t* unit = packed + pu * 128 * H;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4* dst = reinterpret_cast<u32x4*>(unit + (int64_t)(2 * s2 + h) * 4096 + 32 * r);
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) dst[kp ^ sw] = v[4 * h + kp];
+    }
   }
 }
 
@@ -377,25 +405,50 @@ __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(
   const int lane = threadIdx.x & 63;
   if (row >= T) return;
   const float4* pr = part + (int64_t)row * G * units;
+  // Lane j folds groups j, j + 64, ... of each slice in order. The records of
+  // the first four of them in every slice are loaded before any merge, the
+  // rest in batches of four, so the load latency is paid once per batch
+  // rather than once per record; the merge order is unchanged.
+  constexpr int NB = 4;
+  auto group_rec = [&](const float4& a, const float4& b, int g) {
+    Part q{a.x, a.y, a.z, a.w};
+    if (units == 2 && 128 < min(GROUP, Vs - g * GROUP)) q = part_merge(q, Part{b.x, b.y, b.z, b.w});
+    return q;
+  };
+  auto load = [&](int p, int g, float4& a, float4& b) {
+    if (units == 1) {
+      a = pr[p * Gs + g];
+    } else {
+      a = pr[2 * (p * Gs + g)];
+      if (128 < min(GROUP, Vs - g * GROUP)) b = pr[2 * (p * Gs + g) + 1];
+    }
+  };
   Part rs[kVirtualSlices];
+  float4 qa[kVirtualSlices][NB], qb[kVirtualSlices][NB];
+#pragma unroll
+  for (int p = 0; p < kVirtualSlices; ++p)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int g = lane + 64 * b;
+      if (p < P && g < Gs) load(p, g, qa[p][b], qb[p][b]);
+    }
 #pragma unroll
   for (int p = 0; p < kVirtualSlices; ++p) {
     if (p < P) {
       Part acc = part_empty();
-      for (int g = lane; g < Gs; g += 64) {
-        Part q;
-        if (units == 1) {
-          const float4 a = pr[p * Gs + g];
-          q = Part{a.x, a.y, a.z, a.w};
-        } else {
-          const float4 a = pr[2 * (p * Gs + g)];
-          q = Part{a.x, a.y, a.z, a.w};
-          if (128 < min(GROUP, Vs - g * GROUP)) {
-            const float4 b = pr[2 * (p * Gs + g) + 1];
-            q = part_merge(q, Part{b.x, b.y, b.z, b.w});
-          }
-        }
-        acc = part_merge(acc, q);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int g = lane + 64 * b;
+        if (g < Gs) acc = part_merge(acc, group_rec(qa[p][b], qb[p][b], g));
+      }
+      for (int g0 = lane + 64 * NB; g0 < Gs; g0 += 64 * NB) {
+        float4 ta[NB], tb[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (g0 + 64 * b < Gs) load(p, g0 + 64 * b, ta[b], tb[b]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (g0 + 64 * b < Gs) acc = part_merge(acc, group_rec(ta[b], tb[b], g0 + 64 * b));
       }
 #pragma unroll
       for (int s = 1; s < 64; s <<= 1) {
@@ -759,7 +812,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
       const int32_t* y = a.targets + r0;
       float4* pr = a.part + (int64_t)r0 * 2 * G;
 #define RLK_STREAM(MI, PK)                                                                     \
-  RLK_LAUNCH(K_FWD_STREAM, (fwd_stream_kernel<kStreamStages, MI, PK>), grid, st, h, a.weight, y, \
+  RLK_LAUNCH(K_FWD_STREAM, (fwd_stream_kernel<MI, PK>), grid, st, h, a.weight, y,              \
              rows, a.H, sl.Vs, Us, sl.P, sl.Gs, a.vocab_start, grid, 2 * G, pr)
       if (a.packed) {
         if (rows <= 16) RLK_STREAM(1, true);
@@ -786,10 +839,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
 hipError_t launch_pack(const uint16_t* weight, int H, const FwdSlicing& sl, uint16_t* packed,
                        hipStream_t st) {
   const int Us = cdiv(sl.Vs, 128);
-  const int64_t n_pieces = (int64_t)sl.P * Us * 16 * H;
-  const int64_t want = (n_pieces + kThreads - 1) / kThreads;
+  const int64_t n_lines = (int64_t)sl.P * Us * 128 * (H / 64);
+  const int64_t want = (n_lines + kThreads - 1) / kThreads;
   const int grid = (int)(want < 8192 ? want : 8192);
-  RLK_LAUNCH(K_PACK, pack_weight_kernel, grid, st, weight, H, sl.Vs, Us, n_pieces, packed);
+  RLK_LAUNCH(K_PACK, pack_weight_kernel, grid, st, weight, H, sl.Vs, Us, n_lines, packed);
   return hipGetLastError();
 }
 
