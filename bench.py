@@ -41,9 +41,13 @@ METRIC = "linear-logp fwd+bwd tokens/s and % bf16 MFMA peak at H4096 V151936 T51
 CSRC = os.path.join(ROOT, "rollout_rlk_linear_amd", "csrc")
 
 
+# the sources that decide the linear-logp kernels' code and launches
+HASHED_SOURCES = ("rlk_abi.cpp", "rlk_device.cuh", "rlk_internal.h", "rlk_kernels.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in HASHED_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -283,6 +287,25 @@ def workload_runs(torch, rlk, wl, read_gbs, steps):
         "TFLOPs": round(fl / (ms["median"] * 1e-3) / 1e12, 1),
         "frac_bf16_peak": round(fl / (ms["median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     wl.clear_cache()
+
+    # LoRA linear on the three shapes of the runtime report's gate (rank 16,
+    # scale 2): forward, and forward + full backward (dx, dA, dB). Base-product
+    # flops 2TKN per product (fwd 1, fwd+bwd 2); bytes of W per product.
+    lora = {}
+    for c in wl.lora_page_cases():
+        x, W, A, B, dy = (t.to("cuda:0").contiguous() for t in (c.x, c.W, c.A, c.B, c.dy))
+        yb = torch.empty(c.T, c.N, dtype=torch.bfloat16, device="cuda:0")
+        ws = torch.empty(max(256, rlk.load_library().rlk_lora_linear_workspace_bytes(
+            c.T, c.K, c.N, c.r)), dtype=torch.uint8, device="cuda:0")
+        per_f, _ = timed(torch, lambda: rlk.lora_fwd(x, W, A, B, 2.0, out=yb, ws=ws), 3, steps)
+        per_b, _ = timed(torch, lambda: (rlk.lora_fwd(x, W, A, B, 2.0, out=yb, ws=ws),
+                                         rlk.lora_bwd(x, W, A, B, dy, 2.0, ws=ws)), 3, steps)
+        mf, mb = median_ci(per_f), median_ci(per_b)
+        wbytes = 2 * c.N * c.K
+        lora[c.name] = {"rank": c.r, "fwd_ms": mf, "fwd_bwd_ms": mb,
+                        "fwd_W_GBps": round(wbytes / (mf["median"] * 1e-3) / 1e9, 1),
+                        "fwd_TFLOPs": round(2 * c.T * c.K * c.N / (mf["median"] * 1e-3) / 1e12, 2)}
+    res["lora_gate_shapes"] = lora
     return res
 
 

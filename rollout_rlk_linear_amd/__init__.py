@@ -98,6 +98,14 @@ def load_library(path: str | None = None):
     lib.rlk_profile_kernel_name.restype = ctypes.c_char_p
     lib.rlk_microbench_copy.argtypes = [vp, vp, sz, vp]
     lib.rlk_microbench_copy.restype = ctypes.c_int
+    lib.rlk_lora_linear_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.rlk_lora_linear_workspace_bytes.restype = sz
+    lib.rlk_lora_linear_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, vp, vp,
+                                        sz, vp]
+    lib.rlk_lora_linear_fwd.restype = ctypes.c_int
+    lib.rlk_lora_linear_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, vp,
+                                        f32p, f32p, vp, sz, vp]
+    lib.rlk_lora_linear_bwd.restype = ctypes.c_int
     lib.rlk_microbench_read.argtypes = [vp, sz, vp, i64, vp]
     lib.rlk_microbench_read.restype = ctypes.c_int
     lib.rlk_microbench_mfma.argtypes = [vp, i64, i64, vp]
@@ -411,3 +419,73 @@ class LinearLogp(torch.autograd.Function):
 def linear_logp(hidden, weight, targets):
     """(logp, entropy) per token; differentiable in hidden and weight."""
     return LinearLogp.apply(hidden, weight, targets)
+
+
+# ------------------------------------------------------------ LoRA linear ----
+
+def _lora_check(x, W, A, B):
+    for name, t in (("x", x), ("W", W), ("A", A), ("B", B)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    T, K = x.shape
+    N = W.shape[0]
+    r = A.shape[0]
+    if W.shape != (N, K) or A.shape != (r, K) or B.shape != (N, r):
+        raise ValueError(f"shapes x{tuple(x.shape)} W{tuple(W.shape)} A{tuple(A.shape)} "
+                         f"B{tuple(B.shape)} do not form x[T,K] W[N,K] A[r,K] B[N,r]")
+    return T, K, N, r
+
+
+def lora_fwd(x, W, A, B, scale: float = 1.0, out: torch.Tensor | None = None, ws=None):
+    """y = x W^T + scale (x A^T) B^T through ``rlk_lora_linear_fwd`` (bf16 [T,N])."""
+    lib = load_library()
+    T, K, N, r = _lora_check(x, W, A, B)
+    y = out if out is not None else torch.empty(T, N, dtype=torch.bfloat16, device=x.device)
+    nws = lib.rlk_lora_linear_workspace_bytes(T, K, N, r)
+    ws = ws if ws is not None and ws.numel() >= nws else _workspace(nws, x.device)
+    _check(lib.rlk_lora_linear_fwd(_ptr(x), _ptr(W), _ptr(A), _ptr(B), T, K, N, r, float(scale),
+                                   _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y
+
+
+def lora_bwd(x, W, A, B, dy, scale: float = 1.0, *, want_dx=True, want_da=True, want_db=True,
+             ws=None):
+    """(dx bf16 [T,K], dA fp32 [r,K], dB fp32 [N,r]) through ``rlk_lora_linear_bwd``;
+    None where not wanted. W is frozen: no gradient."""
+    lib = load_library()
+    T, K, N, r = _lora_check(x, W, A, B)
+    if dy.dtype != torch.bfloat16 or not dy.is_cuda or not dy.is_contiguous() or dy.shape != (T, N):
+        raise ValueError("dy must be a contiguous bfloat16 device tensor [T, N]")
+    dev = x.device
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=dev) if want_dx else None
+    da = torch.empty(r, K, dtype=torch.float32, device=dev) if want_da else None
+    db = torch.empty(N, r, dtype=torch.float32, device=dev) if want_db else None
+    nws = lib.rlk_lora_linear_workspace_bytes(T, K, N, r)
+    ws = ws if ws is not None and ws.numel() >= nws else _workspace(nws, dev)
+    _check(lib.rlk_lora_linear_bwd(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(dy), T, K, N, r,
+                                   float(scale), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), ws.numel(),
+                                   _stream(dev)))
+    return dx, da, db
+
+
+class _LoraLinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, W, A, B, scale):
+        ctx.save_for_backward(x, W, A, B)
+        ctx.scale = scale
+        return lora_fwd(x, W, A, B, scale)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, W, A, B = ctx.saved_tensors
+        dx, da, db = lora_bwd(x, W, A, B, dy.contiguous(), ctx.scale,
+                              want_dx=ctx.needs_input_grad[0], want_da=ctx.needs_input_grad[2],
+                              want_db=ctx.needs_input_grad[3])
+        return (dx, None, None if da is None else da.to(A.dtype),
+                None if db is None else db.to(B.dtype), None)
+
+
+def lora_linear(x, W, A, B, scale: float = 1.0):
+    """Autograd-aware LoRA linear (W frozen: it never receives a gradient)."""
+    return _LoraLinearFn.apply(x, W, A, B, scale)
+

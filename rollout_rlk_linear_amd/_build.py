@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librlk_linear.so")
 ARCH = "gfx950"
 
-SOURCES = ["rlk_kernels.hip", "rlk_microbench.hip", "rlk_abi.cpp"]
+SOURCES = ["rlk_kernels.hip", "rlk_microbench.hip", "rlk_lora.hip", "rlk_abi.cpp"]
 HEADERS = ["rlk_device.cuh", "rlk_internal.h"]
 
 

@@ -245,6 +245,42 @@ def test_fwd_packed_T0_is_noop(lib):
     assert lib.rlk_call_count(5) == before + 1
 
 
+def lora_fwd(lib, x=P, W=P, A=P, B=P, T=4, K=64, N=128, r=16, y=P, ws=P, nws=1 << 20):
+    return lib.rlk_lora_linear_fwd(x, W, A, B, T, K, N, r, 1.0, y, ws, nws, NULL)
+
+
+def lora_bwd(lib, x=P, W=P, A=P, B=P, dy=P, T=4, K=64, N=128, r=16, dx=P, da=P, db=P, ws=P,
+             nws=1 << 20):
+    return lib.rlk_lora_linear_bwd(x, W, A, B, dy, T, K, N, r, 1.0, dx, da, db, ws, nws, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(K=0), INVALID), (dict(r=0), INVALID),
+    (dict(K=96), SHAPE), (dict(N=100), SHAPE), (dict(r=65), SHAPE), (dict(K=65536 + 64), SHAPE),
+    (dict(N=(1 << 20) + 64), SHAPE), (dict(T=(1 << 21) + 1), SHAPE),
+    (dict(x=NULL), INVALID), (dict(W=NULL), INVALID), (dict(A=NULL), INVALID),
+    (dict(B=NULL), INVALID), (dict(y=NULL), INVALID), (dict(ws=NULL), INVALID),
+    (dict(x=ctypes.c_void_p((1 << 20) + 2)), INVALID), (dict(nws=4 * 16 * 8 - 1), WS_SMALL),
+])
+def test_lora_fwd_argument_errors(lib, kw, code):
+    assert lora_fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dx=NULL, da=NULL, db=NULL), INVALID), (dict(dy=NULL), INVALID), (dict(K=32), SHAPE),
+    (dict(da=ctypes.c_void_p((1 << 20) + 4)), INVALID), (dict(nws=0), WS_SMALL),
+])
+def test_lora_bwd_argument_errors(lib, kw, code):
+    assert lora_bwd(lib, **kw) == code
+
+
+def test_lora_workspace_and_empty_forward(lib):
+    f = lib.rlk_lora_linear_workspace_bytes
+    assert f(33, 5120, 5120, 16) == 4352          # u and v: 2 x 33 x 16 fp32, rounded to 256
+    assert f(0, 64, 64, 16) == 0 and f(4, 96, 64, 16) == 0
+    assert lora_fwd(lib, T=0, x=NULL, y=NULL, ws=NULL, nws=0) == OK
+
+
 def test_workspace_sizes(lib):
     f = lib.rlk_linear_logp_fwd_workspace_bytes
     assert f(0, 4096, 151936) == 0

@@ -1,0 +1,144 @@
+"""GPU tests of the LoRA linear (include/rlk_lora.h) against the float64 oracle.
+
+The runtime report's gate (page "RL-Kernel h3-runtime-integration-b200
+report.json", key lora_gate) asks of the layer: repeatable, forward rows
+independent, base frozen, and norm-wise relative errors against float64 of
+about 1.66e-3 for the bf16 outputs (y, grad x) and about 1e-6 for the fp32
+adapter gradients. A bf16 output cannot do better than its own rounding
+(rel_err of RNE over an N(0,1) tensor is 1.66e-3), so the bars here are: y and
+dx within 2e-3, every element within half a bf16 ulp plus the fp32
+accumulation bound of the float64 value (and equal to its correct rounding
+for >= 99% of the elements); dA and dB within 1e-5. Row independence and repeatability are checked bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import rollout_rlk_linear_amd as rlk
+import workloads as wl
+from oracle import lora_backward, lora_forward, rel_err
+from tests._util import bits_equal, dev
+
+pytestmark = pytest.mark.gpu
+
+BF16_BAR = 2e-3
+F32_BAR = 1e-5
+
+
+def rounding_check(got_bf16, ref64, abs_terms, n_terms, what):
+    """bf16 output vs the float64 value: within half a bf16 ulp plus the fp32
+    accumulation bound (n_terms * 2^-24 * sum of |terms|), and equal to the
+    correctly rounded value for >= 99% of the elements."""
+    got = got_bf16.cpu().float().double().numpy()
+    ulp = np.spacing(np.abs(got).astype(np.float32)).astype(np.float64) * 2.0 ** 16
+    bound = 0.5 * ulp + n_terms * 2.0 ** -24 * abs_terms
+    err = np.abs(got - ref64)
+    assert np.all(err <= bound), f"{what}: worst excess {float((err - bound).max()):.3e}"
+    want = torch.from_numpy(ref64).to(torch.bfloat16).float().double().numpy()
+    assert (got == want).mean() >= 0.99, f"{what}: only {(got == want).mean():.4f} correctly rounded"
+
+
+def abs_terms_y(c, scale):
+    x, W, A, B = (np.abs(t.double().numpy()) for t in (c.x, c.W, c.A, c.B))
+    return x @ W.T + abs(scale) * ((x @ A.T) @ B.T)
+
+
+def abs_terms_dx(c, scale):
+    dy, W, A, B = (np.abs(t.double().numpy()) for t in (c.dy, c.W, c.A, c.B))
+    return dy @ W + abs(scale) * ((dy @ B) @ A)
+
+
+def run(c, scale, **kw):
+    x, W, A, B, dy = (dev(t) for t in (c.x, c.W, c.A, c.B, c.dy))
+    y = rlk.lora_fwd(x, W, A, B, scale)
+    dx, da, db = rlk.lora_bwd(x, W, A, B, dy, scale, **kw)
+    torch.cuda.synchronize()
+    return x, W, A, B, dy, y, dx, da, db
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_page_shapes_against_float64(idx):
+    c = wl.lora_page_cases()[idx]
+    scale = 2.0
+    _, _, _, _, _, y, dx, da, db = run(c, scale)
+    f = lora_forward(c.x, c.W, c.A, c.B, scale)
+    g = lora_backward(c.x, c.W, c.A, c.B, c.dy, scale)
+    ey, ex = rel_err(y.cpu(), f["y"]), rel_err(dx.cpu(), g["dx"])
+    ea, eb = rel_err(da.cpu().double().numpy(), g["dA"]), rel_err(db.cpu().double().numpy(), g["dB"])
+    assert ey <= BF16_BAR and ex <= BF16_BAR, (ey, ex)
+    assert ea <= F32_BAR and eb <= F32_BAR, (ea, eb)
+    rounding_check(y, f["y"], abs_terms_y(c, scale), c.K + c.r + 2, f"{c.name} y")
+    rounding_check(dx, g["dx"], abs_terms_dx(c, scale), c.N + c.r + 2, f"{c.name} dx")
+
+
+@pytest.mark.parametrize("T,K,N,r,scale", [
+    (1, 64, 64, 1, 1.0), (63, 128, 192, 16, 0.5), (64, 256, 128, 64, 2.0),
+    (65, 192, 320, 8, 1.0), (200, 384, 512, 16, -1.5), (3, 1024, 64, 32, 1.0),
+])
+def test_ragged_shapes_and_ranks(T, K, N, r, scale):
+    c = wl.lora_case(N, K, T, 50 + T, r=r)
+    _, _, _, _, _, y, dx, da, db = run(c, scale)
+    f = lora_forward(c.x, c.W, c.A, c.B, scale)
+    g = lora_backward(c.x, c.W, c.A, c.B, c.dy, scale)
+    rounding_check(y, f["y"], abs_terms_y(c, scale), K + r + 2, "y")
+    rounding_check(dx, g["dx"], abs_terms_dx(c, scale), N + r + 2, "dx")
+    assert rel_err(da.cpu().double().numpy(), g["dA"]) <= F32_BAR
+    assert rel_err(db.cpu().double().numpy(), g["dB"]) <= F32_BAR
+
+
+def test_rows_independent_bitwise():
+    c = wl.lora_page_cases()[1]  # N2048 K1024 T257
+    x, W, A, B, dy, y, dx, _, _ = run(c, 2.0)
+    for r0, r1 in ((0, 1), (5, 9), (60, 130), (256, 257), (0, 64)):
+        ys = rlk.lora_fwd(x[r0:r1].contiguous(), W, A, B, 2.0)
+        dxs, _, _ = rlk.lora_bwd(x[r0:r1].contiguous(), W, A, B, dy[r0:r1].contiguous(), 2.0,
+                                 want_da=False, want_db=False)
+        torch.cuda.synchronize()
+        assert bits_equal(ys, y[r0:r1]), f"y rows {r0}:{r1}"
+        assert bits_equal(dxs, dx[r0:r1]), f"dx rows {r0}:{r1}"
+    # a permutation of the rows permutes the outputs, bit for bit
+    p = torch.randperm(c.T, generator=torch.Generator().manual_seed(5)).cuda()
+    yp = rlk.lora_fwd(x[p].contiguous(), W, A, B, 2.0)
+    torch.cuda.synchronize()
+    assert bits_equal(yp, y[p])
+
+
+def test_repeatable_and_base_frozen():
+    c = wl.lora_page_cases()[2]  # N5120 K5120 T33
+    x, W, A, B, dy = (dev(t) for t in (c.x, c.W, c.A, c.B, c.dy))
+    W0 = W.clone()
+    outs = []
+    for _ in range(3):
+        y = rlk.lora_fwd(x, W, A, B, 2.0)
+        outs.append((y, *rlk.lora_bwd(x, W, A, B, dy, 2.0)))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert bits_equal(a, b)
+    assert torch.equal(W, W0), "the base weight changed"
+
+
+def test_autograd_wrapper_matches_and_freezes_base():
+    c = wl.lora_case(256, 128, 40, 61)
+    x, W, A, B, dy = (dev(t) for t in (c.x, c.W, c.A, c.B, c.dy))
+    xr, Ar, Br = (t.clone().requires_grad_(True) for t in (x, A, B))
+    y = rlk.lora_linear(xr, W, Ar, Br, 2.0)
+    y.backward(dy)
+    dx, da, db = rlk.lora_bwd(x, W, A, B, dy, 2.0)
+    torch.cuda.synchronize()
+    assert W.grad is None
+    assert torch.equal(xr.grad, dx)
+    assert torch.equal(Ar.grad, da.to(torch.bfloat16))
+    assert torch.equal(Br.grad, db.to(torch.bfloat16))
+
+
+def test_empty_batch():
+    c = wl.lora_case(128, 64, 1, 62)
+    x, W, A, B = (dev(t) for t in (c.x, c.W, c.A, c.B))
+    x0 = x[:0].contiguous()
+    assert rlk.lora_fwd(x0, W, A, B).shape == (0, 128)
+    dx, da, db = rlk.lora_bwd(x0, W, A, B, torch.empty(0, 128, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 64)
+    assert torch.count_nonzero(da) == 0 and torch.count_nonzero(db) == 0
