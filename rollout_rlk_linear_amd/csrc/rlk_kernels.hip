@@ -344,37 +344,28 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
 // (k = 32 s .. + 31) is 8 KB at s 4096 inside it, laid out exactly as a B
 // slot of the ring: 16-byte piece i of 1 KB block jb holds row 16 jb + i / 4,
 // k piece (i % 4) ^ row_swz(i / 4). Rows past the slice are zero.
-// One thread moves one 128-byte line of a W row (two stages' worth of that
-// row: each line is read once) to its two 64-byte slots; consecutive threads
-// take consecutive rows, so the slots they write are contiguous.
+// One thread moves one 16-byte piece: eight consecutive threads read one
+// whole 128-byte line of a W row (two stages' worth of that row), a wave
+// reads eight rows' lines, and its writes fill two 512-byte runs of slots.
 __global__ __launch_bounds__(kThreads) void pack_weight_kernel(
-    const uint16_t* __restrict__ weight, int H, int Vs, int Us, int64_t n_lines,
+    const uint16_t* __restrict__ weight, int H, int Vs, int Us, int64_t n_pieces,
     uint16_t* __restrict__ packed) {
   const int pairs = H / 64;  // 128-byte lines per W row
-  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n_lines;
-       idx += (int64_t)gridDim.x * kThreads) {
-    const int r = (int)(idx & 127);
-    const int64_t rest = idx >> 7;
+  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < n_pieces;
+       q += (int64_t)gridDim.x * kThreads) {
+    const int e = (int)(q & 7);  // 16-byte piece of the line
+    const int r = (int)((q >> 3) & 127);
+    const int64_t rest = q >> 10;
     const int s2 = (int)(rest % pairs);
     const int64_t pu = rest / pairs;
     const int p = (int)(pu / Us), iu = (int)(pu - (int64_t)p * Us);
     const int srow = 128 * iu + r;
-    u32x4 v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = u32x4{0u, 0u, 0u, 0u};
-    if (srow < Vs) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(weight + ((int64_t)p * Vs + srow) * H + 64 * s2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = src[e];
-    }
-    const int sw = row_swz(r & 15);
-    uint16_t* unit = packed + pu * 128 * H;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4* dst = reinterpret_cast<u32x4*>(unit + (int64_t)(2 * s2 + h) * 4096 + 32 * r);
-#pragma unroll
-      for (int kp = 0; kp < 4; ++kp) dst[kp ^ sw] = v[4 * h + kp];
-    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (srow < Vs)
+      v = *reinterpret_cast<const u32x4*>(weight + ((int64_t)p * Vs + srow) * H + 64 * s2 + 8 * e);
+    uint16_t* dst = packed + pu * 128 * H + (int64_t)(2 * s2 + (e >> 2)) * 4096 + 32 * r +
+                    8 * ((e & 3) ^ row_swz(r & 15));
+    *reinterpret_cast<u32x4*>(dst) = v;
   }
 }
 
@@ -395,27 +386,24 @@ __device__ __forceinline__ void finalize_row(const Part& acc, bool target_ok, fl
 // One wave per row. Each virtual slice's groups: lane j folds groups j,
 // j + 64, ... of the slice in order, then a 64-lane xor tree (lower lane
 // left); the P slice records then merge by the fixed tree (P = 1, 2 or 4).
-// With units = 2 the records are per 128-column half (fwd_chunk_kernel) and
-// a group's record is merged from its halves here, as fwd_tile merges them.
+// One workgroup per row; wave p folds virtual slice p: lane j merges groups
+// j, j + 64, ... in order (their records loaded four at a time ahead of the
+// merges), then a 64-lane xor tree with the lower lane as left operand; wave
+// 0 merges the slice records by the fixed tree and finalises. With units = 2
+// the records are per 128-column half (the streaming kernel) and a group's
+// record is merged from its halves here, as fwd_tile merges them.
 __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(
     const float4* __restrict__ part, const int32_t* __restrict__ targets, int T, int G, int P,
     int Gs, int Vs, int units, int64_t vocab_total, int full, float* __restrict__ logp,
     float* __restrict__ entropy, float4* __restrict__ stats) {
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  static_assert(kThreads / 64 >= kVirtualSlices, "a wave per virtual slice");
+  __shared__ float4 srec[kVirtualSlices];
+  const int row = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  if (row >= T) return;
+  const int p = wave_id();
   const float4* pr = part + (int64_t)row * G * units;
-  // Lane j folds groups j, j + 64, ... of each slice in order. The records of
-  // the first four of them in every slice are loaded before any merge, the
-  // rest in batches of four, so the load latency is paid once per batch
-  // rather than once per record; the merge order is unchanged.
   constexpr int NB = 4;
-  auto group_rec = [&](const float4& a, const float4& b, int g) {
-    Part q{a.x, a.y, a.z, a.w};
-    if (units == 2 && 128 < min(GROUP, Vs - g * GROUP)) q = part_merge(q, Part{b.x, b.y, b.z, b.w});
-    return q;
-  };
-  auto load = [&](int p, int g, float4& a, float4& b) {
+  auto load = [&](int g, float4& a, float4& b) {
     if (units == 1) {
       a = pr[p * Gs + g];
     } else {
@@ -423,45 +411,40 @@ __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(
       if (128 < min(GROUP, Vs - g * GROUP)) b = pr[2 * (p * Gs + g) + 1];
     }
   };
-  Part rs[kVirtualSlices];
-  float4 qa[kVirtualSlices][NB], qb[kVirtualSlices][NB];
+  auto group_rec = [&](const float4& a, const float4& b, int g) {
+    Part q{a.x, a.y, a.z, a.w};
+    if (units == 2 && 128 < min(GROUP, Vs - g * GROUP)) q = part_merge(q, Part{b.x, b.y, b.z, b.w});
+    return q;
+  };
+  if (p < P) {
+    Part acc = part_empty();
+    for (int g0 = lane; g0 < Gs; g0 += 64 * NB) {
+      float4 ta[NB], tb[NB];
 #pragma unroll
-  for (int p = 0; p < kVirtualSlices; ++p)
+      for (int b = 0; b < NB; ++b)
+        if (g0 + 64 * b < Gs) load(g0 + 64 * b, ta[b], tb[b]);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int g = lane + 64 * b;
-      if (p < P && g < Gs) load(p, g, qa[p][b], qb[p][b]);
+      for (int b = 0; b < NB; ++b)
+        if (g0 + 64 * b < Gs) acc = part_merge(acc, group_rec(ta[b], tb[b], g0 + 64 * b));
     }
 #pragma unroll
-  for (int p = 0; p < kVirtualSlices; ++p) {
-    if (p < P) {
-      Part acc = part_empty();
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int g = lane + 64 * b;
-        if (g < Gs) acc = part_merge(acc, group_rec(qa[p][b], qb[p][b], g));
-      }
-      for (int g0 = lane + 64 * NB; g0 < Gs; g0 += 64 * NB) {
-        float4 ta[NB], tb[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          if (g0 + 64 * b < Gs) load(p, g0 + 64 * b, ta[b], tb[b]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          if (g0 + 64 * b < Gs) acc = part_merge(acc, group_rec(ta[b], tb[b], g0 + 64 * b));
-      }
-#pragma unroll
-      for (int s = 1; s < 64; s <<= 1) {
-        const Part o = shfl_xor_part(acc, s);
-        acc = (lane & s) ? part_merge(o, acc) : part_merge(acc, o);
-      }
-      rs[p] = acc;
+    for (int s = 1; s < 64; s <<= 1) {
+      const Part o = shfl_xor_part(acc, s);
+      acc = (lane & s) ? part_merge(o, acc) : part_merge(acc, o);
     }
+    if (lane == 0) srec[p] = make_float4(acc.m, acc.R, acc.B, acc.zy);
   }
-  Part acc = rs[0];
-  if (P == 2) acc = part_merge(rs[0], rs[1]);
-  if (P == 4) acc = part_merge(part_merge(rs[0], rs[1]), part_merge(rs[2], rs[3]));
-  if (lane == 0) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Part rs[kVirtualSlices];
+#pragma unroll
+    for (int q = 0; q < kVirtualSlices; ++q) {
+      const float4 v = srec[q < P ? q : 0];
+      rs[q] = Part{v.x, v.y, v.z, v.w};
+    }
+    Part acc = rs[0];
+    if (P == 2) acc = part_merge(rs[0], rs[1]);
+    if (P == 4) acc = part_merge(part_merge(rs[0], rs[1]), part_merge(rs[2], rs[3]));
     if (stats) stats[row] = make_float4(acc.m, acc.R, acc.B, acc.zy);
     if (full) {
       const int32_t y = targets[row];
@@ -831,7 +814,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
     RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2>), G8 * nt, st, a.hidden, a.weight,
                a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, a.part);
   }
-  RLK_LAUNCH(K_FWD_COMBINE, fwd_combine_kernel, cdiv(a.T, kThreads / 64), st, a.part, a.targets,
+  RLK_LAUNCH(K_FWD_COMBINE, fwd_combine_kernel, a.T, st, a.part, a.targets,
              a.T, G, sl.P, sl.Gs, sl.Vs, units, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
   return hipGetLastError();
 }
@@ -839,10 +822,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
 hipError_t launch_pack(const uint16_t* weight, int H, const FwdSlicing& sl, uint16_t* packed,
                        hipStream_t st) {
   const int Us = cdiv(sl.Vs, 128);
-  const int64_t n_lines = (int64_t)sl.P * Us * 128 * (H / 64);
-  const int64_t want = (n_lines + kThreads - 1) / kThreads;
-  const int grid = (int)(want < 8192 ? want : 8192);
-  RLK_LAUNCH(K_PACK, pack_weight_kernel, grid, st, weight, H, sl.Vs, Us, n_lines, packed);
+  const int64_t n_pieces = (int64_t)sl.P * Us * 16 * H;
+  const int64_t want = (n_pieces + kThreads - 1) / kThreads;
+  const int grid = (int)(want < 16384 ? want : 16384);
+  RLK_LAUNCH(K_PACK, pack_weight_kernel, grid, st, weight, H, sl.Vs, Us, n_pieces, packed);
   return hipGetLastError();
 }
 
