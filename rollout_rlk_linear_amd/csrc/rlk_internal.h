@@ -8,9 +8,11 @@
 
 namespace rlk {
 
-// Batches of at most this many rows use 32-row tiles, larger ones 256-row
-// tiles. Both instantiate the same per-element arithmetic and reduction
-// order, so a row's bits do not depend on which one ran.
+// Batches of at most this many rows run the forward as a stream over W
+// (fwd_stream_kernel) and the backward on 32-row tiles; larger ones run
+// 256-row tiles. All of them compute each logit by the same MFMA chain and
+// each record by the same reduction order, so a row's bits do not depend on
+// which one ran.
 constexpr int kSmallT = 64;
 
 // dH is reduced over fixed vocabulary splits: at most kMaxSplits of them,

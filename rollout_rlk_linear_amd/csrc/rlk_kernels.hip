@@ -623,22 +623,44 @@ __device__ __forceinline__ void dw_tile(unsigned char* lds, const uint16_t* __re
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % 2, wn = wave / 2;
-  // rows past the chunk or the vocabulary are skipped per lane; a 16-column
-  // block is whole or absent (H is a multiple of 64), a wave-uniform test
+  // The output leaves through the freed ring, 128 rows at a time: the two
+  // waves that own the rows write their accumulators to LDS, then every wave
+  // stores whole rows, 32 lanes x 16 bytes covering one 512-byte row segment,
+  // so each write request carries full lines (written from the accumulator
+  // layout, a store instruction carries 64-byte pieces of four rows).
+  static_assert(Gm::WTM == 128 && kDwBN == 128, "one half-tile of rows per wave row");
+  constexpr int ZS = kDwBN + 4;  // floats per staged row (conflict-free writes)
+  static_assert(128 * ZS * 4 <= Gm::LDS_BYTES, "half a tile fits the ring");
+  float* stage = reinterpret_cast<float*>(lds);
   const int vlim = min(chunk_w, V - chunk_v0);
-  const int hb = h0 + wn * Gm::WTN;
-  float* const base = dweight + (int64_t)chunk_v0 * H + hb + (lane & 15);
+  const int hcols = min(kDwBN, H - h0);  // a multiple of 64
+  const int c4 = 4 * (lane & 31);        // column of this lane's 16 bytes
 #pragma unroll
-  for (int i = 0; i < Gm::MI; ++i) {
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int vl = v0 + wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
-      if (vl >= vlim) continue;
-      float* rowp = base + (int64_t)vl * H;
+      for (int i = 0; i < Gm::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < Gm::NJ; ++j)
-        if (hb + 16 * j < H) __builtin_nontemporal_store(gm.acc[i][j][r], rowp + 16 * j);
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * i + 4 * (lane >> 4) + r;
+#pragma unroll
+          for (int j = 0; j < Gm::NJ; ++j)
+            stage[row * ZS + wn * Gm::WTN + 16 * j + (lane & 15)] = gm.acc[i][j][r];
+        }
     }
+    __syncthreads();
+    // wave w stores rows 2 k + lane / 32 for k = w, w + 4, ...
+#pragma unroll 4
+    for (int k = wave; k < 64; k += 4) {
+      const int row = 2 * k + (lane >> 5);
+      const int vl = v0 + 128 * half + row;
+      if (vl < vlim && c4 < hcols) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * ZS + c4);
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<f32x4*>(dweight + (int64_t)(chunk_v0 + vl) * H + h0 + c4));
+      }
+    }
+    __syncthreads();
   }
 }
 
