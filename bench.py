@@ -68,18 +68,24 @@ def load_traffic(kernel: str):
 
 
 def algorithmic_work(T, H, V, nsplits):
-    """Per-step algorithmic flops (MFMA kernels) and bytes (the others)."""
+    """Per-step algorithmic flops and HBM bytes of each kernel: every operand
+    read once and every output written once (G = the bf16 logit gradient
+    [T][V], records 16 B per row and 256-column group, dH split partials fp32)."""
     G = -(-V // 256)
     f = 2.0 * T * H * V
+    W, h, Gt = 2.0 * V * H, 2.0 * T * H, 2.0 * T * V
     return {
-        "fwd_tile": ("flops", f),
-        "bwd_recompute": ("flops", f),
-        "bwd_dw": ("flops", f),
-        "bwd_dh": ("flops", f),
-        "fwd_combine": ("bytes", T * G * 16 + T * 4 * 6),
-        "bwd_rowprep": ("bytes", T * (16 + 12 + 32)),
-        "bwd_dh_reduce": ("bytes", nsplits * T * H * 4 + T * H * 2),
+        "fwd_tile": (f, W + h + 16.0 * T * G),
+        "bwd_recompute": (f, W + h + Gt),
+        "bwd_dw": (f, Gt + h + 4.0 * V * H),
+        "bwd_dh": (f, Gt + W + 4.0 * nsplits * T * H),
+        "fwd_combine": (0.0, T * G * 16.0 + T * 4 * 6.0),
+        "bwd_rowprep": (0.0, T * (16 + 12 + 32.0)),
+        "bwd_dh_reduce": (0.0, nsplits * T * H * 4.0 + T * H * 2.0),
     }
+
+
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/B where the two roofs meet
 
 
 def median_ci(xs):
@@ -432,16 +438,19 @@ def main():
     for k, (ms, n) in prof.items():
         if n == 0:
             continue
-        kind, per_step = work.get(k, ("bytes", 0.0))
-        per_launch = per_step / max(1, launches[k])
+        fl, by = work.get(k, (0.0, 0.0))
+        nl = max(1, launches[k])
+        fl_l, by_l = fl / nl, by / nl
         avg_s = ms / n / 1e3
-        rate = per_launch / avg_s / (1e12 if kind == "flops" else 1e9)
+        ai = fl_l / by_l if by_l else None
         kernels[k] = {"ms_per_step": ms / args.steps, "launches_per_step": launches[k],
-                      "avg_launch_ms": ms / n, "kind": kind, "work_per_launch": per_launch,
-                      ("tflops" if kind == "flops" else "gbs"): rate}
+                      "avg_launch_ms": ms / n, "flops_per_launch": fl_l, "bytes_per_launch": by_l,
+                      "flop_per_byte": round(ai, 1) if ai else None,
+                      "bound": "mfma" if fl_l and ai >= RIDGE else "hbm",
+                      "tflops": fl_l / avg_s / 1e12, "gbs": by_l / avg_s / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
-    if dk["kind"] == "flops":
+    if dk["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": round(dk["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4)}
     else:
@@ -449,6 +458,9 @@ def main():
                 "unit": "GB/s", "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4)}
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(dk["avg_launch_ms"], 4)
+    roof["flop_per_byte"] = dk["flop_per_byte"]
+    roof["ridge_flop_per_byte"] = round(RIDGE, 1)
+    roof["tflops"] = round(dk["tflops"], 2)
     roof["traffic"] = load_traffic(dom)
 
     result = {
