@@ -104,6 +104,50 @@ def test_ragged_shapes(T, H, V):
         assert float(dh.float().abs().max()) == 0.0 and float(dw.abs().max()) == 0.0
 
 
+# ------------------------------------------------------- maximum sizes
+
+@pytest.mark.parametrize("T", [3, 70])
+def test_max_hidden_size(T):
+    # H = 65536 (RLK_MAX_H): the largest operand rows; T = 3 takes the
+    # streaming forward (natural and packed W), T = 70 the tile kernels
+    H, V = 65536, 300
+    c = wl.make_case("maxH", T, H, V, seed=70 + T, rms=True)
+    d = case_to_device(c)
+    o = run_fwd(d)
+    ref = forward(c.hidden, c.weight, c.targets)
+    check_logp(o["logp"].cpu().numpy(), ref["logp"], f"logp T={T} H={H}")
+    check_entropy(o["entropy"].cpu().numpy(), ref["entropy"], f"entropy T={T} H={H}")
+    op = rlk.fwd_packed(d["hidden"], rlk.pack_weight(d["weight"]), d["targets"])
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], d["dentropy"])
+    torch.cuda.synchronize()
+    for k in ("logp", "entropy", "stats"):
+        assert torch.equal(op[k].view(torch.int32), o[k].view(torch.int32)), f"packed {k}"
+    rb = backward(c.hidden, c.weight, c.targets, c.dlogp, c.dentropy)
+    check_grad(f64(dh), rb["dH"], f"dH T={T} H={H}")
+    check_grad(f64(dw), rb["dW"], f"dW T={T} H={H}")
+    check_column_sum(dw, f"dW T={T} H={H}")
+
+
+def test_max_batch_size():
+    # T = 2^21 (RLK_MAX_T) rows: every row tile and dW's 2^21-long reduction;
+    # sampled rows and vocabulary entries against the oracle
+    T, H, V = 1 << 21, 64, 256
+    c = wl.make_case("maxT", T, H, V, seed=77, rms=False)
+    d = case_to_device(c)
+    o = run_fwd(d)
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], None)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, T, 4099), [T - 1]]))
+    ref = forward(c.hidden[rows], c.weight, c.targets[rows])
+    check_logp(o["logp"].cpu().numpy()[rows], ref["logp"], "logp T=2^21")
+    check_entropy(o["entropy"].cpu().numpy()[rows], ref["entropy"], "entropy T=2^21")
+    vrows = np.array([0, 5, 100, 255])
+    rb = backward(c.hidden, c.weight, c.targets, c.dlogp, None, dh_rows=rows, dw_rows=vrows)
+    check_grad(f64(dh[torch.from_numpy(rows).cuda()]), rb["dH"], "dH rows T=2^21")
+    check_grad(f64(dw[torch.from_numpy(vrows).cuda()]), rb["dW"], "dW rows T=2^21")
+    check_column_sum(dw, "dW T=2^21")
+
+
 def test_single_entry_vocabulary():
     c = wl.make_case("v1", 5, 64, 1, seed=3)
     o = run_fwd(case_to_device(c))
