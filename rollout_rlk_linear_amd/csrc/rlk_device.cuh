@@ -1,9 +1,10 @@
 // rlk_device.cuh — device building blocks for the gfx950 linear log-prob kernels.
 //
 // * LDS-DMA fed bf16 MFMA mainloops (v_mfma_f32_16x16x32_bf16) computing a
-//   BM x BN fp32 tile with K walked in ascending steps of 32: AsyncGemm for
-//   two K-contiguous operands (A * B^T), AsyncGemmKN for a K-major B (A * B,
-//   fragments assembled by transposing LDS reads).
+//   BM x BN fp32 tile with K walked in ascending steps of 32: AsyncGemmP for
+//   two K-contiguous operands (A * B^T), AsyncGemmKN for a K-major B (A * B)
+//   and AsyncGemmKK for two K-major operands (A^T * B), the last two with
+//   fragments assembled by transposing LDS reads.
 // * The fixed-order reductions that make every output row independent of the
 //   batch: a 16-lane DPP tree, the (m, R, B, zy) merge algebra, bf16 RNE.
 //
@@ -223,44 +224,41 @@ __device__ __forceinline__ void barrier_only() {
 }
 
 // C[BM x BN] += A[BM x K] * B[BN x K]^T, both operands K-contiguous
-// (element (r, k) at base[r * ld + k]). k runs over [k_begin, k_end) in
-// ascending MFMA steps of 32, starting at k_begin; (k_end - k_begin) must be
-// a multiple of 32 and every row must hold at least k_end elements past its
-// start. WM x WN waves (4 or 8); wave (wm, wn) owns rows wm*WTM.. and
+// (element (r, k) at base[r * ld + k]), rows past a_rows / b_rows reading as
+// zero. k runs over [k_begin, k_end) in ascending MFMA steps of 32;
+// (k_end - k_begin) must be a multiple of 64 and every valid row must hold
+// k_end elements. WM x WN = 4 waves; wave (wm, wn) owns rows wm*WTM.. and
 // columns wn*WTN.. of the tile, and acc[i][j][r] is element
 // (row wm*WTM + 16 i + 4 (lane / 16) + r, col wn*WTN + 16 j + lane % 16).
-// NSTG slots (3 to 8) of LDS ring.
 //
-// run() is the whole loop for a workgroup of WM x WN waves. setup(),
-// issue(), wait_for() and compute() are its steps, for kernels that drive
-// several groups of waves through one barrier sequence: wait_for(s), then a
-// barrier, then issue(s + NST - 1) and compute(s).
-template <int BM, int BN, int WM, int WN, int NSTG = 4>
-struct AsyncGemm {
+// k-steps are staged in pairs: a slot holds 128 bytes of each operand row
+// (two k-steps), so each group of eight 16-byte DMA pieces of a row is one
+// whole 128-byte line and every L2 request carries a full line (with
+// 64-byte rows each line takes two requests; with W streaming from HBM the
+// number of requests in flight per CU is what bounds the copy rate). Two
+// slots: the pair after the one being multiplied is in flight, its DMA
+// blocks issued between the first k-step's MFMAs. The 16-byte pieces of row
+// r are XOR-permuted by (r ^ (r >> 3)) & 7, which keeps the 16-row fragment
+// reads free of bank conflicts. Within a k-step all B fragments and two A
+// fragments are read first, then A fragment i+2 is read while the MFMAs of
+// row block i run (scheduling group barriers pin the order).
+template <int BM, int BN, int WM, int WN>
+struct AsyncGemmP {
   static constexpr int NW = WM * WN;
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves per tile");
-  static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row DMA blocks");
-  static_assert(NSTG >= 3 && NSTG <= 8, "3- to 8-slot ring");
+  static_assert(NW == 4, "4 waves per tile");
+  static_assert(BM % 8 == 0 && BN % 8 == 0, "8-row DMA blocks");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NJ = WTN / 16;
-  static constexpr int NST = NSTG;
-  static constexpr int ROWB = 64;                       // bytes per staged row
-  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
-  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
-  static constexpr int NI_A = BM / 16, NI_B = BN / 16;  // 1 KB DMA blocks per stage
+  static constexpr int ROWB = 128;
+  static constexpr int SLOT_BYTES = (BM + BN) * ROWB;
+  static constexpr int LDS_BYTES = 2 * SLOT_BYTES;
+  static constexpr int NI_A = BM / 8, NI_B = BN / 8;  // 1 KB blocks = 8 rows
   static constexpr int NI = NI_A + NI_B;
-  static constexpr int NI_W_MAX = (NI + NW - 1) / NW;   // blocks issued by one wave per stage
-  static constexpr int NI_W_MIN = NI / NW;
+  static_assert(NI_A % NW == 0 && NI % NW == 0, "DMA blocks divide among the waves");
+  static constexpr int NB = NI / NW;  // blocks per wave per pair
+  static __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
   f32x4 acc[MI][NJ];
-  // loop state (wave-uniform except voff and foff)
-  unsigned char* lds_;
-  uint32_t lds0_;
-  i32x4 rsA_, rsB_;
-  int voff_[NI_W_MAX];
-  int foff_;
-  int wave_, wm_, wn_;
-  int k_begin_, nsteps_;
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -269,152 +267,91 @@ struct AsyncGemm {
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // lds: LDS_BYTES of shared memory (16-byte aligned), this tile's ring.
-  // A, B: row 0 of the tile; lda, ldb in elements; a_rows, b_rows: valid
-  // rows (<= 0: none); wave: 0 .. NW-1 within the waves sharing the tile.
-  // Returns the number of k-steps.
-  __device__ __forceinline__ int setup(unsigned char* lds, const uint16_t* A, int64_t lda,
-                                       int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
-                                       int k_begin, int k_end, int wave) {
-    const int lane = threadIdx.x & 63;
-    lds_ = lds;
-    lds0_ = lds_addr(lds);
-    wave_ = wave;
-    wm_ = wave % WM;
-    wn_ = wave / WM;
-    k_begin_ = k_begin;
-    nsteps_ = (k_end - k_begin) / 32;
-    // buffer resources over the valid rows only (rows past them read as zero)
-    const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
-    const int br = b_rows < 0 ? 0 : (b_rows > BN ? BN : b_rows);
-    rsA_ = make_rsrc(A, (uint32_t)(ar * lda * 2));
-    rsB_ = make_rsrc(B, (uint32_t)(br * ldb * 2));
-    // lane -> (row within a 16-row block, logical 16-byte piece) of one DMA block
-    const int drow = lane >> 2;
-    const int dpiece = (lane & 3) ^ row_swz(lane >> 2);
-#pragma unroll
-    for (int ii = 0; ii < NI_W_MAX; ++ii) {
-      const int j = wave + NW * ii;
-      if (j < NI_A)
-        voff_[ii] = (int)((16 * j + drow) * lda * 2) + 16 * dpiece;
-      else
-        voff_[ii] = (int)((16 * (j - NI_A) + drow) * ldb * 2) + 16 * dpiece;
-    }
-    // fragment read offset of this lane inside a 16-row block (swizzled)
-    foff_ = (lane & 15) * ROWB + 16 * ((lane >> 4) ^ row_swz(lane & 15));
-    return nsteps_;
-  }
-
-  // DMA of stage s into slot s % NST. When the A blocks divide evenly among
-  // the waves, which operand block ii of a wave belongs to is known at
-  // compile time (block wave + NW ii is an A block iff ii < NI_A / NW).
-  __device__ __forceinline__ void issue(int s) {
-    const uint32_t st = lds0_ + (uint32_t)((s % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave_;
-    const int koff = (k_begin_ + 32 * s) * 2;
-    if constexpr (NI_A % NW == 0 && NI % NW == 0) {
-#pragma unroll
-      for (int ii = 0; ii < NI / NW; ++ii)
-        dma16(ii < NI_A / NW ? rsA_ : rsB_, st + 1024u * NW * ii, voff_[ii], koff);
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < NI_W_MAX; ++ii) {
-        const int j = wave_ + NW * ii;
-        if (j < NI) {
-          if (j < NI_A)
-            dma16(rsA_, st + 1024u * NW * ii, voff_[ii], koff);
-          else
-            dma16(rsB_, st + 1024u * NW * ii, voff_[ii], koff);
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void prologue() {
-    for (int s = 0; s < NST - 1 && s < nsteps_; ++s) issue(s);
-  }
-
-  // Wait until this wave's DMA of stage s has landed, given that stages up
-  // to s + NST - 2 (clamped) have been issued and nothing else is pending.
-  __device__ __forceinline__ void wait_for(int s) { wait_until(s, s + NST - 2); }
-
-  // Fragments of stage s from LDS, then its MFMAs. All B fragments and the
-  // first two A fragments are read up front; A fragment i+2 is read while
-  // the MFMAs of row block i run, so most of the LDS reads overlap MFMAs.
-  // If dma_stage >= 0 its DMA blocks are issued one per row block, between
-  // the MFMAs (its slot must already be free).
-  __device__ __forceinline__ void compute(int s, int dma_stage = -1) {
-    const unsigned char* st = lds_ + (s % NST) * STAGE_BYTES;
-    bf16x8 af[MI], bfr[NJ];
-    constexpr int A0 = MI < 2 ? MI : 2;
-    constexpr bool SPLIT = NI_A % NW == 0 && NI % NW == 0 && NI / NW <= MI;
-    if constexpr (!SPLIT) {
-      if (dma_stage >= 0) issue(dma_stage);
-    }
-    const uint32_t dst = lds0_ + (uint32_t)((dma_stage % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave_;
-    const int koff = (k_begin_ + 32 * dma_stage) * 2;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      bfr[j] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn_ * WTN + 16 * j) * ROWB + foff_));
-#pragma unroll
-    for (int i = 0; i < A0; ++i)
-      af[i] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * i) * ROWB + foff_));
-    __builtin_amdgcn_sched_group_barrier(0x100, NJ + A0, 0);  // DS reads
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      if (i + A0 < MI)
-        af[i + A0] = __builtin_bit_cast(
-            bf16x8,
-            *reinterpret_cast<const u32x4*>(st + (wm_ * WTM + 16 * (i + A0)) * ROWB + foff_));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      if (i + A0 < MI) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // the next A read
-        __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);  // the rest of the row
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
-      }
-      if constexpr (SPLIT) {
-        if (i < NI / NW && dma_stage >= 0)
-          dma16(i < NI_A / NW ? rsA_ : rsB_, dst + 1024u * NW * i, voff_[i], koff);
-      }
-    }
-  }
-
-  // Wait for this wave's DMA of stage `want` when stages up to `last`
-  // (clamped to the final stage) have been issued and nothing else is pending.
-  __device__ __forceinline__ void wait_until(int want, int last) {
-    last = last < nsteps_ - 1 ? last : nsteps_ - 1;
-    switch (last - want) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<NI_W_MIN>(); break;
-      case 2: wait_vmcnt<2 * NI_W_MIN>(); break;
-      case 3: wait_vmcnt<3 * NI_W_MIN>(); break;
-      case 4: wait_vmcnt<(NST > 5 ? 4 : 3) * NI_W_MIN>(); break;
-      case 5: wait_vmcnt<(NST > 6 ? 5 : 3) * NI_W_MIN>(); break;
-      default: wait_vmcnt<(NST > 7 ? 6 : 3) * NI_W_MIN>(); break;
-    }
-  }
-
-  // The whole loop for one workgroup of NW waves: a ring of NST slots,
-  // stage s computes while s+1..s+NST-1 are in flight; slot s-1 is refilled
-  // (with s+NST-1) once every wave is past the barrier of stage s, which it
-  // reaches only after its MFMAs of s-1 consumed their reads.
   __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
                                       int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
                                       int k_begin, int k_end) {
-    const int n = setup(lds, A, lda, a_rows, B, ldb, b_rows, k_begin, k_end, wave_id());
-    if (n <= 0) return;
-    prologue();
-    for (int s = 0; s < n; ++s) {
-      wait_for(s);
-      barrier_only();
-      compute(s, s + NST - 1 < n ? s + NST - 1 : -1);
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int wm = wave % WM, wn = wave / WM;
+    const int npairs = (k_end - k_begin) / 64;
+    if (npairs <= 0) return;
+    const uint32_t lds0 = lds_addr(lds);
+    const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
+    const int br = b_rows < 0 ? 0 : (b_rows > BN ? BN : b_rows);
+    const i32x4 rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
+    const i32x4 rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
+    // DMA: block j holds rows 8 j .. 8 j + 7 of the slot (A rows, then B rows);
+    // lane -> row 8 j + lane / 8, physical piece lane % 8, which holds the
+    // logical piece (lane % 8) ^ swz(row). Block wave + NW ii is row 8 wave +
+    // lane / 8 plus 32 ii rows (same row % 16): the 32 ii rows go in the
+    // scalar offset, so two vector offsets serve all blocks.
+    const int row0 = 8 * wave + (lane >> 3);
+    const int piece = (lane & 7) ^ swz(row0 & 15);
+    const int voffA = (int)(row0 * lda * 2) + 16 * piece;
+    const int voffB = (int)(row0 * ldb * 2) + 16 * piece;
+    constexpr int NB_A = NI_A / NW;
+    auto issue_block = [&](int ii, uint32_t dst, int koff) {
+      if (ii < NB_A)
+        dma16(rsA, dst + 1024u * NW * ii, voffA, koff + (int)(ii * 64 * lda));
+      else
+        dma16(rsB, dst + 1024u * NW * ii, voffB, koff + (int)((ii - NB_A) * 64 * ldb));
+    };
+    auto slot_dst = [&](int p) {
+      return lds0 + (uint32_t)((p & 1) * SLOT_BYTES) + 1024u * (uint32_t)wave;
+    };
+    // fragment offsets of this lane in a slot for half h (k-step 2 p + h):
+    // row l % 16 of the block, logical piece 4 h + l / 16
+    const int fr = lane & 15;
+    const uint32_t foff0 = fr * ROWB + 16 * ((lane >> 4) ^ swz(fr));
+    const uint32_t foff1 = fr * ROWB + 16 * ((4 + (lane >> 4)) ^ swz(fr));
+
+#pragma unroll
+    for (int ii = 0; ii < NB; ++ii) issue_block(ii, slot_dst(0), k_begin * 2);
+    for (int p = 0; p < npairs; ++p) {
+      wait_vmcnt<0>();  // this wave's part of pair p has landed
+      barrier_only();   // everyone's has; the other slot (pair p - 1) is free
+      const bool refill = p + 1 < npairs;
+      const uint32_t dst = slot_dst(p + 1);
+      const int koff = (k_begin + 64 * (p + 1)) * 2;
+      const unsigned char* st = lds + (p & 1) * SLOT_BYTES;
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        constexpr int A0 = MI < 2 ? MI : 2;
+        const uint32_t fo = h ? foff1 : foff0;
+        bf16x8 af[MI], bfr[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          bfr[j] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn * WTN + 16 * j) * ROWB + fo));
+#pragma unroll
+        for (int i = 0; i < A0; ++i)
+          af[i] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB + fo));
+        __builtin_amdgcn_sched_group_barrier(0x100, NJ + A0, 0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          if (i + A0 < MI)
+            af[i + A0] = __builtin_bit_cast(
+                bf16x8,
+                *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * (i + A0)) * ROWB + fo));
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          if (i + A0 < MI) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
+          }
+          // the next pair's DMA blocks go out during the first k-step's MFMAs
+          if (h == 0 && refill) {
+#pragma unroll
+            for (int ii = (i * NB) / MI; ii < ((i + 1) * NB) / MI; ++ii) issue_block(ii, dst, koff);
+          }
+        }
+      }
     }
-    // all DMA done and every wave past its last fragment read: LDS is free
     wait_vmcnt<0>();
     __syncthreads();
   }
@@ -427,7 +364,7 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 // C[BM x BN] += A[BM x K] * B[K x BN] with A K-contiguous (element (r, k) at
 // A[r * lda + k]) and B K-major (element (k, n) at B[k * ldb + n]): the
 // contraction over the vocabulary, where B is W in its natural layout.
-// A is staged as in AsyncGemm (same accumulator layout). A B stage is 32 rows k of BN columns copied
+// A is staged in 64-byte rows, pieces permuted by row_swz (accumulator layout as AsyncGemmP). A B stage is 32 rows k of BN columns copied
 // verbatim by LDS-DMA, the 16-byte pieces of row k permuted by XOR with
 // 2 (k % 4) + 8 ((k / 8) % 2), which spreads the transposing reads below
 // over all banks. The MFMA B fragment (lane l: column l % 16, k = 8 (l / 16)
@@ -575,7 +512,7 @@ struct AsyncGemmKN {
       return make_rsrc(B + (int64_t)k0 * ldb, bbytes);
     };
 
-    // same ring as AsyncGemm; A fragments read two row blocks ahead
+    // a ring of NST single-k-step slots; A fragments read two row blocks ahead
     for (int s = 0; s < NST - 1 && s < nsteps; ++s) issue(s);
     for (int s = 0; s < nsteps; ++s) {
       wait_stage(s, last_of(s + NST - 2));
@@ -641,7 +578,7 @@ namespace rlk {
 // ka_valid / kb_valid read as zero, and so do columns at or past na_valid /
 // nb_valid in the last valid row; other columns past them read what follows
 // in memory and only reach outputs the caller discards. WM x WN = 4 waves,
-// same accumulator layout as AsyncGemm (rows = A columns, cols = B columns).
+// same accumulator layout as AsyncGemmP (rows = A columns, cols = B columns).
 template <int BM, int BN, int WM, int WN, int NSTG>
 struct AsyncGemmKK {
   static constexpr int NW = WM * WN;

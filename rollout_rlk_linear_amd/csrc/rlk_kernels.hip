@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int Vs, int Gs, int64_t vocab_start, int G,
     int n_ttiles, float4* __restrict__ part) {
-  using Gm = AsyncGemm<BM, GROUP, WM, WN>;
+  using Gm = AsyncGemmP<BM, GROUP, WM, WN>;
   static_assert(WN == 2 && Gm::WTN == 128 && Gm::NJ == 8, "one 128-column chunk per wave");
   static_assert(BM * 2 * 16 <= Gm::LDS_BYTES, "chunk records fit in the stages");
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
     int V, int chunk_g0, int n_groups, int n_ttiles, const float4* __restrict__ rowc,
     uint16_t* __restrict__ gtv, int64_t ldg) {
-  using Gm = AsyncGemm<BM, GROUP, WM, WN>;
+  using Gm = AsyncGemmP<BM, GROUP, WM, WN>;
   constexpr int LDG_S = GROUP + 8;  // [t][v] staging row (bf16), 528 B
   constexpr int STG = BM * LDG_S * 2;
   constexpr int LDSB = Gm::LDS_BYTES > STG ? Gm::LDS_BYTES : STG;

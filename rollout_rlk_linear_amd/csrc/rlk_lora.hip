@@ -2,7 +2,7 @@
 // and its gradients dx, dA, dB (W frozen), declared in include/rlk_lora.h.
 //
 // The base products are the library's LDS-DMA MFMA mainloops: x W^T is a
-// K-contiguous x K-contiguous product (AsyncGemm, as the logits), dy W is a
+// K-contiguous x K-contiguous product (AsyncGemmP, as the logits), dy W is a
 // K-contiguous x K-major product (AsyncGemmKN, as dH). The rank-r adapter
 // enters in the epilogue of each tile in fp32. Every output element of y and
 // dx is computed by the same instruction sequence whatever T, the tile shape
@@ -20,7 +20,7 @@ namespace {
 constexpr int kLoraBM = 64;    // rows (tokens) per tile
 constexpr int kLoraBN = 128;   // output columns per tile
 constexpr int kLoraMaxRank = 64;
-using LoraFwdGemm = AsyncGemm<kLoraBM, kLoraBN, 2, 2, 4>;
+using LoraFwdGemm = AsyncGemmP<kLoraBM, kLoraBN, 2, 2>;
 using LoraDxGemm = AsyncGemmKN<kLoraBM, kLoraBN, 2, 2, 4>;
 static_assert((kLoraBM + kLoraBN) * kLoraMaxRank * 4 <= LoraFwdGemm::LDS_BYTES &&
                   (kLoraBM + kLoraBN) * kLoraMaxRank * 4 <= LoraDxGemm::LDS_BYTES,
