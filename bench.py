@@ -15,7 +15,8 @@ peak (published, and measured on the box by the library's microbenchmark);
 the roofline of the dominant kernel (per-launch duration from HIP events the
 library records on the launch stream); the other workloads (tiny, small-T
 forward against the HBM roofline with a bitwise check, the 5208-token step,
-one 37984-row vocabulary slice); and the float64 CPU oracle timed on the same
+one 37984-row vocabulary slice); the same GEMM shapes through torch.matmul
+(hipBLASLt) as a yardstick; and the float64 CPU oracle timed on the same
 batch.
 
     python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-cpu-baseline] [--quick]
@@ -158,6 +159,41 @@ def microbench(torch, rlk):
             "read_bytes": n,
             "mfma_bf16_TFLOPs": round(mf, 1),
             "mfma_workgroups": wg, "mfma_iters": iters}
+
+
+def library_yardstick(torch, hidden, weight, kernels):
+    """The same three GEMM shapes through torch.matmul (hipBLASLt on ROCm), as
+    context for the per-kernel rates: the logits GEMM h W^T (bf16 logits
+    written out, no softmax), dH = G W and dW = G^T h (bf16 out, and fp32 out
+    where torch offers it), with G a random bf16 [T, V]. Only a yardstick:
+    the library never calls it."""
+    dev = hidden.device
+    T, H = hidden.shape
+    V = weight.shape[0]
+    g = torch.Generator(device="cpu").manual_seed(11)
+    G = torch.randn(T, V, generator=g).to(torch.bfloat16).to(dev)
+    GT = G.t().contiguous()
+    fl = 2.0 * T * H * V
+    out = {"flops_per_gemm": fl, "T": T, "H": H, "V": V}
+    cases = [("logits_hWt_bf16", lambda: torch.matmul(hidden, weight.t()), "fwd_tile"),
+             ("dH_GW_bf16", lambda: torch.matmul(G, weight), "bwd_dh"),
+             ("dW_GtH_bf16", lambda: torch.matmul(GT, hidden), "bwd_dw"),
+             ("dW_GtH_fp32", lambda: torch.mm(GT, hidden, out_dtype=torch.float32), "bwd_dw")]
+    for name, fn, ours in cases:
+        try:
+            per, _ = timed(torch, fn, 2, 5)
+        except Exception as e:  # an op this torch build lacks is reported, not fatal
+            out[name] = {"error": f"{type(e).__name__}: {str(e)[:120]}"}
+            continue
+        ms = sorted(per)[len(per) // 2]
+        ent = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+        if ours in kernels:
+            ent["library_kernel"] = ours
+            ent["library_kernel_ms"] = round(kernels[ours]["avg_launch_ms"], 4)
+        out[name] = ent
+    del G, GT
+    torch.cuda.empty_cache()
+    return out
 
 
 def to_dev(torch, c):
@@ -485,6 +521,7 @@ def main():
     del fo, bo
     if not args.quick:
         result["device"] = device_info(torch)
+        result["hipblaslt_yardstick"] = library_yardstick(torch, hidden, weight, kernels)
         mb = microbench(torch, rlk)
         result["microbench"] = mb
         result["frac_measured_mfma"] = round(tflops / mb["mfma_bf16_TFLOPs"], 4)
