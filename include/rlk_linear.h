@@ -142,8 +142,8 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
  * units numbered pu = p * ceil(Vs/128) + iu, each 128 * H bf16 at offset
  * pu * 128 * H. Inside a unit, k-step s (elements 32 s .. 32 s + 31 of each
  * row) is 4096 bf16 at offset 4096 s; inside a step, 16-byte piece i of
- * 1 KB block b holds row 16 b + i / 4 and 8-element piece
- * (i % 4) XOR (((r >> 1) XOR (r >> 3)) & 3) with r = i / 4. Rows past the
+ * 1 KB block b holds row 16 b + r, r = i / 4, and its 8-element piece
+ * ((i % 4) - r / 2) mod 4 (integer r / 2). Rows past the
  * slice are zero. The layout is tied to (H, V, vocab_start, vocab_total):
  * pack and use with the same four values. */
 RLK_API size_t rlk_linear_pack_weight_bytes(int64_t H, int64_t V, int64_t vocab_start,

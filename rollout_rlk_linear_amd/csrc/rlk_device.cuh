@@ -158,8 +158,8 @@ __device__ __forceinline__ void acc_row_block(const f32x4 (&acc)[MI][NJ], int i,
 // lds` stores lane i's 16 bytes at (LDS base + 16 i), so one instruction
 // fills 1 KB. Operand rows are staged as 64-byte rows (32 bf16 = one MFMA
 // k-step) in a ring of stages; the 16-byte pieces of each row are stored
-// XOR-permuted (row_swz below), which keeps the 16-row fragment reads free
-// of bank conflicts. Rows past the valid range read as
+// rotated by the row index (row_slot below), which keeps the 16-row fragment
+// reads free of bank conflicts. Rows past the valid range read as
 // zero through the buffer's hardware range check (num_records), the k offset
 // of a stage travels in the scalar offset, so the steady-state loop issues
 // no vector ALU work for addressing and holds no staging registers.
@@ -183,11 +183,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
 }
 
-// Piece permutation of a staged 64-byte row: row r (within its 16-row block)
-// keeps logical 16-byte piece c at slot c ^ row_swz(r). A fragment read
-// (lane l: row l % 16, piece l / 16) then touches distinct banks whether the
-// LDS serves 16 lanes over 64 banks or 8 lanes over 32 banks per cycle.
-__device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Piece placement of a staged 64-byte row: row r (within its 16-row block)
+// keeps logical 16-byte piece c at slot (c + r / 2) mod 4, and slot s holds
+// piece (s - r / 2) mod 4. A 16-byte fragment read (lane l: row l % 16,
+// piece l / 16) is then free of bank conflicts on gfx950 (measured with the
+// LDS bank-conflict counter: 0 cycles per ds_read_b128, where XOR placements
+// such as c ^ ((r / 2) ^ (r / 8)) cost 4 and a linear row layout 12).
+__device__ __forceinline__ int row_slot(int c, int r) { return (c + (r >> 1)) & 3; }
+__device__ __forceinline__ int row_piece(int s, int r) { return (s - (r >> 1)) & 3; }
 
 // One 1 KB LDS-DMA block: lane i's 16 bytes from (base + voff + soff) land at
 // LDS (addr + 16 i). Written as inline asm so that the compiler does not
@@ -238,8 +241,8 @@ __device__ __forceinline__ void barrier_only() {
 // number of requests in flight per CU is what bounds the copy rate). Two
 // slots: the pair after the one being multiplied is in flight, its DMA
 // blocks issued between the first k-step's MFMAs. The 16-byte pieces of row
-// r are XOR-permuted by (r ^ (r >> 3)) & 7, which keeps the 16-row fragment
-// reads free of bank conflicts. Within a k-step all B fragments and two A
+// r are rotated by r (slot = (piece + r) mod 8), which keeps the 16-row
+// fragment reads of both k-steps free of bank conflicts. Within a k-step all B fragments and two A
 // fragments are read first, then A fragment i+2 is read while the MFMAs of
 // row block i run (scheduling group barriers pin the order).
 template <int BM, int BN, int WM, int WN>
@@ -256,7 +259,10 @@ struct AsyncGemmP {
   static constexpr int NI = NI_A + NI_B;
   static_assert(NI_A % NW == 0 && NI % NW == 0, "DMA blocks divide among the waves");
   static constexpr int NB = NI / NW;  // blocks per wave per pair
-  static __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+  // 128-byte staged rows: logical piece c of row r sits at slot (c + r) mod 8
+  // (conflict-free 16-byte fragment reads for both k-steps of the pair)
+  static __device__ __forceinline__ int slot(int c, int r) { return (c + r) & 7; }
+  static __device__ __forceinline__ int piece_at(int s, int r) { return (s - r) & 7; }
 
   f32x4 acc[MI][NJ];
 
@@ -282,11 +288,11 @@ struct AsyncGemmP {
     const i32x4 rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
     // DMA: block j holds rows 8 j .. 8 j + 7 of the slot (A rows, then B rows);
     // lane -> row 8 j + lane / 8, physical piece lane % 8, which holds the
-    // logical piece (lane % 8) ^ swz(row). Block wave + NW ii is row 8 wave +
+    // logical piece piece_at(lane % 8, row). Block wave + NW ii is row 8 wave +
     // lane / 8 plus 32 ii rows (same row % 16): the 32 ii rows go in the
     // scalar offset, so two vector offsets serve all blocks.
     const int row0 = 8 * wave + (lane >> 3);
-    const int piece = (lane & 7) ^ swz(row0 & 15);
+    const int piece = piece_at(lane & 7, row0 & 15);
     const int voffA = (int)(row0 * lda * 2) + 16 * piece;
     const int voffB = (int)(row0 * ldb * 2) + 16 * piece;
     constexpr int NB_A = NI_A / NW;
@@ -302,8 +308,8 @@ struct AsyncGemmP {
     // fragment offsets of this lane in a slot for half h (k-step 2 p + h):
     // row l % 16 of the block, logical piece 4 h + l / 16
     const int fr = lane & 15;
-    const uint32_t foff0 = fr * ROWB + 16 * ((lane >> 4) ^ swz(fr));
-    const uint32_t foff1 = fr * ROWB + 16 * ((4 + (lane >> 4)) ^ swz(fr));
+    const uint32_t foff0 = fr * ROWB + 16 * slot(lane >> 4, fr);
+    const uint32_t foff1 = fr * ROWB + 16 * slot(4 + (lane >> 4), fr);
 
 #pragma unroll
     for (int ii = 0; ii < NB; ++ii) issue_block(ii, slot_dst(0), k_begin * 2);
@@ -364,7 +370,8 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 // C[BM x BN] += A[BM x K] * B[K x BN] with A K-contiguous (element (r, k) at
 // A[r * lda + k]) and B K-major (element (k, n) at B[k * ldb + n]): the
 // contraction over the vocabulary, where B is W in its natural layout.
-// A is staged in 64-byte rows, pieces permuted by row_swz (accumulator layout as AsyncGemmP). A B stage is 32 rows k of BN columns copied
+// A is staged in 64-byte rows, pieces placed by row_slot (accumulator layout
+// as AsyncGemmP). A B stage is 32 rows k of BN columns copied
 // verbatim by LDS-DMA, the 16-byte pieces of row k permuted by XOR with
 // 2 (k % 4) + 8 ((k / 8) % 2), which spreads the transposing reads below
 // over all banks. The MFMA B fragment (lane l: column l % 16, k = 8 (l / 16)
@@ -424,7 +431,7 @@ struct AsyncGemmKN {
     const uint32_t lds0 = lds_addr(lds);
 
     const int drow = lane >> 2;
-    const int dpiece = (lane & 3) ^ row_swz(lane >> 2);
+    const int dpiece = row_piece(lane & 3, lane >> 2);
     const int brow = lane / PPR, bslot = lane % PPR;
     int voff[NI_W_MAX];
 #pragma unroll
@@ -469,7 +476,7 @@ struct AsyncGemmKN {
       }
     };
 
-    const int foff = (lane & 15) * ROWB_A + 16 * ((lane >> 4) ^ row_swz(lane & 15));
+    const int foff = (lane & 15) * ROWB_A + 16 * row_slot(lane >> 4, lane & 15);
     // transposing reads: 16-lane group g, source lane sl; read q covers rows
     // 8 g + 4 q + sl / 4 at columns n0 + 4 (sl % 4) .. + 3
     const int g = lane >> 4, sl = lane & 15;

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
 
   const uint32_t lds0 = lds_addr(lds);
   const int drow = lane >> 2;
-  const int dpiece = (lane & 3) ^ row_swz(drow);
+  const int dpiece = row_piece(lane & 3, drow);
   const i32x4 rsA = make_rsrc(hidden, (uint32_t)((T < 16 * MI ? T : 16 * MI) * H * 2));
   const bool loads_a = wave < MI;  // waves 0 .. MI-1 move one 16-row block of hidden each
   const int voffA = (16 * wave + drow) * H * 2 + 16 * dpiece;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
   if (Q > 0) set_unit(0);
   for (int q = 0; q < NST - 1 && q < Q; ++q) issue(q);
 
-  const int foff = (lane & 15) * 64 + 16 * ((lane >> 4) ^ row_swz(lane & 15));
+  const int foff = (lane & 15) * 64 + 16 * row_slot(lane >> 4, lane & 15);
   f32x4 acc[MI][2];
 #pragma unroll
   for (int i = 0; i < MI; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
 // slice rows 128 iu .. + 127) is 128 H elements at pu 128 H; its stage s
 // (k = 32 s .. + 31) is 8 KB at s 4096 inside it, laid out exactly as a B
 // slot of the ring: 16-byte piece i of 1 KB block jb holds row 16 jb + i / 4,
-// k piece (i % 4) ^ row_swz(i / 4). Rows past the slice are zero.
+// k piece row_piece(i % 4, i / 4). Rows past the slice are zero.
 // One thread moves one 16-byte piece: eight consecutive threads read one
 // whole 128-byte line of a W row (two stages' worth of that row), a wave
 // reads eight rows' lines, and its writes fill two 512-byte runs of slots.
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void pack_weight_kernel(
     if (srow < Vs)
       v = *reinterpret_cast<const u32x4*>(weight + ((int64_t)p * Vs + srow) * H + 64 * s2 + 8 * e);
     uint16_t* dst = packed + pu * 128 * H + (int64_t)(2 * s2 + (e >> 2)) * 4096 + 32 * r +
-                    8 * ((e & 3) ^ row_swz(r & 15));
+                    8 * row_slot(e & 3, r & 15);
     *reinterpret_cast<u32x4*>(dst) = v;
   }
 }

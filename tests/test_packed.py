@@ -39,7 +39,7 @@ def pack_reference(W: np.ndarray, vs0: int, vt: int) -> np.ndarray:
     Us = -(-Vs // 128)
     i = np.arange(64)
     r = i // 4
-    piece = (i % 4) ^ (((r >> 1) ^ (r >> 3)) & 3)
+    piece = ((i % 4) - (r // 2)) % 4   # slot i % 4 of row r holds this 16-byte piece
     rows = 16 * np.arange(8)[:, None] + r[None, :]          # [block, lane]
     out = np.zeros((P * Us, H // 32, 8, 64, 8), dtype=np.uint16)
     for p in range(P):
