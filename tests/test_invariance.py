@@ -143,3 +143,29 @@ def test_dweight_repeat_deterministic(setup):
     dh2, dw2 = rlk.bwd(h, W, y, st, dl, None)
     torch.cuda.synchronize()
     assert bits_equal(dw1, dw2) and bits_equal(dh1, dh2)
+
+
+@pytest.mark.parametrize("T,H,V", [(65, 64, 1001), (130, 64, 1001), (300, 192, 4000),
+                                   (257, 4096, 151936)])
+def test_tile_forward_repeats_bitwise(T, H, V):
+    """Repeated calls of the large-batch forward give the same bits every time,
+    and the same bits as the streaming path over the packed weight, at shapes
+    where the mainloop has one or three k-step pairs (H = 64, 192) and the
+    last vocabulary group is partial (V = 1001, 4000), and at the full LM-head
+    width; streaming calls between the repeats vary the timing."""
+    c = wl.make_case(f"rep{V}", T, H, V, 31 + T, rms=False)
+    h, W, y = dev(c.hidden), dev(c.weight), dev(c.targets)
+    pw = rlk.pack_weight(W)
+    first = rlk.fwd(h, W, y)["stats"].clone()
+    streamed = rlk.fwd_packed(h, pw, y)["stats"]
+    torch.cuda.synchronize()
+    assert bits_equal(first, streamed), f"T={T} H={H} V={V}: tile and stream records differ"
+    reps = 40 if H < 4096 else 8
+    out = {}
+    for k in range(reps):
+        got = rlk.fwd(h, W, y, out=out)["stats"]
+        if k % 2:
+            rlk.fwd_packed(h, pw, y)
+        torch.cuda.synchronize()
+        bad = int((got.view(torch.int32) != first.view(torch.int32)).any(dim=1).sum())
+        assert bad == 0, f"T={T} H={H} V={V}: repeat {k} differs in {bad} rows"
