@@ -381,10 +381,10 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="only the T=512 step (no microbenchmarks, other workloads or clocks)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
-    ap.add_argument("--profile-case", choices=["fwd_t1", "fwd_packed_t1", "fwd_packed_t64", "read"],
+    ap.add_argument("--profile-case", choices=["fwd_t1", "fwd_t64", "fwd_packed_t1", "fwd_packed_t64", "read"],
                     default=None,
-                    help="run only this case's calls (warmup + steps), for profilers: fwd_t1 = "
-                         "the T=1 forward over the full vocabulary (natural layout), "
+                    help="run only this case's calls (warmup + steps), for profilers: fwd_t1 / _t64 = "
+                         "the forward of 1 / 64 rows over the full vocabulary (natural layout), "
                          "fwd_packed_t1 / _t64 = the same over the packed weight with 1 / 64 rows, "
                          "read = the 1 GiB streaming-read microbenchmark")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -430,7 +430,7 @@ def main():
         nrow = 64 if args.profile_case.endswith("t64") else 1
         h1, y1 = pool["hidden"][:nrow].to("cuda:0"), pool["targets"][:nrow].to("cuda:0")
         fo1 = {}
-        if args.profile_case == "fwd_t1":
+        if args.profile_case in ("fwd_t1", "fwd_t64"):
             fn = lambda: rlk.fwd(h1, w, y1, out=fo1)  # noqa: E731
         else:
             pw = rlk.pack_weight(w)

@@ -178,42 +178,52 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
 // record comes from the same chunk tree; the combine merges a group's two
 // halves as fwd_tile does, so the bits match the large-batch path.
 //
-// W is read either in its natural [V, H] layout (a stage holds 64 bytes of
-// each of the unit's 128 rows) or packed by pack_weight_kernel (a stage is
-// 8 KB contiguous, already in the slot's LDS order), which streams from HBM
-// at a markedly higher rate than 128 strided 64-byte pieces.
+// W is read either in its natural [V, H] layout (a stage holds 128 bytes of
+// each of the unit's 128 rows when H is a multiple of 128, else 64) or packed
+// by pack_weight_kernel (a stage is 8 KB contiguous, already in the slot's
+// LDS order), which streams from HBM at a higher rate than 128 strided
+// 64-byte pieces.
 constexpr int kStreamRows = 64;  // rows of hidden per launch
-// Per row count (MI 16-row blocks): a stage holds 16 MI rows of hidden and the
-// unit's 128 W rows, 64 bytes each; the logit buffer holds 128 columns of
-// 16 MI rows at a stride of ZS floats (ZS = 4 mod 64 keeps the epilogue's
-// reads and writes free of bank conflicts); the ring takes what remains.
-template <int MI>
+// Per row count (MI 16-row blocks) and k-steps per stage (KS): a stage holds
+// 16 MI rows of hidden and the unit's 128 W rows, 64 KS bytes each; the
+// logit buffer holds 128 columns of 16 MI rows at a stride of ZS floats
+// (ZS = 4 mod 64 keeps the epilogue's reads and writes free of bank
+// conflicts); the ring takes what remains.
+template <int MI, int KS>
 struct StreamCfg {
-  static constexpr int STAGE = (16 * MI + 128) * 64;
+  static constexpr int STAGE = (16 * MI + 128) * 64 * KS;
   static constexpr int ZS = 16 * MI + 4;
   static constexpr int ZBYTES = 128 * ZS * 4;
   static constexpr int NST = (160 * 1024 - ZBYTES) / STAGE;
 };
 
-template <int MI, bool PACKED>
+// KS = 2 (H a multiple of 128): a stage is a pair of k-steps. Hidden, and W in
+// its natural layout, are staged as 128 bytes of each row, so every DMA
+// request carries a whole line, the pieces of staged row r at slot
+// (piece + r) mod 8 as in the tile forward; packed W is two consecutive
+// packed stages, 16 KB contiguous, each in its single-step LDS order.
+template <int MI, bool PACKED, int KS>
 __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int Vs, int Us, int P, int Gs,
     int64_t vocab_start, int n_wg, int ldp, float4* __restrict__ part) {
   static_assert(MI == 1 || MI == 2 || MI == 4, "16, 32 or 64 rows");
-  using C = StreamCfg<MI>;
+  static_assert(KS == 1 || KS == 2, "one k-step or a pair a stage");
+  using C = StreamCfg<MI, KS>;
   constexpr int NST = C::NST, STAGE = C::STAGE, ZS = C::ZS;
-  constexpr int A_BYTES = 16 * MI * 64;
+  constexpr int ROWB = 64 * KS;  // bytes of a staged row
+  constexpr int A_BYTES = 16 * MI * ROWB;
+  constexpr int NA2 = 2 * MI;  // KS = 2: 1 KB blocks (8 rows) of hidden per stage
   static_assert(NST >= 3 && NST * STAGE + C::ZBYTES <= 160 * 1024, "ring and logits fit the LDS");
-  static_assert(3 * (NST - 2) < 64, "vmcnt range");
+  static_assert((KS == 1 ? 3 : 6) * (NST - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) unsigned char lds[NST * STAGE];
   __shared__ __attribute__((aligned(16))) float zbuf[128 * ZS];  // [column][row]
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int n_units = P * Us;
   const int my_units = (int)blockIdx.x < n_units ? (n_units - 1 - (int)blockIdx.x) / n_wg + 1 : 0;
-  const int nsteps = H / 32;
-  const int Q = my_units * nsteps;  // stages of this workgroup, all units in a row
+  const int nsteps = H / (32 * KS);  // stages of a unit
+  const int Q = my_units * nsteps;   // stages of this workgroup, all units in a row
 
   // targets of this lane's epilogue rows 16 i + 4 wave + lane / 16
   int yv[MI];
@@ -234,7 +244,19 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
   const int voffB0 = PACKED ? 1024 * wave + 16 * lane : (16 * wave + drow) * H * 2 + 16 * dpiece;
   const int voffB1 = PACKED ? 1024 * (wave + 4) + 16 * lane
                             : (16 * (wave + 4) + drow) * H * 2 + 16 * dpiece;
-  const int sB = PACKED ? 8192 : 64;  // bytes between consecutive stages of a unit's B
+  const int sB = PACKED ? 8192 : ROWB;  // bytes between consecutive stages of a unit's B
+  // KS = 2: 8-row blocks, lane -> row 8 (wave + 4 k) + lane / 8 (k = 0, 1, ... in
+  // the block's vector offset, so the range check covers every row), physical
+  // piece lane % 8 holding logical piece (lane % 8 - row) mod 8
+  const int prow = 8 * wave + (lane >> 3);
+  const int ppiece = ((lane & 7) - prow) & 7;
+  const int nA2w = wave < NA2 ? (NA2 - wave + 3) / 4 : 0;  // hidden blocks of this wave
+  int voffA2[2], voffB2[4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) voffA2[k] = (prow + 32 * k) * H * 2 + 16 * ppiece;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    voffB2[k] = PACKED ? 1024 * (wave + 4 * k) + 16 * lane : (prow + 32 * k) * H * 2 + 16 * ppiece;
 
   // issue state: the next stage to issue is stage iss_s of this workgroup's unit iss_u
   int iss_u = 0, iss_s = 0;
@@ -250,9 +272,19 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
   };
   auto issue = [&](int slot) {
     const uint32_t st = lds0 + (uint32_t)(slot * STAGE);
-    if (loads_a) dma16(rsA, st + 1024u * wave, voffA, 64 * iss_s);
-    dma16(rsB, st + A_BYTES + 1024u * wave, voffB0, sB * iss_s);
-    dma16(rsB, st + A_BYTES + 1024u * (wave + 4), voffB1, sB * iss_s);
+    if constexpr (KS == 1) {
+      if (loads_a) dma16(rsA, st + 1024u * wave, voffA, 64 * iss_s);
+      dma16(rsB, st + A_BYTES + 1024u * wave, voffB0, sB * iss_s);
+      dma16(rsB, st + A_BYTES + 1024u * (wave + 4), voffB1, sB * iss_s);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (k < nA2w) dma16(rsA, st + 1024u * (wave + 4 * k), voffA2[k], ROWB * iss_s);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        dma16(rsB, st + A_BYTES + 1024u * (wave + 4 * k), voffB2[k],
+              (PACKED ? 16384 : ROWB) * iss_s);
+    }
     if (++iss_s == nsteps) {
       iss_s = 0;
       if (++iss_u < my_units) set_unit(iss_u);
@@ -262,35 +294,52 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(
   if (Q > 0) set_unit(0);
   for (int q = 0; q < NST - 1 && q < Q; ++q) issue(q);
 
-  const int foff = (lane & 15) * 64 + 16 * row_slot(lane >> 4, lane & 15);
+  // fragment offsets of this lane (row lane % 16 of a 16-row block) in 64-byte
+  // rows (single steps, packed W) and, for k-step h, in 128-byte rows
+  const int foff1 = (lane & 15) * 64 + 16 * row_slot(lane >> 4, lane & 15);
+  auto foff2 = [&](int h) {
+    return (lane & 15) * 128 + 16 * ((4 * h + (lane >> 4) + (lane & 15)) & 7);
+  };
   f32x4 acc[MI][2];
 #pragma unroll
   for (int i = 0; i < MI; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   int unit = 0, s = 0;
   for (int q = 0; q < Q; ++q) {
     // this wave's DMA of stage q has landed once at most NST - 2 later stages are
-    // pending (3 blocks a stage for the waves that move hidden, else 2)
+    // pending (per stage: 2 W blocks, and 1 of hidden for waves < MI; with k-step
+    // pairs 4 W blocks, and nA2w of hidden)
     if (q + NST - 2 >= Q)
       wait_vmcnt<0>();
-    else if (loads_a)
-      wait_vmcnt<3 * (NST - 2)>();
+    else if (KS == 1 ? loads_a : nA2w == 1)
+      wait_vmcnt<(KS == 1 ? 3 : 5) * (NST - 2)>();
+    else if (KS == 1 || nA2w == 0)
+      wait_vmcnt<(KS == 1 ? 2 : 4) * (NST - 2)>();
     else
-      wait_vmcnt<2 * (NST - 2)>();
+      wait_vmcnt<(KS == 1 ? 2 : 6) * (NST - 2)>();
     barrier_only();  // every wave's part of stage q is in; slot (q - 1) % NST is free
     if (q + NST - 1 < Q) issue((q + NST - 1) % NST);
     const unsigned char* st = lds + (q % NST) * STAGE;
-    const bf16x8 b0 = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(st + A_BYTES + 32 * wave * 64 + foff));
-    const bf16x8 b1 = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(st + A_BYTES + (32 * wave + 16) * 64 + foff));
-    bf16x8 af[MI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + 16 * i * 64 + foff));
+    for (int h = 0; h < KS; ++h) {
+      const int fa = KS == 1 ? foff1 : foff2(h);  // hidden
+      // W: 16-row block 2 wave + jj of the unit at byte wb + jj wbs
+      const int wb = KS == 1   ? A_BYTES + 32 * wave * 64 + foff1
+                     : PACKED ? A_BYTES + 8192 * h + 32 * wave * 64 + foff1
+                              : A_BYTES + 32 * wave * 128 + foff2(h);
+      const int wbs = KS == 2 && !PACKED ? 16 * 128 : 16 * 64;
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + wb));
+      const bf16x8 b1 =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + wb + wbs));
+      bf16x8 af[MI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[i][1], 0, 0, 0);
+      for (int i = 0; i < MI; ++i)
+        af[i] =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + 16 * i * ROWB + fa));
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[i][1], 0, 0, 0);
+      }
     }
     if (++s < nsteps) continue;
 
@@ -816,17 +865,25 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
       const uint16_t* h = a.hidden + (int64_t)r0 * a.H;
       const int32_t* y = a.targets + r0;
       float4* pr = a.part + (int64_t)r0 * 2 * G;
-#define RLK_STREAM(MI, PK)                                                                     \
-  RLK_LAUNCH(K_FWD_STREAM, (fwd_stream_kernel<MI, PK>), grid, st, h, a.weight, y,              \
+#define RLK_STREAM(MI, PK, KS)                                                                 \
+  RLK_LAUNCH(K_FWD_STREAM, (fwd_stream_kernel<MI, PK, KS>), grid, st, h, a.weight, y,          \
              rows, a.H, sl.Vs, Us, sl.P, sl.Gs, a.vocab_start, grid, 2 * G, pr)
-      if (a.packed) {
-        if (rows <= 16) RLK_STREAM(1, true);
-        else if (rows <= 32) RLK_STREAM(2, true);
-        else RLK_STREAM(4, true);
+      if (a.packed && a.H % 128 == 0) {  // k-step pairs: at least two stages a unit
+        if (rows <= 16) RLK_STREAM(1, true, 2);
+        else if (rows <= 32) RLK_STREAM(2, true, 2);
+        else RLK_STREAM(4, true, 2);
+      } else if (a.packed) {
+        if (rows <= 16) RLK_STREAM(1, true, 1);
+        else if (rows <= 32) RLK_STREAM(2, true, 1);
+        else RLK_STREAM(4, true, 1);
+      } else if (a.H % 128 == 0) {  // k-step pairs: at least two stages a unit
+        if (rows <= 16) RLK_STREAM(1, false, 2);
+        else if (rows <= 32) RLK_STREAM(2, false, 2);
+        else RLK_STREAM(4, false, 2);
       } else {
-        if (rows <= 16) RLK_STREAM(1, false);
-        else if (rows <= 32) RLK_STREAM(2, false);
-        else RLK_STREAM(4, false);
+        if (rows <= 16) RLK_STREAM(1, false, 1);
+        else if (rows <= 32) RLK_STREAM(2, false, 1);
+        else RLK_STREAM(4, false, 1);
       }
 #undef RLK_STREAM
     }
