@@ -6,9 +6,9 @@ the rollout engine's CUDA-graph batches of 1 to 4 ("RL-Kernel evidence
 h100-cp-gradient.json", validation.train_rollout_logprob and
 validation.cuda_graph.expected_capture_sizes). Here a fixed pool of 64
 Qwen3-8B-shaped rows (H = 4096, V = 151936) is scored in batches of 1, 2, 3,
-4 and 64, under 3 row permutations, embedded in a batch of 512 other rows,
+4, 24 and 64, under 3 row permutations, embedded in a batch of 512 other rows,
 and repeated, and scored through the packed-weight rollout path in batches
-of 1 to 4 and 64; every row's logp, entropy and statistics record must be
+of 1 to 4, 24 and 64; every row's logp, entropy and statistics record must be
 bit-identical across all of them. The same holds for each row of dhidden.
 """
 
@@ -56,7 +56,7 @@ def test_batch_sizes_bitwise(setup):
     ref, ref_st = score(W, h, y)
     torch.cuda.synchronize()
     assert torch.isfinite(ref).all()
-    for bs in (1, 2, 3, 4, 64):
+    for bs in (1, 2, 3, 4, 24, 64):
         for rep in range(3):
             got, st = batched(W, h, y, bs)
             torch.cuda.synchronize()
@@ -90,14 +90,14 @@ def test_composition_bitwise(setup):
 
 
 def test_rollout_packed_batches_match_training_batch(setup):
-    # the rollout engine's path (packed W, decode batches of 1 to 4 and 64)
+    # the rollout engine's path (packed W, decode batches of 1 to 4, 24 and 64)
     # against the trainer's: the pool's rows inside a 512-row batch
     W, h, y = setup["W"], setup["h"], setup["y"]
     emb = setup["pool"]["embed"]
     pos = emb["positions"].cuda()
     train, train_st = score(W, dev(emb["hidden"]), dev(emb["targets"]))
     pw = rlk.pack_weight(W)
-    for bs in (1, 2, 3, 4, 64):
+    for bs in (1, 2, 3, 4, 24, 64):
         outs, stats = [], []
         for r0 in range(0, 64, bs):
             o = rlk.fwd_packed(h[r0:r0 + bs].contiguous(), pw, y[r0:r0 + bs].contiguous())

@@ -74,7 +74,7 @@ def test_pack_layout(H, V, vs0, vt):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
 
 
-@pytest.mark.parametrize("T", [1, 2, 5, 64, 65, 130])
+@pytest.mark.parametrize("T", [1, 2, 5, 20, 32, 64, 65, 130])
 @pytest.mark.parametrize("H,V", [(128, 4000), (64, 1001), (256, 4 * 2500 + 4)])
 def test_fwd_packed_bitwise(T, H, V):
     c = wl.make_case(f"pk{V}", T, H, V, 22 + T, rms=False)

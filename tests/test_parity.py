@@ -82,7 +82,8 @@ def test_tiny_backward(with_dent, dh_f32):
 # ---------------------------------------------------- ragged / edge shapes
 
 RAGGED = [(1, 64, 1), (1, 64, 2), (2, 64, 31), (3, 128, 33), (64, 64, 257), (65, 192, 1000),
-          (70, 128, 4099), (300, 64, 777), (257, 256, 2304), (33, 320, 5000)]
+          (70, 128, 4099), (300, 64, 777), (257, 256, 2304), (33, 320, 5000),
+          (20, 256, 3001), (27, 192, 2000)]
 
 
 @pytest.mark.parametrize("T,H,V", RAGGED)
