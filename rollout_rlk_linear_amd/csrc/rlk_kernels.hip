@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
 // of one virtual slice: unit iu of slice p holds slice rows 128 iu .. (the
 // half iu % 2 of group iu / 2), i.e. one wave-chunk of fwd_tile's 256-column
 // group. A persistent grid of n_wg workgroups (one per CU) takes units
-// b, b + n_wg, ... and runs them as ONE pipeline of 32-k stages: the ring of
+// b, b + n_wg, ... and runs them as ONE pipeline of stages of 32 KS k: the ring of
 // NST slots keeps NST - 1 stages in flight across unit boundaries, and a
 // unit's epilogue runs while the next unit's first stages land.
 //
