@@ -553,16 +553,20 @@ __global__ __launch_bounds__(kThreads) void bwd_rowprep_kernel(
   rowc[2 * t + 1] = make_float4(de, __int_as_float(yli), s.y / (1.f + s.y), 0.f);
 }
 
-// G for one (T-tile, group) of the chunk, rounded to bf16 into an LDS tile
-// [t][v], then stored as gtv[t][lg*256 + c] (rows t < T, 16-byte row pieces;
-// the columns past V are zeros). Both dH and dW read G from there.
-template <int BM, int WM, int WN>
+// G for one (T-tile, BN-column tile) of the chunk, rounded to bf16 into an
+// LDS tile [t][v], then stored as gtv[t][lg*BN + c] (rows t < T, 16-byte row
+// pieces; the columns past V up to the tile's end are zeros, which covers
+// dH's k-range; dW's last v-tile may also read columns beyond, which feed
+// only dW rows past V, never stored). Both dH and dW read G from there.
+// Each element depends on its logit and its row's constants only, so the
+// column width of the tile does not change a bit.
+template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
     int V, int chunk_g0, int n_groups, int n_ttiles, const float4* __restrict__ rowc,
     uint16_t* __restrict__ gtv, int64_t ldg) {
-  using Gm = AsyncGemmP<BM, GROUP, WM, WN>;
-  constexpr int LDG_S = GROUP + 8;  // [t][v] staging row (bf16), 528 B
+  using Gm = AsyncGemmP<BM, BN, WM, WN>;
+  constexpr int LDG_S = BN + 8;  // [t][v] staging row (bf16), 16 B longer than the tile's
   constexpr int STG = BM * LDG_S * 2;
   constexpr int LDSB = Gm::LDS_BYTES > STG ? Gm::LDS_BYTES : STG;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
@@ -573,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
   if (lg >= n_groups) return;
   const int g = chunk_g0 + lg;
   const int row0 = tt * BM;
-  const int col0 = g * GROUP;
+  const int col0 = g * BN;
   const int tid = threadIdx.x;
 
   Gm gm;
@@ -627,13 +631,15 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     }
   }
   __syncthreads();
-  // gtv rows: 32 threads per row, 16 B each
-  const int c8 = (tid & 31) * 8;
-  for (int rl = tid >> 5; rl < BM; rl += kThreads / 32) {
+  // gtv rows: BN / 8 threads per row, 16 B each
+  constexpr int TPR = BN / 8;
+  static_assert(kThreads % TPR == 0, "whole rows per pass");
+  const int c8 = (tid % TPR) * 8;
+  for (int rl = tid / TPR; rl < BM; rl += kThreads / TPR) {
     const int t = row0 + rl;
     if (t >= T) break;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * LDG_S + c8);
-    *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * GROUP + c8) = v;
+    *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * BN + c8) = v;
   }
 }
 
@@ -823,8 +829,8 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   template __global__ void fwd_tile_kernel<BM, WM, WN>(                                       \
       const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__, \
       int, int, int, int, int64_t, int, int, float4* __restrict__);
-#define RLK_RECOMPUTE(BM, WM, WN)                                                             \
-  template __global__ void bwd_recompute_kernel<BM, WM, WN>(                                  \
+#define RLK_RECOMPUTE(BM, BN, WM, WN)                                                         \
+  template __global__ void bwd_recompute_kernel<BM, BN, WM, WN>(                              \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
       const float4* __restrict__, uint16_t* __restrict__, int64_t);
 #define RLK_DH(BM, BN, WM, WN)                                                             \
@@ -832,8 +838,8 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, int, \
       int, int, int, int, int, int, float* __restrict__);
 RLK_FWD_TILE(256, 2, 2)
-RLK_RECOMPUTE(32, 2, 2)
-RLK_RECOMPUTE(256, 2, 2)
+RLK_RECOMPUTE(32, 128, 2, 2)
+RLK_RECOMPUTE(256, 256, 2, 2)
 RLK_DH(32, 128, 1, 4)
 RLK_DH(256, 256, 2, 2)
 
@@ -933,12 +939,17 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
     const int ngroups = cdiv(width, GROUP);
     const int chunk_g0 = v0 / GROUP;
     const int ng8 = cdiv(ngroups, 8) * 8;
-    if (small)
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, 2, 2>), ng8 * nt, st, a.hidden,
+    if (small) {
+      // 128-column tiles: the W stream of a small batch splits over twice as
+      // many workgroups, so the last round is fuller
+      constexpr int BN = 128;
+      const int ntl = cdiv(width, BN);
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, BN, 2, 2>), cdiv(ntl, 8) * 8 * nt, st,
+                 a.hidden, a.weight, T, H, V, v0 / BN, ntl, nt, a.rowc, a.gtv, p.ldg);
+    } else {
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2>), ng8 * nt, st, a.hidden,
                  a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
-    else
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 2, 2>), ng8 * nt, st, a.hidden,
-                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
+    }
     const int nvt = cdiv(width, 256);
     const int nhw = cdiv(H, kDwBN);
     const int nsp = s1 - s0;
