@@ -17,8 +17,8 @@ import torch
 import rollout_rlk_linear_amd as rlk
 import workloads as wl
 from oracle import backward, decode_bf16, forward, slice_partials
-from tests._util import (GRAD_REL, case_to_device, check_entropy, check_grad, check_logp, dev,
-                         f64)
+from tests._util import (GRAD_REL, bits_equal, case_to_device, check_entropy, check_grad,
+                         check_logp, dev, f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,6 +103,30 @@ def test_ragged_shapes(T, H, V):
         check_grad(f64(dw), rb["dW"], f"dW {T,H,V}")
     else:  # one vocabulary entry: every gradient is exactly zero
         assert float(dh.float().abs().max()) == 0.0 and float(dw.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("T,V", [(20, 1100), (64, 300), (70, 1100)])
+def test_backward_ignores_stale_workspace(T, V):
+    # The logit-gradient buffer in the workspace is written tile by tile; a
+    # 256-row dW v-tile may read columns past V that no tile of a small batch
+    # wrote (V = 1100: columns 1152..1279). Those feed only dW rows past V,
+    # which are never stored. A workspace full of NaN bytes must give the
+    # same bits as a zeroed one.
+    H = 128
+    c = wl.make_case("stale", T, H, V, seed=41 + T, rms=True)
+    d = case_to_device(c)
+    o = run_fwd(d)
+    nws = max(rlk.bwd_workspace_bytes(T, H, V), 256)
+    res = []
+    for fill in (0x00, 0xFF):  # 0xFF bytes: every bf16 and fp32 value a NaN
+        ws = torch.full((nws,), fill, dtype=torch.uint8, device="cuda")
+        dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"],
+                         d["dentropy"], out={"_ws_bwd": ws})
+        torch.cuda.synchronize()
+        res.append((dh.clone(), dw.clone()))
+    assert torch.isfinite(res[1][0].float()).all() and torch.isfinite(res[1][1]).all()
+    assert bits_equal(res[1][0], res[0][0]), f"dH depends on stale workspace bytes (T={T}, V={V})"
+    assert bits_equal(res[1][1], res[0][1]), f"dW depends on stale workspace bytes (T={T}, V={V})"
 
 
 # ------------------------------------------------------- maximum sizes
