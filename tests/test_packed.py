@@ -136,3 +136,30 @@ def test_fwd_packed_reuses_buffers_across_sizes():
     torch.cuda.synchronize()
     for k in ("logp", "entropy", "stats"):
         assert bits_equal(small[k], a[k][:7]), k
+
+
+@pytest.mark.parametrize("T", [1, 20, 70])
+def test_forward_ignores_stale_workspace(T):
+    # every record the combine reads is written by the same call: a workspace
+    # full of NaN bytes gives the same bits as a zeroed one, for the tile and
+    # stream forwards over natural W and for the packed forward
+    H, V = 128, 1100
+    c = wl.make_case("stalef", T, H, V, 43 + T, rms=False)
+    h, W, y = dev(c.hidden), dev(c.weight), dev(c.targets)
+    pw = rlk.pack_weight(W)
+    lib = rlk.load_library()
+    calls = {"_ws_fwd": (lib.rlk_linear_logp_fwd_workspace_bytes(T, H, V),
+                         lambda o: rlk.fwd(h, W, y, out=o)),
+             "_ws_fwdp": (lib.rlk_linear_logp_fwd_packed_workspace_bytes(T, H, V),
+                          lambda o: rlk.fwd_packed(h, pw, y, out=o))}
+    res = {}
+    for fill in (0x00, 0xFF):  # 0xFF bytes: every fp32 value a NaN
+        for key, (nws, call) in calls.items():
+            ws = torch.full((max(nws, 256),), fill, dtype=torch.uint8, device="cuda")
+            o = call({key: ws})
+            torch.cuda.synchronize()
+            res[key, fill] = {k: o[k].clone() for k in ("logp", "entropy", "stats")}
+    for key in calls:
+        for k in ("logp", "entropy", "stats"):
+            assert bits_equal(res[key, 0xFF][k], res[key, 0x00][k]), f"{key} {k} T={T}"
+    assert bits_equal(res["_ws_fwdp", 0x00]["stats"], res["_ws_fwd", 0x00]["stats"])
