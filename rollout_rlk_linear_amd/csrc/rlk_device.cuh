@@ -160,9 +160,10 @@ __device__ __forceinline__ void acc_row_block(const f32x4 (&acc)[MI][NJ], int i,
 // k-step) in a ring of stages; the 16-byte pieces of each row are stored
 // rotated by the row index (row_slot below), which keeps the 16-row fragment
 // reads free of bank conflicts. Rows past the valid range read as
-// zero through the buffer's hardware range check (num_records), the k offset
-// of a stage travels in the scalar offset, so the steady-state loop issues
-// no vector ALU work for addressing and holds no staging registers.
+// zero through the buffer's hardware range check (num_records), which tests
+// the vector offset alone: every row offset therefore sits in the vector
+// offset and only the k offset of a stage, which stays inside a valid row,
+// travels in the scalar offset.
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -289,8 +290,11 @@ struct AsyncGemmP {
     // DMA: block j holds rows 8 j .. 8 j + 7 of the slot (A rows, then B rows);
     // lane -> row 8 j + lane / 8, physical piece lane % 8, which holds the
     // logical piece piece_at(lane % 8, row). Block wave + NW ii is row 8 wave +
-    // lane / 8 plus 32 ii rows (same row % 16): the 32 ii rows go in the
-    // scalar offset, so two vector offsets serve all blocks.
+    // lane / 8 plus 32 ii rows (same row % 16). The buffer range check covers
+    // the vector offset only (the scalar offset is added after it), so the
+    // whole row offset, 32 ii rows included, travels in the vector offset and
+    // only the k offset in the scalar one: a row at or past a_rows / b_rows
+    // then fails the check and is never fetched.
     const int row0 = 8 * wave + (lane >> 3);
     const int piece = piece_at(lane & 7, row0 & 15);
     const int voffA = (int)(row0 * lda * 2) + 16 * piece;
@@ -298,9 +302,9 @@ struct AsyncGemmP {
     constexpr int NB_A = NI_A / NW;
     auto issue_block = [&](int ii, uint32_t dst, int koff) {
       if (ii < NB_A)
-        dma16(rsA, dst + 1024u * NW * ii, voffA, koff + (int)(ii * 64 * lda));
+        dma16(rsA, dst + 1024u * NW * ii, voffA + (int)(ii * 64 * lda), koff);
       else
-        dma16(rsB, dst + 1024u * NW * ii, voffB, koff + (int)((ii - NB_A) * 64 * ldb));
+        dma16(rsB, dst + 1024u * NW * ii, voffB + (int)((ii - NB_A) * 64 * ldb), koff);
     };
     auto slot_dst = [&](int p) {
       return lds0 + (uint32_t)((p & 1) * SLOT_BYTES) + 1024u * (uint32_t)wave;
