@@ -98,18 +98,30 @@ typedef enum rlk_status {
 #define RLK_MAX_V (1LL << 24)
 #define RLK_MAX_VOCAB ((1LL << 31) - 1)
 
-/* Bytes of device workspace the forward needs for (T, H, V): one 16-byte
+/* Source: the rollout side runs the op inside captured CUDA graphs of batch
+ * 1-4 (page "RL-Kernel evidence h100-cp-gradient.json",
+ * validation.cudagraph.expected_capture_sizes), where nothing may allocate:
+ * the caller sizes and owns every scratch buffer.
+ * Bytes of device workspace the forward needs for (T, H, V): one 16-byte
  * record per row and group of 256 columns, (ceil(V/256) + 3) groups at most,
  * two records per group (one per 128-column half) when T <= 64, rounded up
  * to 256 bytes. 0 when T == 0. */
 RLK_API size_t rlk_linear_logp_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V);
 
-/* Bytes of device workspace the backward needs for (T, H, V, flags, whether
+/* Source: the training side differentiates through the op (page "RL-Kernel
+ * evidence h100-cp-gradient.json", validation.runtime_readbacks.frameworks
+ * ['megatron/training'].modules.logp); its scratch is the caller's, as above.
+ * Bytes of device workspace the backward needs for (T, H, V, flags, whether
  * dhidden is requested). 0 when T == 0. */
 RLK_API size_t rlk_linear_logp_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V,
                                                    uint32_t flags, int want_dhidden);
 
-/* Forward.
+/* Forward. Source: the linear-logp provider that stands in for VIME's
+ * calculate_log_probs_and_entropy (page "VIME Qwen3-8B TP4/CP2 200-round
+ * consistency experiment", section "User-facing operator matrix"), called by
+ * both the trainer and the rollout engine with bit-equal results (page
+ * "RL-Kernel evidence h100-cp-gradient.json", validation.train_rollout_logprob
+ * and validation.runtime_scalar_logprob: 0 bitwise mismatches, max |d| = 0).
  *   hidden   bf16 [T,H]
  *   weight   bf16 [V,H], rows vocab_start .. vocab_start+V-1 of the LM head
  *   targets  int32 [T], global ids; 0 <= y < vocab_total is a precondition
@@ -125,7 +137,12 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
                                        float* entropy, float* stats, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
-/* Packed weight for the streaming forward.
+/* Packed weight for the streaming forward. Source: the rollout engine scores
+ * decode batches of 1-4 rows (page "RL-Kernel evidence h100-cp-gradient.json",
+ * validation.cudagraph.expected_capture_sizes; page "VIME Qwen3-8B TP4/CP2
+ * 200-round consistency experiment", section "Required gates": CUDA Graph
+ * evidence must match) and must return the trainer's bits
+ * (validation.train_rollout_logprob).
  *
  * Rollout calls the forward with a few rows at a time (the decode batch) and
  * a weight that stays fixed for the whole rollout, so the forward is a read
@@ -148,16 +165,22 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
  * pack and use with the same four values. */
 RLK_API size_t rlk_linear_pack_weight_bytes(int64_t H, int64_t V, int64_t vocab_start,
                                             int64_t vocab_total);
-/* weight bf16 [V,H] (16-byte aligned); packed: device buffer of packed_bytes >=
+/* Source: as the size query above (rollout-side scoring, same bits).
+ * weight bf16 [V,H] (16-byte aligned); packed: device buffer of packed_bytes >=
  * rlk_linear_pack_weight_bytes(...), 16-byte aligned, written on `stream`.
  * Errors as the forward's shape and argument checks;
  * RLK_ERR_WORKSPACE_TOO_SMALL if packed_bytes is short. */
 RLK_API rlk_status rlk_linear_pack_weight(const void* weight, int64_t H, int64_t V,
                                           int64_t vocab_start, int64_t vocab_total, void* packed,
                                           size_t packed_bytes, void* stream);
-/* Workspace of the packed forward: two 16-byte records per row and group. */
+/* Source: as rlk_linear_logp_fwd_workspace_bytes (no allocation inside a
+ * captured rollout graph). Workspace of the packed forward: two 16-byte
+ * records per row and group. */
 RLK_API size_t rlk_linear_logp_fwd_packed_workspace_bytes(int64_t T, int64_t H, int64_t V);
-/* The forward over a packed weight: arguments and results as
+/* Source: rollout-side scoring with the trainer's bits (page "RL-Kernel
+ * evidence h100-cp-gradient.json", validation.runtime_readbacks.frameworks
+ * ['vllm/rollout'].modules.logp and validation.train_rollout_logprob).
+ * The forward over a packed weight: arguments and results as
  * rlk_linear_logp_fwd, with packed_weight/packed_bytes from
  * rlk_linear_pack_weight for the same (H, V, vocab_start, vocab_total)
  * (RLK_ERR_INVALID_ARG if packed_bytes is short) and the workspace from
@@ -171,7 +194,12 @@ RLK_API rlk_status rlk_linear_logp_fwd_packed(const void* hidden, const void* pa
                                               void* workspace, size_t workspace_bytes,
                                               void* stream);
 
-/* Backward.
+/* Backward. Source: the actor-train phase back-propagates through the op
+ * (page "RL-Kernel evidence h100-cp-gradient.json",
+ * validation.runtime_readbacks.frameworks['megatron/training'].modules.logp),
+ * and its gradients must not depend on the parallel layout
+ * (gradient_norm_comparisons: exactly_equal between the TP2/CP4 and TP4/CP2
+ * runs; all_parameter_hash_comparisons: bitwise_equal).
  *   hidden, weight, targets, T, H, V, vocab_start, vocab_total: as in the forward
  *   stats    fp32 [T,4] whole-vocabulary record (the forward's `stats` for a
  *            full call, or the combined record for slices)
@@ -193,7 +221,13 @@ RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
                                        uint32_t flags, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
-/* Merge of S slice records (slices in vocabulary order) by the fixed merge
+/* Source: the actor runs the LM head at TP=4 (page "VIME Qwen3-8B TP4/CP2
+ * 200-round consistency experiment", section "Required gates"), and the
+ * TP2/CP4 and TP4/CP2 runs agree bit for bit (page "RL-Kernel evidence
+ * h100-cp-gradient.json", gradient_norm_comparisons,
+ * all_parameter_hash_comparisons), so slice records merge in an order that
+ * does not depend on the TP degree.
+ * Merge of S slice records (slices in vocabulary order) by the fixed merge
  * tree: adjacent pairs first, (r0 + r1), (r2 + r3), ..., an odd last record
  * carried up unchanged, repeated until one record is left; so S = 2 gives
  * r0 + r1 and S = 4 gives (r0 + r1) + (r2 + r3).
@@ -215,15 +249,30 @@ RLK_API rlk_status rlk_linear_logp_combine(const float* partials, int64_t S, int
 RLK_API rlk_status rlk_linear_logp_combine_host(const float* partials, int64_t S, int64_t T,
                                                 float* logp, float* entropy, float* stats);
 
-/* Provenance. */
+/* Source: strict mode fails on any fallback (page "RL-Kernel
+ * h3-runtime-integration-b200 report.json", runtime_modes.strict:
+ * fail_on_fallback) and R/R runs must show no fallback provenance (page "VIME
+ * Qwen3-8B TP4/CP2 200-round consistency experiment", section "Required
+ * gates"): every failure is a status code, never a silent other route.
+ * Text of a status code. */
 RLK_API const char* rlk_status_string(int status);
+/* Source: the runtime reads back, per framework and module, the backend ids
+ * and call counts that ran (page "RL-Kernel evidence h100-cp-gradient.json",
+ * validation.runtime_readbacks: backend_ids, call_count).
+ * Backend id of this library ("rlk.linear_logp.bitwise.gfx950.v1"). */
 RLK_API const char* rlk_backend_id(void);
-/* Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host,
+/* Source: as rlk_backend_id (validation.runtime_readbacks: call_count).
+ * Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host,
  * 3 combine, 4 pack_weight, 5 fwd_packed. */
 RLK_API uint64_t rlk_call_count(int which);
+/* Source: as rlk_backend_id (the readback names the exact backend version).
+ * Version of this ABI (1). */
 RLK_API int rlk_abi_version(void);
 
-/* Per-launch event timer, for measurement. After rlk_profile_begin every
+/* Source: the pages time the log-prob pass per phase (page "RL-Kernel
+ * evidence h100-cp-gradient.json", runs[].performance: perf/log_probs_time,
+ * perf/actor_train_time); this timer splits such a pass per kernel.
+ * Per-launch event timer, for measurement. After rlk_profile_begin every
  * kernel launch of the library is bracketed by two HIP events recorded on the
  * launch's own stream (launch order and work are unchanged).
  * rlk_profile_end waits for those events, stops the timer and writes, per

@@ -15,8 +15,8 @@ What is computed (sources are the three pages on RL-Kernel):
   ``calculate_log_probs_and_entropy``, so per token it returns the log-prob of
   the target token and the entropy of the softmax over the vocabulary, with
   logits given by a linear LM head (hidden times the vocabulary weight).
-* "RL-Kernel evidence h100-cp-gradient.json", ``validation.module_provenance
-  .groups['megatron/train'].modules.logp`` (backend
+* "RL-Kernel evidence h100-cp-gradient.json", ``validation.runtime_readbacks
+  .frameworks['megatron/training'].modules.logp`` (backend
   ``rlkernel.linear_logp.bitwise.v1``): the operator runs in the training
   framework, whose actor-train phase differentiates through it, so a backward
   pass (gradients of hidden and weight) belongs to the op.

@@ -25,8 +25,8 @@ out, R_t = sum_{v != v*} exp(z_{t,v} - m_t), so log sum exp(z - m) = log1p(R)
 keeps full relative accuracy when the softmax is peaky (R << 1).
 
 The backward pass is the derivative of the two outputs. The evidence page
-"RL-Kernel evidence h100-cp-gradient.json" (``validation.module_provenance``,
-module ``logp`` under ``megatron/train``) shows the op inside the training
+"RL-Kernel evidence h100-cp-gradient.json" (``validation.runtime_readbacks``,
+module ``logp`` under ``megatron/training``) shows the op inside the training
 framework whose actor-train phase back-propagates through it; the gradient is
 fixed by calculus:
 
@@ -248,7 +248,8 @@ def finalize_partials(p):
 
 def backward_f64(h: np.ndarray, W: np.ndarray, y: np.ndarray, dlogp: np.ndarray,
                  dentropy: np.ndarray | None = None, *, dh_rows=None, dw_rows=None,
-                 vocab_range: tuple[int, int] | None = None, row_block: int = ROW_BLOCK):
+                 vocab_range: tuple[int, int] | None = None, with_abs: bool = False,
+                 row_block: int = ROW_BLOCK):
     """Gradients of sum_t (dlogp_t logp_t + dent_t entropy_t) in float64.
 
     h [T,H], W [V,H] full vocabulary (the softmax always spans all V rows).
@@ -258,7 +259,12 @@ def backward_f64(h: np.ndarray, W: np.ndarray, y: np.ndarray, dlogp: np.ndarray,
     vocab_range: (a, b) restricts the vocabulary *contribution*: dH is then
              sum_{a <= v < b} G[:, v] W[v] (one slice's share) and dW rows must
              lie in [a, b). Default: the whole vocabulary.
-    Returns dict with dH [len(dh_rows), H], dW [len(dw_rows), H], dh_rows, dw_rows.
+    with_abs: also return the sums of the absolute values of the terms of each
+             returned element, dH_abs = |G| |W| and dW_abs = |G|^T |h| over the
+             same rows and vocabulary range (the scale of the rounding error of
+             any summation of those terms).
+    Returns dict with dH [len(dh_rows), H], dW [len(dw_rows), H], dh_rows, dw_rows
+    (and dH_abs, dW_abs of the same shapes with ``with_abs``).
     """
     h = np.asarray(h, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
@@ -275,7 +281,10 @@ def backward_f64(h: np.ndarray, W: np.ndarray, y: np.ndarray, dlogp: np.ndarray,
     dh_pos = {int(r): i for i, r in enumerate(dh_rows)}
     dH = np.zeros((dh_rows.size, H))
     dW = np.zeros((dw_rows.size, H))
+    dH_abs = np.zeros((dh_rows.size, H)) if with_abs else None
+    dW_abs = np.zeros((dw_rows.size, H)) if with_abs else None
     Wr = W[a:b]
+    Wr_abs = np.abs(Wr) if with_abs else None
     for r0 in range(0, T, row_block):
         r1 = min(T, r0 + row_block)
         z = h[r0:r1] @ W.T
@@ -290,8 +299,15 @@ def backward_f64(h: np.ndarray, W: np.ndarray, y: np.ndarray, dlogp: np.ndarray,
         if sel:
             loc = np.array(sel) - r0
             dH[[dh_pos[t] for t in sel]] = Gr[loc] @ Wr
+            if with_abs:
+                dH_abs[[dh_pos[t] for t in sel]] = np.abs(Gr[loc]) @ Wr_abs
         dW += G[:, dw_rows].T @ h[r0:r1]
-    return {"dH": dH, "dW": dW, "dh_rows": dh_rows, "dw_rows": dw_rows}
+        if with_abs:
+            dW_abs += np.abs(G[:, dw_rows]).T @ np.abs(h[r0:r1])
+    out = {"dH": dH, "dW": dW, "dh_rows": dh_rows, "dw_rows": dw_rows}
+    if with_abs:
+        out.update({"dH_abs": dH_abs, "dW_abs": dW_abs})
+    return out
 
 
 def backward(hidden_bf16, weight_bf16, targets, dlogp, dentropy=None, **kw):

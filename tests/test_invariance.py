@@ -4,7 +4,7 @@ The pages' acceptance form for the linear-logp route is zero bitwise
 mismatches and max |diff| = 0 between the trainer's large packed batches and
 the rollout engine's CUDA-graph batches of 1 to 4 ("RL-Kernel evidence
 h100-cp-gradient.json", validation.train_rollout_logprob and
-validation.cuda_graph.expected_capture_sizes). Here a fixed pool of 64
+validation.cudagraph.expected_capture_sizes). Here a fixed pool of 64
 Qwen3-8B-shaped rows (H = 4096, V = 151936) is scored in batches of 1, 2, 3,
 4, 24 and 64, under 3 row permutations, embedded in a batch of 512 other rows,
 and repeated, and scored through the packed-weight rollout path in batches

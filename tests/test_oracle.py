@@ -296,3 +296,63 @@ def test_bf16_entry_points_decode_inputs():
     a = forward(hb, Wb, y)
     b = forward_f64(hb.double().numpy(), Wb.double().numpy(), y.numpy())
     assert np.array_equal(a["logp"], b["logp"]) and np.array_equal(a["entropy"], b["entropy"])
+
+
+# ------------------------------------ sampled rows of the backward (used by
+# every full-size GPU gradient comparison) and the absolute-term sums
+
+@pytest.mark.parametrize("vocab_range", [None, (7, 31)])
+@pytest.mark.parametrize("with_dent", [False, True])
+def test_backward_sampled_rows_equal_full_rows(vocab_range, with_dent):
+    # rows spread over several row blocks, out of order; vocabulary rows out
+    # of order, with repeats of target rows
+    h, W, y, gl, ge = _rand_case(41, T=23, H=12, V=45, scale=1.5)
+    ge = ge if with_dent else None
+    full = backward_f64(h, W, y, gl, ge, vocab_range=vocab_range, with_abs=True, row_block=4)
+    a, b = vocab_range or (0, 45)
+    rows = np.array([17, 0, 5, 22, 8, 9])
+    vrows = np.array([b - 1, a, a + 3, a + 9, a + 4]) if vocab_range else np.array([44, 0, int(y[3]), 9, 30])
+    part = backward_f64(h, W, y, gl, ge, dh_rows=rows, dw_rows=vrows, vocab_range=vocab_range,
+                        with_abs=True, row_block=4)
+    assert np.array_equal(part["dh_rows"], rows) and np.array_equal(part["dw_rows"], vrows)
+    np.testing.assert_allclose(part["dH"], full["dH"][rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(part["dW"], full["dW"][vrows - a], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(part["dH_abs"], full["dH_abs"][rows], rtol=1e-12, atol=0)
+    np.testing.assert_allclose(part["dW_abs"], full["dW_abs"][vrows - a], rtol=1e-12, atol=0)
+    # the row-block size does not change the rows
+    one = backward_f64(h, W, y, gl, ge, dh_rows=rows, dw_rows=vrows, vocab_range=vocab_range,
+                       row_block=256)
+    np.testing.assert_allclose(one["dH"], part["dH"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(one["dW"], part["dW"], rtol=1e-12, atol=1e-15)
+
+
+def test_backward_sampled_rows_reject_rows_outside_the_range():
+    h, W, y, gl, _ = _rand_case(42, T=4, V=20)
+    with pytest.raises(ValueError):
+        backward_f64(h, W, y, gl, dw_rows=np.array([3]), vocab_range=(5, 10))
+
+
+def test_abs_terms_closed_form_uniform_softmax():
+    # identical W rows give p = 1/V and log p + entropy = 0, so
+    # G[t, v] = dlogp_t ([v == y_t] - 1/V):
+    #   dH_abs[t, k] = |dlogp_t| sum_v |[v == y_t] - 1/V| |W[v, k]|
+    #   dW_abs[v, k] = sum_t |dlogp_t| |[v == y_t] - 1/V| |h[t, k]|
+    r = rng(43)
+    T, H, V = 5, 4, 6
+    W = np.tile(r.standard_normal(H), (V, 1))
+    h = r.standard_normal((T, H))
+    y = np.array([0, 0, 2, 5, 3])
+    gl, ge = r.standard_normal(T), r.standard_normal(T)
+    g = backward_f64(h, W, y, gl, ge, with_abs=True)
+    coef = np.abs(gl)[:, None] * np.abs(np.eye(V)[y] - 1.0 / V)  # [T, V]
+    np.testing.assert_allclose(g["dH_abs"], coef @ np.abs(W), rtol=1e-12)
+    np.testing.assert_allclose(g["dW_abs"], coef.T @ np.abs(h), rtol=1e-12)
+
+
+def test_abs_terms_bound_the_gradients():
+    h, W, y, gl, ge = _rand_case(44, T=9, V=60, scale=2.0)
+    g = backward_f64(h, W, y, gl, ge, with_abs=True)
+    assert (np.abs(g["dH"]) <= g["dH_abs"] * (1 + 1e-12)).all()
+    assert (np.abs(g["dW"]) <= g["dW_abs"] * (1 + 1e-12)).all()
+    # mixed signs cancel: the bound is strict somewhere
+    assert (np.abs(g["dH"]) < 0.999 * g["dH_abs"]).any()
