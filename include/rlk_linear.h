@@ -73,7 +73,8 @@ typedef enum rlk_status {
   RLK_ERR_UNSUPPORTED_SHAPE = 2,   /* H not a positive multiple of 64, or a size beyond the limits */
   RLK_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the matching *_workspace_bytes() */
   RLK_ERR_UNSUPPORTED_DEVICE = 4,  /* the current device is not gfx950 */
-  RLK_ERR_HIP = 5                  /* a HIP runtime call failed (no device, launch failure) */
+  RLK_ERR_HIP = 5,                 /* a HIP runtime call failed (no device, launch failure) */
+  RLK_ERR_SCRATCH_LIMIT = 6        /* rlk_linear_logp_fwd_noalloc: records beyond its static scratch */
 } rlk_status;
 
 /* Per-row statistics record, 4 floats per row (row-major [T][4]):
@@ -136,6 +137,29 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
                                        int64_t vocab_start, int64_t vocab_total, float* logp,
                                        float* entropy, float* stats, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Arguments and results as rlk_linear_logp_fwd (the same kernels,
+ * so the same bits) without workspace: the records go to a static device
+ * array of RLK_NOALLOC_SCRATCH_BYTES that the library holds on each device it
+ * runs on until the process ends. Calls whose
+ * rlk_linear_logp_fwd_workspace_bytes(T, H, V) exceeds it return
+ * RLK_ERR_SCRATCH_LIMIT before anything is launched (8 MiB holds T up to 878
+ * rows of a 151,936-row vocabulary, or 64 rows of a 1,000,000-row one).
+ * Nothing in the scratch needs to start at zero: every record a result
+ * depends on is written by the same call. All calls on one device share that
+ * device's scratch, which keeps the last call's records: calls that overlap
+ * in time on one device (different streams, or host threads without
+ * ordering) race and give undefined results; calls ordered on one stream are
+ * safe. The first call on a device looks up the scratch's device address
+ * (hipGetSymbolAddress, with that device current) and keeps it. */
+#define RLK_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+RLK_API rlk_status rlk_linear_logp_fwd_noalloc(const void* hidden, const void* weight,
+                                               const int32_t* targets, int64_t T, int64_t H,
+                                               int64_t V, int64_t vocab_start,
+                                               int64_t vocab_total, float* logp, float* entropy,
+                                               float* stats, void* stream);
 
 /* Packed weight for the streaming forward. Source: the rollout engine scores
  * decode batches of 1-4 rows (page "RL-Kernel evidence h100-cp-gradient.json",
@@ -263,7 +287,7 @@ RLK_API const char* rlk_status_string(int status);
 RLK_API const char* rlk_backend_id(void);
 /* Source: as rlk_backend_id (validation.runtime_readbacks: call_count).
  * Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host,
- * 3 combine, 4 pack_weight, 5 fwd_packed. */
+ * 3 combine, 4 pack_weight, 5 fwd_packed, 6 fwd_noalloc. */
 RLK_API uint64_t rlk_call_count(int which);
 /* Source: as rlk_backend_id (the readback names the exact backend version).
  * Version of this ABI (1). */

@@ -34,7 +34,7 @@ RLK_OK = 0
 RLK_DH_F32 = 1
 STATUS_NAMES = {0: "RLK_OK", 1: "RLK_ERR_INVALID_ARG", 2: "RLK_ERR_UNSUPPORTED_SHAPE",
                 3: "RLK_ERR_WORKSPACE_TOO_SMALL", 4: "RLK_ERR_UNSUPPORTED_DEVICE",
-                5: "RLK_ERR_HIP"}
+                5: "RLK_ERR_HIP", 6: "RLK_ERR_SCRATCH_LIMIT"}
 
 _lib = None
 
@@ -64,6 +64,9 @@ def load_library(path: str | None = None):
     lib.rlk_linear_logp_fwd.argtypes = [vp, vp, i32p, i64, i64, i64, i64, i64, f32p, f32p, f32p,
                                         vp, sz, vp]
     lib.rlk_linear_logp_fwd.restype = ctypes.c_int
+    lib.rlk_linear_logp_fwd_noalloc.argtypes = [vp, vp, i32p, i64, i64, i64, i64, i64, f32p, f32p,
+                                                f32p, vp]
+    lib.rlk_linear_logp_fwd_noalloc.restype = ctypes.c_int
     lib.rlk_linear_logp_fwd_packed_workspace_bytes.argtypes = [i64, i64, i64]
     lib.rlk_linear_logp_fwd_packed_workspace_bytes.restype = sz
     lib.rlk_linear_pack_weight_bytes.argtypes = [i64, i64, i64, i64]
@@ -248,6 +251,30 @@ def fwd(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, *,
     _check(lib.rlk_linear_logp_fwd(_ptr(hidden), _ptr(weight), _ptr(targets), T, H, V,
                                    vocab_start, vt, _ptr(logp), _ptr(ent), _ptr(stats),
                                    _ptr(ws), ws.numel(), _stream(dev)))
+    return {"logp": logp, "entropy": ent, "stats": stats}
+
+
+def fwd_noalloc(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor, *,
+                vocab_start: int = 0, vocab_total: int | None = None, want_logp: bool = True,
+                want_entropy: bool = True, want_stats: bool = True, out: dict | None = None):
+    """Forward through ``rlk_linear_logp_fwd_noalloc``: the library's static
+    scratch instead of a workspace (same bits as ``fwd``). Outputs come from
+    ``out`` when they fit, else are allocated here (the library allocates
+    nothing). Raises RlkError(RLK_ERR_SCRATCH_LIMIT) when the records of
+    (T, H, V) exceed the scratch."""
+    lib = load_library()
+    _check_inputs(hidden, weight, targets)
+    T, H = hidden.shape
+    V = weight.shape[0]
+    vt = V if vocab_total is None else vocab_total
+    full = vocab_start == 0 and V == vt
+    dev = hidden.device
+    out = {} if out is None else out
+    logp, ent, stats = _outputs(out, T, full, want_logp, want_entropy, want_stats, dev)
+    out.update({"logp": logp, "entropy": ent, "stats": stats})
+    _check(lib.rlk_linear_logp_fwd_noalloc(_ptr(hidden), _ptr(weight), _ptr(targets), T, H, V,
+                                           vocab_start, vt, _ptr(logp), _ptr(ent), _ptr(stats),
+                                           _stream(dev)))
     return {"logp": logp, "entropy": ent, "stats": stats}
 
 

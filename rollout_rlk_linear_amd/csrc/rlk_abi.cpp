@@ -17,7 +17,38 @@ namespace {
 constexpr int kAbiVersion = 1;
 const char kBackendId[] = "rlk.linear_logp.bitwise.gfx950.v1";
 
-std::atomic<uint64_t> g_calls[6];
+std::atomic<uint64_t> g_calls[7];
+
+// Scratch of rlk_linear_logp_fwd_noalloc: the forward's per-(row, group)
+// record buffer, in device memory that the code object itself holds (one
+// copy per device, from module load until the process ends), so that the
+// entry point allocates nothing. In host code `scratch` is only a stand-in
+// for the symbol, never a device address: kernels and copies get the address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = RLK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+rlk_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RLK_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RLK_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return RLK_OK;
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -222,12 +253,14 @@ RLK_API size_t rlk_linear_logp_bwd_workspace_bytes(int64_t T, int64_t H, int64_t
 }
 
 namespace {
-// The forward for the natural layout (packed_bytes == 0) or the packed one.
+// The forward for the natural layout (packed_bytes == 0) or the packed one;
+// with noalloc the records go to the static scratch instead of the caller's
+// workspace.
 rlk_status fwd_call(const void* hidden, const void* weight, bool packed, size_t packed_bytes,
                     const int32_t* targets, int64_t T, int64_t H, int64_t V, int64_t vocab_start,
                     int64_t vocab_total, float* logp, float* entropy, float* stats,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  const int counter = packed ? 5 : 0;
+                    void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
+  const int counter = noalloc ? 6 : packed ? 5 : 0;
 
   rlk_status s = check_shape(T, H, V, vocab_start, vocab_total);
   if (s != RLK_OK) return s;
@@ -247,11 +280,19 @@ rlk_status fwd_call(const void* hidden, const void* weight, bool packed, size_t 
       packed_bytes < rlk::packed_weight_bytes(H, rlk::fwd_slicing(V, vocab_start, vocab_total)))
     return RLK_ERR_INVALID_ARG;
   const size_t need = rlk::fwd_workspace(T, H, V, packed);
-  if (workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
-  if (!workspace || !aligned(workspace, 16)) return RLK_ERR_INVALID_ARG;
+  if (noalloc) {
+    if (need > kScratchBytes) return RLK_ERR_SCRATCH_LIMIT;
+  } else {
+    if (workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned(workspace, 16)) return RLK_ERR_INVALID_ARG;
+  }
   int n_cu = 0;
   s = check_device(&n_cu);
   if (s != RLK_OK) return s;
+  if (noalloc) {
+    s = scratch_address(&workspace);
+    if (s != RLK_OK) return s;
+  }
 
   rlk::FwdArgs a{};
   a.n_cu = n_cu;
@@ -283,6 +324,15 @@ RLK_API rlk_status rlk_linear_logp_fwd(const void* hidden, const void* weight,
                                        size_t workspace_bytes, void* stream) {
   return fwd_call(hidden, weight, false, 0, targets, T, H, V, vocab_start, vocab_total, logp,
                   entropy, stats, workspace, workspace_bytes, stream);
+}
+
+RLK_API rlk_status rlk_linear_logp_fwd_noalloc(const void* hidden, const void* weight,
+                                               const int32_t* targets, int64_t T, int64_t H,
+                                               int64_t V, int64_t vocab_start,
+                                               int64_t vocab_total, float* logp, float* entropy,
+                                               float* stats, void* stream) {
+  return fwd_call(hidden, weight, false, 0, targets, T, H, V, vocab_start, vocab_total, logp,
+                  entropy, stats, nullptr, 0, stream, true);
 }
 
 RLK_API rlk_status rlk_linear_logp_fwd_packed(const void* hidden, const void* packed_weight,
@@ -443,6 +493,9 @@ RLK_API const char* rlk_status_string(int status) {
     case RLK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case RLK_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
     case RLK_ERR_HIP: return "HIP runtime error";
+    case RLK_ERR_SCRATCH_LIMIT:
+      return "records exceed the static scratch of rlk_linear_logp_fwd_noalloc "
+             "(RLK_NOALLOC_SCRATCH_BYTES); use rlk_linear_logp_fwd with a workspace";
     default: return "unknown status";
   }
 }
@@ -450,7 +503,7 @@ RLK_API const char* rlk_status_string(int status) {
 RLK_API const char* rlk_backend_id(void) { return kBackendId; }
 
 RLK_API uint64_t rlk_call_count(int which) {
-  if (which < 0 || which > 5) return 0;
+  if (which < 0 || which > 6) return 0;
   return g_calls[which].load(std::memory_order_relaxed);
 }
 

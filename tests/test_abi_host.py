@@ -23,7 +23,7 @@ from oracle import finalize_partials, forward_f64, merge_partials, slice_partial
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
-OK, INVALID, SHAPE, WS_SMALL, DEVICE, HIPERR = 0, 1, 2, 3, 4, 5
+OK, INVALID, SHAPE, WS_SMALL, DEVICE, HIPERR, SCRATCH = 0, 1, 2, 3, 4, 5, 6
 P = ctypes.c_void_p(1 << 20)  # aligned fake device pointer, never dereferenced on the host
 NULL = None
 
@@ -125,8 +125,9 @@ def test_microbench_argument_errors():
 def test_provenance(lib):
     assert lib.rlk_backend_id().decode() == "rlk.linear_logp.bitwise.gfx950.v1"
     assert lib.rlk_abi_version() == 1
-    for s in range(6):
+    for s in range(7):
         assert lib.rlk_status_string(s)
+    assert b"scratch" in lib.rlk_status_string(SCRATCH)
     assert lib.rlk_status_string(99).decode() == "unknown status"
     assert lib.rlk_call_count(7) == 0
 
@@ -348,3 +349,49 @@ def test_combine_host_empty_slice_and_missing_target():
     assert math.isclose(st[0, 2].item(), B, rel_tol=1e-6)
     assert math.isclose(logp[0].item(), -math.log1p(R), rel_tol=1e-6)
     assert math.isclose(ent[0].item(), math.log1p(R) - B / (1 + R), rel_tol=1e-6)
+
+
+# ------------------------------------------------ allocation-free forward --
+
+def fwd_na(lib, hidden=P, weight=P, targets=P, T=4, H=64, V=100, vs=0, vt=None, logp=P, ent=P,
+           stats=P):
+    vt = V if vt is None else vt
+    return lib.rlk_linear_logp_fwd_noalloc(hidden, weight, targets, T, H, V, vs, vt, logp, ent,
+                                           stats, NULL)
+
+
+def scratch_bytes():
+    txt = open(os.path.join(ROOT, "include", "rlk_linear.h")).read()
+    m = re.search(r"#define RLK_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
+    return int(m.group(1)) << int(m.group(2))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(H=96), SHAPE), (dict(vs=10, vt=105), INVALID),
+    (dict(vs=5, vt=200, stats=P), INVALID), (dict(logp=NULL, ent=NULL, stats=NULL), INVALID),
+    (dict(weight=NULL), INVALID), (dict(hidden=ctypes.c_void_p((1 << 20) + 2)), INVALID),
+    # records of the tile path: T x (ceil(V/256) + 3) x 16 bytes > 8 MiB
+    (dict(T=879, H=4096, V=151936), SCRATCH),
+    # records of the streaming path: two per group
+    (dict(T=64, H=64, V=1 << 20), SCRATCH),
+])
+def test_fwd_noalloc_argument_errors(lib, kw, code):
+    assert fwd_na(lib, **kw) == code
+
+
+def test_fwd_noalloc_limit_matches_the_workspace_query(lib):
+    cap = scratch_bytes()
+    assert cap == 8 << 20
+    for T, V in [(878, 151936), (879, 151936), (64, 1000000), (1, (1 << 24) - 1)]:
+        need = lib.rlk_linear_logp_fwd_workspace_bytes(T, 4096, V)
+        st = fwd_na(lib, T=T, H=4096, V=V)
+        assert (need <= cap) == (st != SCRATCH), (T, V, need, st)
+    # within the limit, a valid call passes every check up to the device
+    if not torch.cuda.is_available():
+        assert fwd_na(lib, T=878, H=4096, V=151936) in (HIPERR, DEVICE)
+
+
+def test_fwd_noalloc_T0_is_noop(lib):
+    before = lib.rlk_call_count(6)
+    assert fwd_na(lib, T=0, hidden=NULL, targets=NULL) == OK
+    assert lib.rlk_call_count(6) == before + 1
