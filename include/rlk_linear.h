@@ -53,7 +53,16 @@
  * slices, aligned to its own size (TP = 4, 2 or 1 with equal shares), computes
  * exactly its subtree, and rlk_linear_logp_combine merges call records with
  * the same tree: so TP = 1, 2 and 4 give identical bits for logp, entropy and
- * stats. Any other call covers one segment starting at its first row.
+ * stats. The backward does the same for dhidden: each virtual slice's
+ * contribution sum_{v in slice} G[t,v] W[v,:] is summed over splits that start
+ * at the slice's first row and are sized by the slice alone, and the slices'
+ * fp32 contributions are added by the same tree before the bf16 rounding; a
+ * slice call returns its subtree in fp32 (RLK_DH_F32) and
+ * rlk_linear_logp_dh_merge adds slice results by the tree. So dhidden has the
+ * same bits at TP = 1, 2 and 4, and every row of dweight (one owner per
+ * element, a chain over t) has the same bits in a slice call as in the
+ * whole-vocabulary call. Any other call covers one segment starting at its
+ * first row.
  */
 #ifndef RLK_LINEAR_H
 #define RLK_LINEAR_H
@@ -230,7 +239,8 @@ RLK_API rlk_status rlk_linear_logp_fwd_packed(const void* hidden, const void* pa
  *   dlogp    fp32 [T] or NULL (= 0)
  *   dentropy fp32 [T] or NULL (= 0)
  *   dhidden  [T,H] bf16 (fp32 with RLK_DH_F32), or NULL to skip. For a slice it
- *            is that slice's contribution sum_{v in slice} G[t,v] W[v,:].
+ *            is that slice's contribution sum_{v in slice} G[t,v] W[v,:]
+ *            (ask for fp32 and add slices with rlk_linear_logp_dh_merge).
  *   dweight  fp32 [V,H], overwritten, or NULL to skip
  *   flags    0 or RLK_DH_F32
  *   workspace, workspace_bytes: >= rlk_linear_logp_bwd_workspace_bytes(
@@ -273,6 +283,21 @@ RLK_API rlk_status rlk_linear_logp_combine(const float* partials, int64_t S, int
 RLK_API rlk_status rlk_linear_logp_combine_host(const float* partials, int64_t S, int64_t T,
                                                 float* logp, float* entropy, float* stats);
 
+/* Source: as rlk_linear_logp_combine (actor at TP=4; gradient_norm_comparisons
+ * exactly_equal across parallel layouts).
+ * Sum of S fp32 dH contributions of slice calls (slices in vocabulary order,
+ * each from rlk_linear_logp_bwd with RLK_DH_F32) by the fixed merge tree of
+ * rlk_linear_logp_combine (S = 2: p0 + p1; S = 4: (p0 + p1) + (p2 + p3)),
+ * then bf16 round-to-nearest-even into dhidden, or fp32 with RLK_DH_F32.
+ * With the slice calls of a TP = 2 or 4 layout it returns the bits of the
+ * whole-vocabulary backward's dhidden.
+ *   parts    fp32 [S][T][H] device, 1 <= S <= 1024
+ *   dhidden  [T,H] bf16 (fp32 with RLK_DH_F32) device
+ * H a positive multiple of 64 (RLK_ERR_UNSUPPORTED_SHAPE otherwise); T == 0
+ * is a no-op. Runs on `stream`. */
+RLK_API rlk_status rlk_linear_logp_dh_merge(const float* parts, int64_t S, int64_t T, int64_t H,
+                                            void* dhidden, uint32_t flags, void* stream);
+
 /* Source: strict mode fails on any fallback (page "RL-Kernel
  * h3-runtime-integration-b200 report.json", runtime_modes.strict:
  * fail_on_fallback) and R/R runs must show no fallback provenance (page "VIME
@@ -287,7 +312,7 @@ RLK_API const char* rlk_status_string(int status);
 RLK_API const char* rlk_backend_id(void);
 /* Source: as rlk_backend_id (validation.runtime_readbacks: call_count).
  * Number of successful calls since load: which = 0 fwd, 1 bwd, 2 combine_host,
- * 3 combine, 4 pack_weight, 5 fwd_packed, 6 fwd_noalloc. */
+ * 3 combine, 4 pack_weight, 5 fwd_packed, 6 fwd_noalloc, 7 dh_merge. */
 RLK_API uint64_t rlk_call_count(int which);
 /* Source: as rlk_backend_id (the readback names the exact backend version).
  * Version of this ABI (1). */

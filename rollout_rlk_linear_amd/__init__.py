@@ -83,6 +83,8 @@ def load_library(path: str | None = None):
     lib.rlk_linear_logp_combine_host.restype = ctypes.c_int
     lib.rlk_linear_logp_combine.argtypes = [f32p, i64, i64, f32p, f32p, f32p, vp]
     lib.rlk_linear_logp_combine.restype = ctypes.c_int
+    lib.rlk_linear_logp_dh_merge.argtypes = [f32p, i64, i64, i64, vp, u32, vp]
+    lib.rlk_linear_logp_dh_merge.restype = ctypes.c_int
     lib.rlk_status_string.argtypes = [ctypes.c_int]
     lib.rlk_status_string.restype = ctypes.c_char_p
     lib.rlk_backend_id.argtypes = []
@@ -421,6 +423,24 @@ def combine(partials, out: dict | None = None):
     _check(lib.rlk_linear_logp_combine(_ptr(parts), S, T, _ptr(logp), _ptr(ent), _ptr(stats),
                                        _stream(parts.device)))
     return {"logp": logp, "entropy": ent, "stats": stats}
+
+
+def dh_merge(parts, f32: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Sum fp32 dH contributions of slice calls (``bwd(..., dhidden_f32=True)`` of
+    each slice, in vocabulary order) by the library's fixed tree
+    (``rlk_linear_logp_dh_merge``); bf16 [T,H] (fp32 with ``f32``)."""
+    lib = load_library()
+    p = parts if isinstance(parts, torch.Tensor) else torch.stack(list(parts))
+    p = p.contiguous()
+    if p.dim() != 3 or p.dtype != torch.float32 or not p.is_cuda:
+        raise ValueError("parts must be device fp32 [S,T,H] (or a list of [T,H])")
+    S, T, H = p.shape
+    dt = torch.float32 if f32 else torch.bfloat16
+    if out is None or tuple(out.shape) != (T, H) or out.dtype != dt or not out.is_contiguous():
+        out = torch.empty(T, H, dtype=dt, device=p.device)
+    _check(lib.rlk_linear_logp_dh_merge(_ptr(p), S, T, H, _ptr(out), RLK_DH_F32 if f32 else 0,
+                                        _stream(p.device)))
+    return out
 
 
 class LinearLogp(torch.autograd.Function):

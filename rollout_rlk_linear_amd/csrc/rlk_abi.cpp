@@ -17,7 +17,7 @@ namespace {
 constexpr int kAbiVersion = 1;
 const char kBackendId[] = "rlk.linear_logp.bitwise.gfx950.v1";
 
-std::atomic<uint64_t> g_calls[7];
+std::atomic<uint64_t> g_calls[8];
 
 // Scratch of rlk_linear_logp_fwd_noalloc: the forward's per-(row, group)
 // record buffer, in device memory that the code object itself holds (one
@@ -128,7 +128,7 @@ int check_device_status() { return (int)check_device(); }
 
 const char* const kKernelNames[K_COUNT] = {
     "fwd_tile",  "fwd_combine", "bwd_rowprep", "bwd_recompute", "bwd_dw",     "bwd_dh",
-    "bwd_dh_reduce", "fill_zero", "combine",   "fwd_stream",    "pack_weight"};
+    "bwd_dh_reduce", "fill_zero", "combine",   "fwd_stream",    "pack_weight", "dh_merge"};
 
 void prof_before(int id, hipStream_t st) {
   if (!g_prof.on.load(std::memory_order_relaxed)) return;
@@ -169,7 +169,7 @@ size_t packed_weight_bytes(int64_t H, const FwdSlicing& sl) {
 }
 
 FwdSlicing fwd_slicing(int64_t V, int64_t vocab_start, int64_t vocab_total) {
-  FwdSlicing f{1, (int)V, 0, 0};
+  FwdSlicing f{1, (int)V, 0, 0, 0};
   if (vocab_total % kVirtualSlices == 0) {
     const int64_t vs = vocab_total / kVirtualSlices;
     if (vocab_start % vs == 0 && V % vs == 0) {
@@ -177,6 +177,7 @@ FwdSlicing fwd_slicing(int64_t V, int64_t vocab_start, int64_t vocab_total) {
       if ((p == 1 || p == 2 || p == 4) && first % p == 0) {
         f.P = (int)p;
         f.Vs = (int)vs;
+        f.sliced = 1;
       }
     }
   }
@@ -185,14 +186,20 @@ FwdSlicing fwd_slicing(int64_t V, int64_t vocab_start, int64_t vocab_total) {
   return f;
 }
 
-BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh) {
+BwdPlan bwd_plan(int64_t T, int64_t H, const FwdSlicing& sl, bool want_dh) {
   BwdPlan p{};
-  const int64_t Vp = round_up(V, 256);
-  int64_t S = V / kSplitCols;
+  p.P = sl.P;
+  p.Vs = sl.Vs;
+  p.Vs_pad = (int)round_up(sl.Vs, 256);
+  // splits per slice: from the slice size alone (and, for the virtual slices,
+  // a cap that keeps 4 slices within kMaxSplits)
+  int64_t S = sl.Vs / kSplitCols;
+  const int64_t cap = sl.sliced ? kMaxSplits / kVirtualSlices : kMaxSplits;
   if (S < 1) S = 1;
-  if (S > kMaxSplits) S = kMaxSplits;
-  p.split_w = (int)round_up(ceil_div(Vp, S), 256);
-  p.nsplits = (int)ceil_div(Vp, p.split_w);
+  if (S > cap) S = cap;
+  p.split_w = (int)round_up(ceil_div(p.Vs_pad, S), 256);
+  p.n_sub = (int)ceil_div(p.Vs_pad, p.split_w);
+  p.nsplits = p.P * p.n_sub;
   // dW walks K = t over [0, Tp) in steps of 32 (rows t >= T read as zero)
   p.Tp = round_up(T > 0 ? T : 1, 32);
   int64_t spc = kChunkElems / (p.Tp * p.split_w);
@@ -206,6 +213,19 @@ BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh) {
   p.off_part = align256(p.off_gtv + size_t(p.Tp) * size_t(p.ldg) * 2);
   p.total = align256(p.off_part + (want_dh ? size_t(p.nsplits) * size_t(T) * size_t(H) * 4 : 0));
   return p;
+}
+
+size_t bwd_workspace_any(int64_t T, int64_t H, int64_t V, bool want_dh) {
+  // the unsliced layout, and V as 1, 2 or 4 virtual slices
+  const FwdSlicing whole{1, (int)V, 0, 0, 0};
+  size_t m = bwd_plan(T, H, whole, want_dh).total;
+  for (int P : {1, 2, 4}) {
+    if (V % P != 0) continue;
+    const FwdSlicing sl{P, (int)(V / P), 0, 0, 1};
+    const size_t t = bwd_plan(T, H, sl, want_dh).total;
+    m = t > m ? t : m;
+  }
+  return m;
 }
 
 }  // namespace rlk
@@ -249,7 +269,7 @@ RLK_API size_t rlk_linear_logp_bwd_workspace_bytes(int64_t T, int64_t H, int64_t
                                                    uint32_t flags, int want_dhidden) {
   (void)flags;
   if (T <= 0 || H <= 0 || V <= 0) return 0;
-  return rlk::bwd_plan(T, H, V, want_dhidden != 0).total;
+  return rlk::bwd_workspace_any(T, H, V, want_dhidden != 0);
 }
 
 namespace {
@@ -376,7 +396,8 @@ RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
   if ((dlogp && !aligned(dlogp, 4)) || (dentropy && !aligned(dentropy, 4)))
     return RLK_ERR_INVALID_ARG;
   if (dhidden && !aligned(dhidden, 16)) return RLK_ERR_INVALID_ARG;
-  const rlk::BwdPlan plan = rlk::bwd_plan(T, H, V, dhidden != nullptr);
+  const rlk::FwdSlicing sl = rlk::fwd_slicing(V, vocab_start, vocab_total);
+  const rlk::BwdPlan plan = rlk::bwd_plan(T, H, sl, dhidden != nullptr);
   if (workspace_bytes < plan.total) return RLK_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 256)) return RLK_ERR_INVALID_ARG;
   s = check_device();
@@ -485,6 +506,25 @@ RLK_API rlk_status rlk_linear_logp_combine(const float* partials, int64_t S, int
   return RLK_OK;
 }
 
+RLK_API rlk_status rlk_linear_logp_dh_merge(const float* parts, int64_t S, int64_t T, int64_t H,
+                                            void* dhidden, uint32_t flags, void* stream) {
+  if (S < 1 || S > rlk::kMaxCombine || T < 0 || H <= 0) return RLK_ERR_INVALID_ARG;
+  if (flags & ~uint32_t(RLK_DH_F32)) return RLK_ERR_INVALID_ARG;
+  if (T > RLK_MAX_T || H > RLK_MAX_H || (H % 64) != 0) return RLK_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) {
+    g_calls[7].fetch_add(1, std::memory_order_relaxed);
+    return RLK_OK;
+  }
+  if (!parts || !aligned(parts, 16) || !dhidden || !aligned(dhidden, 16)) return RLK_ERR_INVALID_ARG;
+  const rlk_status s = check_device();
+  if (s != RLK_OK) return s;
+  if (rlk::launch_dh_merge(parts, (int)S, T * H, (flags & RLK_DH_F32) ? 1 : 0, dhidden,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return RLK_ERR_HIP;
+  g_calls[7].fetch_add(1, std::memory_order_relaxed);
+  return RLK_OK;
+}
+
 RLK_API const char* rlk_status_string(int status) {
   switch (status) {
     case RLK_OK: return "ok";
@@ -503,7 +543,7 @@ RLK_API const char* rlk_status_string(int status) {
 RLK_API const char* rlk_backend_id(void) { return kBackendId; }
 
 RLK_API uint64_t rlk_call_count(int which) {
-  if (which < 0 || which > 6) return 0;
+  if (which < 0 || which > 7) return 0;
   return g_calls[which].load(std::memory_order_relaxed);
 }
 

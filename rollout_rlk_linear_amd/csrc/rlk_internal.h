@@ -15,9 +15,9 @@ namespace rlk {
 // which one ran.
 constexpr int kSmallT = 64;
 
-// dH is reduced over fixed vocabulary splits: at most kMaxSplits of them,
-// about one per kSplitCols columns, each a multiple of 256 columns. They
-// depend on V only.
+// dH is reduced over fixed vocabulary splits, about one per kSplitCols
+// columns of a virtual slice (at most kMaxSplits in a call), each a multiple
+// of 256 columns and starting at its slice's first row.
 constexpr int kMaxSplits = 8;
 constexpr int kSplitCols = 16384;
 // Soft bound on the elements of one bf16 logit-gradient chunk (T x columns).
@@ -40,10 +40,11 @@ DwMap dw_map(int n_vtiles, int n_htiles);
 // by the fixed tree. Otherwise P = 1 and the one segment is the call.
 constexpr int kVirtualSlices = 4;
 struct FwdSlicing {
-  int P;   // virtual slices covered by the call (1, 2 or 4)
-  int Vs;  // rows per slice
-  int Gs;  // groups per slice
-  int G;   // P * Gs
+  int P;       // virtual slices covered by the call (1, 2 or 4)
+  int Vs;      // rows per slice
+  int Gs;      // groups per slice
+  int G;       // P * Gs
+  int sliced;  // 1 when the call follows the virtual slices (vocab_total / 4 rows each)
 };
 FwdSlicing fwd_slicing(int64_t V, int64_t vocab_start, int64_t vocab_total);
 // Records merged by one combine call, and the depth of its merge stack.
@@ -66,14 +67,35 @@ struct FwdArgs {
   float4* part;  // workspace [T][G]
 };
 
+// Backward vocabulary layout. The call's rows form P virtual slices of Vs
+// rows (the forward's slicing). Each slice is cut into n_sub splits of
+// split_w columns (a multiple of 256, the last one shorter) from the slice's
+// first row; n_sub depends on Vs alone, so a call at TP = 1, 2 or 4 cuts every
+// virtual slice the same way. The logit gradient, the recompute tiles and the
+// dW tiles live in the padded layout: column u is row u % Vs_pad of slice
+// u / Vs_pad (Vs_pad = Vs rounded up to 256), and the columns past a slice's
+// end hold zeros. dH of a row is the sum over each slice's splits in order,
+// then the slices by the fixed tree ((s0 + s1) + (s2 + s3)).
 struct BwdPlan {
-  int nsplits;          // splits of the (call-local) vocabulary
+  int P, Vs, Vs_pad;    // virtual slices of the call, rows per slice, padded
+  int n_sub;            // splits per slice
   int split_w;          // columns per split (multiple of 256)
+  int nsplits;          // P * n_sub
   int splits_per_chunk;
   int nchunks;
   int64_t ldg;          // row stride of the G chunk buffer (columns)
   int64_t Tp;           // T rounded up to the dW k-step (32)
   size_t off_rowc, off_gtv, off_part, total;
+  // padded column where split s begins / ends, and its valid columns
+  int u_begin(int s) const { return (s / n_sub) * Vs_pad + (s % n_sub) * split_w; }
+  int u_end(int s) const {
+    const int e = (s % n_sub + 1) * split_w;
+    return (s / n_sub) * Vs_pad + (e < Vs_pad ? e : Vs_pad);
+  }
+  int split_len(int s) const {
+    const int r = Vs - (s % n_sub) * split_w;
+    return r < split_w ? r : split_w;
+  }
 };
 
 struct BwdArgs {
@@ -106,6 +128,7 @@ enum KernelId {
   K_COMBINE,
   K_FWD_STREAM,
   K_PACK,
+  K_DH_MERGE,
   K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];
@@ -120,12 +143,16 @@ hipError_t launch_pack(const uint16_t* weight, int H, const FwdSlicing& sl, uint
                        hipStream_t st);
 // RLK_OK when the current device is gfx950, else the rlk_status error.
 int check_device_status();
-BwdPlan bwd_plan(int64_t T, int64_t H, int64_t V, bool want_dh);
+BwdPlan bwd_plan(int64_t T, int64_t H, const FwdSlicing& sl, bool want_dh);
+// Workspace bytes that cover a backward of (T, H, V) under any slicing.
+size_t bwd_workspace_any(int64_t T, int64_t H, int64_t V, bool want_dh);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st);
 hipError_t launch_combine(const float4* partials, int S, int T, float* logp, float* entropy,
                           float4* stats, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_dh_merge(const float* parts, int S, int64_t n, int out_f32, void* out,
+                           hipStream_t st);
 
 }  // namespace rlk

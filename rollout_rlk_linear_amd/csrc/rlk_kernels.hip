@@ -10,7 +10,8 @@
 //   fwd_combine  one wave per row: the row's group records folded in a fixed
 //                lane-strided order plus a fixed 64-lane tree; writes logp,
 //                entropy and the row's statistics record.
-// Backward (per vocabulary chunk, chunks made of whole dH splits):
+// Backward (per vocabulary chunk, chunks made of whole dH splits; columns in
+// the padded per-slice layout of BwdPlan, each virtual slice padded to 256):
 //   bwd_rowprep    per row: log1p(R), -B/(1+R), upstream gradients, local target.
 //   bwd_recompute  logits of the chunk again (same MFMA chain as the forward,
 //                  so the same bits), the logit gradient G in fp32, RNE to
@@ -19,9 +20,11 @@
 //                  K-major through transposing LDS reads), fp32, one owner
 //                  per element.
 //   bwd_dh         dH partial of split s = sum_{v in s} G[t, v] W[v, :], one
-//                  MFMA chain over the split in ascending v; splits are set by
-//                  V alone.
-//   bwd_dh_reduce  dH = sum_s partial_s in the order s = 0, 1, ...; bf16 RNE or fp32.
+//                  MFMA chain over the split in ascending v; splits start at
+//                  the first row of their virtual slice, sized by the slice.
+//   bwd_dh_reduce  per slice the splits' partials in order, then the slices by
+//                  the fixed tree; bf16 RNE or fp32.
+//   dh_merge       the same tree over fp32 dH contributions of slice calls.
 // Nothing uses atomics. All per-row arithmetic is independent of the tile
 // shape and the grid, so every row's outputs are identical for any T.
 #include <hip/hip_runtime.h>
@@ -553,17 +556,27 @@ __global__ __launch_bounds__(kThreads) void bwd_rowprep_kernel(
   rowc[2 * t + 1] = make_float4(de, __int_as_float(yli), s.y / (1.f + s.y), 0.f);
 }
 
+// Padded column u of the backward layout: virtual slice q = u / Vs_pad,
+// slice row l = u - q Vs_pad, call-local vocabulary row q Vs + l (valid while
+// l < Vs).
+__device__ __forceinline__ void padded_col(int u, int Vs, int Vs_pad, int& row, int& valid) {
+  const int q = u / Vs_pad;
+  const int l = u - q * Vs_pad;
+  row = q * Vs + l;
+  valid = Vs - l;
+}
+
 // G for one (T-tile, BN-column tile) of the chunk, rounded to bf16 into an
-// LDS tile [t][v], then stored as gtv[t][lg*BN + c] (rows t < T, 16-byte row
-// pieces; the columns past V up to the tile's end are zeros, which covers
-// dH's k-range; dW's last v-tile may also read columns beyond, which feed
-// only dW rows past V, never stored). Both dH and dW read G from there.
-// Each element depends on its logit and its row's constants only, so the
-// column width of the tile does not change a bit.
+// LDS tile [t][v], then stored as gtv[t][lt*BN + c] (rows t < T, 16-byte row
+// pieces; the tile's columns past its slice's end are zeros, which covers
+// dH's k-range at the end of every split; dW's tiles end on them too). Both
+// dH and dW read G from there. Each element depends on its logit and its
+// row's constants only, so the column width of the tile does not change a
+// bit. Tiles cover the chunk's padded columns [u0, u0 + n_tiles BN).
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
-    int V, int chunk_g0, int n_groups, int n_ttiles, const float4* __restrict__ rowc,
+    int u0, int Vs, int Vs_pad, int n_tiles, int n_ttiles, const float4* __restrict__ rowc,
     uint16_t* __restrict__ gtv, int64_t ldg) {
   using Gm = AsyncGemmP<BM, BN, WM, WN>;
   constexpr int LDG_S = BN + 8;  // [t][v] staging row (bf16), 16 B longer than the tile's
@@ -574,21 +587,20 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
 
   int lg, tt;
   xcd_decode(blockIdx.x, n_ttiles, lg, tt);
-  if (lg >= n_groups) return;
-  const int g = chunk_g0 + lg;
+  if (lg >= n_tiles) return;
   const int row0 = tt * BM;
-  const int col0 = g * BN;
+  int col0, vlim;  // call-local vocabulary row of the tile's first column; valid columns
+  padded_col(u0 + lg * BN, Vs, Vs_pad, col0, vlim);
   const int tid = threadIdx.x;
 
   Gm gm;
   gm.zero();
-  gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, V - col0, 0,
-         H);
+  // a tile wholly in its slice's padding (vlim <= 0) fetches no W row
+  gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, vlim, 0, H);
 
   const int lane = tid & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
-  const int vlim = V - col0;
   // logit gradient, rounded to bf16, into the [t][v] staging tile
   bool cvalid[Gm::NJ];
 #pragma unroll
@@ -664,12 +676,14 @@ DwMap dw_map(int n_vtiles, int n_htiles) {
   return m;
 }
 
-// One dW tile (v-tile vt, h-tile ht) of the chunk; lds holds DwGemm::LDS_BYTES.
+// One dW tile (v-tile vt, h-tile ht) of the chunk: G columns vt 256 .. + 255
+// of the buffer (padded columns u0 + vt 256 ..), dW rows from the call-local
+// vocabulary row of its first column; lds holds DwGemm::LDS_BYTES.
 using DwGemm = AsyncGemmKK<256, kDwBN, 2, 2, 3>;
 __device__ __forceinline__ void dw_tile(unsigned char* lds, const uint16_t* __restrict__ gtv,
                                         int64_t ldg, const uint16_t* __restrict__ hidden, int T,
-                                        int Tp, int H, int V, int chunk_v0, int chunk_w, int vt,
-                                        int ht, float* __restrict__ dweight) {
+                                        int Tp, int H, int u0, int Vs, int Vs_pad, int vt, int ht,
+                                        float* __restrict__ dweight) {
   using Gm = DwGemm;
   const int v0 = vt * 256, h0 = ht * kDwBN;
   Gm gm;
@@ -687,7 +701,8 @@ __device__ __forceinline__ void dw_tile(unsigned char* lds, const uint16_t* __re
   constexpr int ZS = kDwBN + 4;  // floats per staged row (conflict-free writes)
   static_assert(128 * ZS * 4 <= Gm::LDS_BYTES, "half a tile fits the ring");
   float* stage = reinterpret_cast<float*>(lds);
-  const int vlim = min(chunk_w, V - chunk_v0);
+  int vrow0, vlim;  // call-local vocabulary row of the tile's first row; valid rows
+  padded_col(u0 + v0, Vs, Vs_pad, vrow0, vlim);
   const int hcols = min(kDwBN, H - h0);  // a multiple of 64
   const int c4 = 4 * (lane & 31);        // column of this lane's 16 bytes
 #pragma unroll
@@ -708,11 +723,11 @@ __device__ __forceinline__ void dw_tile(unsigned char* lds, const uint16_t* __re
 #pragma unroll 4
     for (int k = wave; k < 64; k += 4) {
       const int row = 2 * k + (lane >> 5);
-      const int vl = v0 + 128 * half + row;
+      const int vl = 128 * half + row;
       if (vl < vlim && c4 < hcols) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * ZS + c4);
         __builtin_nontemporal_store(
-            v, reinterpret_cast<f32x4*>(dweight + (int64_t)(chunk_v0 + vl) * H + h0 + c4));
+            v, reinterpret_cast<f32x4*>(dweight + (int64_t)(vrow0 + vl) * H + h0 + c4));
       }
     }
     __syncthreads();
@@ -728,7 +743,7 @@ __device__ __forceinline__ void dw_tile_of(const DwMap& map, int xcd, int seq, i
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ hidden,
-              int T, int Tp, int H, int V, int chunk_v0, int chunk_w, int n_vtiles, int n_htiles,
+              int T, int Tp, int H, int u0, int Vs, int Vs_pad, int n_vtiles, int n_htiles,
               DwMap map, float* __restrict__ dweight) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[DwGemm::LDS_BYTES];
   const int seq = blockIdx.x >> 3;
@@ -736,35 +751,47 @@ bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __r
   int vt, ht;
   dw_tile_of(map, blockIdx.x & 7, seq, vt, ht);
   if (ht >= n_htiles || vt >= n_vtiles) return;
-  dw_tile(lds, gtv, ldg, hidden, T, Tp, H, V, chunk_v0, chunk_w, vt, ht, dweight);
+  dw_tile(lds, gtv, ldg, hidden, T, Tp, H, u0, Vs, Vs_pad, vt, ht, dweight);
 }
 
-// dH partial of split (split_base + si): rows t of the T-tile, columns h of
-// the H-tile, v over [s_begin, s_end) of the chunk in ascending order (the
-// G columns past V are zeros and the W rows past V read as zero, so the span
-// is rounded up to whole MFMA steps). Work items (t-tile fastest, then
-// h-tile, then split) are dealt to the 8 XCDs in contiguous runs, so one
-// split's G rows and W rows are fetched into one XCD's L2 and reused there.
+// The splits of the backward, as the kernels see them: P virtual slices of Vs
+// rows, padded to Vs_pad columns, each cut into n_sub splits of split_w
+// columns from the slice's first row (the last one shorter).
+struct SplitMap {
+  int Vs, Vs_pad, n_sub, split_w;
+};
+
+// dH partial of split s (of the call): rows t of the T-tile, columns h of the
+// H-tile, v over the split's columns in ascending order, one MFMA chain from
+// the split's first column (its G columns start at u_begin(s) - u0 in the
+// chunk buffer; its W rows at the slice's first row plus its offset). The
+// span is rounded up to whole MFMA steps: the G columns past the split's end
+// there are its slice's zero padding (or the next split's columns, at
+// multiples of 256 no step overruns) and the W rows past it read as zero.
+// Work items (t-tile fastest, then h-tile, then split) are dealt to the 8
+// XCDs in contiguous runs, so one split's G rows and W rows are fetched into
+// one XCD's L2 and reused there.
 template <int BM, int BN, int WM, int WN, int NSTG>
 __device__ __forceinline__ void dh_item(unsigned char* lds, const uint16_t* __restrict__ gtv,
                                         int64_t ldg, const uint16_t* __restrict__ weight, int T,
-                                        int H, int V, int chunk_v0, int split_w, int split_base,
-                                        int tt, int ht, int si, float* __restrict__ part) {
+                                        int H, int u0, SplitMap sm, int tt, int ht, int s,
+                                        float* __restrict__ part) {
   using Gm = AsyncGemmKN<BM, BN, WM, WN, NSTG>;
   const int row0 = tt * BM, h0 = ht * BN;
-  const int s_begin = si * split_w;
-  const int s_end = min(s_begin + split_w, V - chunk_v0);
-  const int k_end = s_begin + ((s_end - s_begin + 31) & ~31);
+  const int q = s / sm.n_sub, j = s - q * sm.n_sub;
+  const int a_col = q * sm.Vs_pad + j * sm.split_w - u0;  // chunk buffer column
+  const int w_row = q * sm.Vs + j * sm.split_w;            // call-local W row
+  const int len = min(sm.split_w, sm.Vs - j * sm.split_w);
   Gm gm;
   gm.zero();
-  gm.run(lds, gtv + (int64_t)row0 * ldg, ldg, T - row0, weight + (int64_t)chunk_v0 * H + h0, H,
-         V - chunk_v0, min(BN, H - h0), s_begin, k_end);
+  gm.run(lds, gtv + (int64_t)row0 * ldg + a_col, ldg, T - row0, weight + (int64_t)w_row * H + h0,
+         H, len, min(BN, H - h0), 0, (len + 31) & ~31);
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
   // a 16-column block is whole or absent (H is a multiple of 64): wave-uniform test
   const int hb = h0 + wn * Gm::WTN;
-  float* const out = part + (int64_t)(split_base + si) * T * H + hb + (lane & 15);
+  float* const out = part + (int64_t)s * T * H + hb + (lane & 15);
 #pragma unroll
   for (int i = 0; i < Gm::MI; ++i) {
 #pragma unroll
@@ -782,8 +809,8 @@ __device__ __forceinline__ void dh_item(unsigned char* lds, const uint16_t* __re
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
     const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ weight, int T,
-    int H, int V, int chunk_v0, int split_w, int n_splits, int split_base, int n_ttiles,
-    int n_htiles, int per_xcd, float* __restrict__ part) {
+    int H, int u0, SplitMap sm, int n_splits, int split_base, int n_ttiles, int n_htiles,
+    int per_xcd, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[AsyncGemmKN<BM, BN, WM, WN>::LDS_BYTES];
   const int seq = blockIdx.x >> 3;
   if (seq >= per_xcd) return;
@@ -792,30 +819,82 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
   const int tt = w % n_ttiles;
   const int ht = (w / n_ttiles) % n_htiles;
   const int si = w / (n_ttiles * n_htiles);
-  dh_item<BM, BN, WM, WN, 4>(lds, gtv, ldg, weight, T, H, V, chunk_v0, split_w, split_base, tt, ht,
-                             si, part);
+  dh_item<BM, BN, WM, WN, 4>(lds, gtv, ldg, weight, T, H, u0, sm, tt, ht, split_base + si, part);
 }
 
-// dH = sum_{s=0}^{S-1} part[s] in order; 4 elements per thread.
+__device__ __forceinline__ float4 add4(const float4& a, const float4& b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Sum of S values by the fixed merge tree of the slice records: a stack of
+// subtrees of decreasing power-of-two sizes, equal neighbours added left +
+// right as values arrive, the rest folded from the right. S = 2 gives
+// v0 + v1, S = 4 gives (v0 + v1) + (v2 + v3). next(i) yields value i.
+template <class Next>
+__device__ __forceinline__ float4 tree_sum(int S, Next next) {
+  float4 st[kCombineDepth];
+  int lvl[kCombineDepth];
+  int n = 0;
+  for (int i = 0; i < S; ++i) {
+    st[n] = next(i);
+    lvl[n++] = 0;
+    while (n >= 2 && lvl[n - 2] == lvl[n - 1]) {
+      st[n - 2] = add4(st[n - 2], st[n - 1]);
+      ++lvl[n - 2];
+      --n;
+    }
+  }
+  float4 acc = st[n - 1];
+  for (int i = n - 2; i >= 0; --i) acc = add4(st[i], acc);
+  return acc;
+}
+
+__device__ __forceinline__ void store_dh4(void* out, int64_t i4, int out_f32, const float4& v) {
+  if (out_f32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + i4) = v;
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i4) =
+        make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
+}
+
+// dH of the call: per virtual slice q its n_sub split partials in order
+// (part[q n_sub] + part[q n_sub + 1] + ...), then the P (1, 2 or 4) slice
+// sums by the fixed tree; 4 elements per thread.
 __global__ __launch_bounds__(kThreads) void bwd_dh_reduce_kernel(const float* __restrict__ part,
-                                                                 int S, int64_t n, int out_f32,
+                                                                 int P, int n_sub, int64_t n,
+                                                                 int out_f32,
                                                                  void* __restrict__ out) {
   const int64_t i4 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (i4 >= n) return;
-  float4 acc = *reinterpret_cast<const float4*>(part + i4);
-  for (int s = 1; s < S; ++s) {
-    const float4 q = *reinterpret_cast<const float4*>(part + (int64_t)s * n + i4);
-    acc.x = acc.x + q.x;
-    acc.y = acc.y + q.y;
-    acc.z = acc.z + q.z;
-    acc.w = acc.w + q.w;
-  }
-  if (out_f32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + i4) = acc;
-  } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i4) =
-        make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
-  }
+  auto slice_sum = [&](int q) {
+    const float* p = part + (int64_t)q * n_sub * n + i4;
+    float4 a = *reinterpret_cast<const float4*>(p);
+    for (int j = 1; j < n_sub; ++j) a = add4(a, *reinterpret_cast<const float4*>(p + j * n));
+    return a;
+  };
+  // tree_sum's expression for P = 1, 2, 4, written out (no stack)
+  float4 acc;
+  if (P == 4)
+    acc = add4(add4(slice_sum(0), slice_sum(1)), add4(slice_sum(2), slice_sum(3)));
+  else if (P == 2)
+    acc = add4(slice_sum(0), slice_sum(1));
+  else
+    acc = slice_sum(0);
+  store_dh4(out, i4, out_f32, acc);
+}
+
+// Merge of S fp32 dH contributions of slice calls (slices in vocabulary
+// order) by the same tree; 4 elements per thread.
+__global__ __launch_bounds__(kThreads) void dh_merge_kernel(const float* __restrict__ parts, int S,
+                                                            int64_t n, int out_f32,
+                                                            void* __restrict__ out) {
+  const int64_t i4 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  const float4 acc = tree_sum(S, [&](int s) {
+    return *reinterpret_cast<const float4*>(parts + (int64_t)s * n + i4);
+  });
+  store_dh4(out, i4, out_f32, acc);
 }
 
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -829,14 +908,14 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   template __global__ void fwd_tile_kernel<BM, WM, WN>(                                       \
       const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__, \
       int, int, int, int, int64_t, int, int, float4* __restrict__);
-#define RLK_RECOMPUTE(BM, BN, WM, WN)                                                         \
-  template __global__ void bwd_recompute_kernel<BM, BN, WM, WN>(                              \
+#define RLK_RECOMPUTE(BM, BN, WM, WN)                                                          \
+  template __global__ void bwd_recompute_kernel<BM, BN, WM, WN>(                               \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
-      const float4* __restrict__, uint16_t* __restrict__, int64_t);
-#define RLK_DH(BM, BN, WM, WN)                                                             \
-  template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                    \
-      const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, int, \
-      int, int, int, int, int, int, float* __restrict__);
+      int, const float4* __restrict__, uint16_t* __restrict__, int64_t);
+#define RLK_DH(BM, BN, WM, WN)                                                                \
+  template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                       \
+      const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, SplitMap, \
+      int, int, int, int, int, float* __restrict__);
 RLK_FWD_TILE(256, 2, 2)
 RLK_RECOMPUTE(32, 128, 2, 2)
 RLK_RECOMPUTE(256, 256, 2, 2)
@@ -922,7 +1001,7 @@ hipError_t launch_combine(const float4* partials, int S, int T, float* logp, flo
 }
 
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
-  const int T = a.T, H = a.H, V = a.V;
+  const int T = a.T, H = a.H;
   const int Tp = (int)p.Tp;
   RLK_LAUNCH(K_BWD_ROWPREP, bwd_rowprep_kernel, cdiv(T, kThreads), st, a.stats, a.dlogp,
              a.dentropy, a.targets, T, a.vocab_start, a.rowc);
@@ -930,52 +1009,56 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
   const int bm = small ? 32 : 256;
   const int nt = cdiv(T, bm);
   const int nht = cdiv(H, 256);
+  const SplitMap sm{p.Vs, p.Vs_pad, p.n_sub, p.split_w};
   for (int c = 0; c < p.nchunks; ++c) {
     const int s0 = c * p.splits_per_chunk;
     const int s1 = s0 + p.splits_per_chunk < p.nsplits ? s0 + p.splits_per_chunk : p.nsplits;
-    const int v0 = s0 * p.split_w;  // call-local
-    const int v1 = (s1 * p.split_w < V) ? s1 * p.split_w : V;
-    const int width = v1 - v0;
-    const int ngroups = cdiv(width, GROUP);
-    const int chunk_g0 = v0 / GROUP;
-    const int ng8 = cdiv(ngroups, 8) * 8;
+    const int u0 = p.u_begin(s0);
+    const int width = p.u_end(s1 - 1) - u0;  // padded columns of the chunk (a multiple of 256)
     if (small) {
       // 128-column tiles: the W stream of a small batch splits over twice as
       // many workgroups, so the last round is fuller
       constexpr int BN = 128;
-      const int ntl = cdiv(width, BN);
+      const int ntl = width / BN;
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, BN, 2, 2>), cdiv(ntl, 8) * 8 * nt, st,
-                 a.hidden, a.weight, T, H, V, v0 / BN, ntl, nt, a.rowc, a.gtv, p.ldg);
+                 a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, a.rowc, a.gtv, p.ldg);
     } else {
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2>), ng8 * nt, st, a.hidden,
-                 a.weight, T, H, V, chunk_g0, ngroups, nt, a.rowc, a.gtv, p.ldg);
+      const int ntl = width / 256;
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2>), cdiv(ntl, 8) * 8 * nt, st,
+                 a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, a.rowc, a.gtv, p.ldg);
     }
-    const int nvt = cdiv(width, 256);
+    const int nvt = width / 256;
     const int nhw = cdiv(H, kDwBN);
     const int nsp = s1 - s0;
     if (a.dweight) {
       const DwMap map = dw_map(nvt, nhw);
       RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, 8 * map.per_xcd, st, a.gtv, p.ldg, a.hidden, T, Tp, H,
-                 V, v0, ngroups * GROUP, nvt, nhw, map, a.dweight);
+                 u0, p.Vs, p.Vs_pad, nvt, nhw, map, a.dweight);
     }
     if (a.dhidden) {
       if (small) {
         const int nh = cdiv(H, 128);
         const int per = cdiv(nt * nh * nsp, 8);
         RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<32, 128, 1, 4>), 8 * per, st, a.gtv, p.ldg, a.weight,
-                   T, H, V, v0, p.split_w, nsp, s0, nt, nh, per, a.part);
+                   T, H, u0, sm, nsp, s0, nt, nh, per, a.part);
       } else {
         const int per = cdiv(nt * nht * nsp, 8);
         RLK_LAUNCH(K_BWD_DH, (bwd_dh_kernel<256, 256, 2, 2>), 8 * per, st, a.gtv, p.ldg, a.weight,
-                   T, H, V, v0, p.split_w, nsp, s0, nt, nht, per, a.part);
+                   T, H, u0, sm, nsp, s0, nt, nht, per, a.part);
       }
     }
   }
   if (a.dhidden) {
     const int64_t n = (int64_t)T * H;
-    RLK_LAUNCH(K_BWD_DH_REDUCE, bwd_dh_reduce_kernel, cdiv(n / 4, kThreads), st, a.part,
-               p.nsplits, n, a.dh_f32, a.dhidden);
+    RLK_LAUNCH(K_BWD_DH_REDUCE, bwd_dh_reduce_kernel, cdiv(n / 4, kThreads), st, a.part, p.P,
+               p.n_sub, n, a.dh_f32, a.dhidden);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_merge(const float* parts, int S, int64_t n, int out_f32, void* out,
+                           hipStream_t st) {
+  RLK_LAUNCH(K_DH_MERGE, dh_merge_kernel, cdiv(n / 4, kThreads), st, parts, S, n, out_f32, out);
   return hipGetLastError();
 }
 

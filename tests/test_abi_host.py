@@ -395,3 +395,26 @@ def test_fwd_noalloc_T0_is_noop(lib):
     before = lib.rlk_call_count(6)
     assert fwd_na(lib, T=0, hidden=NULL, targets=NULL) == OK
     assert lib.rlk_call_count(6) == before + 1
+
+
+# ------------------------------------------------------ dH slice merge --
+
+def test_dh_merge_argument_errors(lib):
+    raw = ctypes.CDLL(rlk.LIB_PATH)
+    raw.rlk_linear_logp_dh_merge.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32,
+                                             ctypes.c_void_p]
+    m = raw.rlk_linear_logp_dh_merge
+    assert m(P, 0, 4, 64, P, 0, NULL) == INVALID                   # no slices
+    assert m(P, 1025, 4, 64, P, 0, NULL) == INVALID                # too many
+    assert m(P, 2, -1, 64, P, 0, NULL) == INVALID
+    assert m(P, 2, 4, 0, P, 0, NULL) == INVALID
+    assert m(P, 2, 4, 64, P, 2, NULL) == INVALID                   # unknown flag
+    assert m(P, 2, 4, 96, P, 0, NULL) == SHAPE                     # H not a multiple of 64
+    assert m(NULL, 2, 4, 64, P, 0, NULL) == INVALID
+    assert m(P, 2, 4, 64, ctypes.c_void_p((1 << 20) + 8), 0, NULL) == INVALID
+    before = lib.rlk_call_count(7)
+    assert m(NULL, 2, 0, 64, NULL, 0, NULL) == OK                  # T = 0: no-op
+    assert lib.rlk_call_count(7) == before + 1
+    if not torch.cuda.is_available():
+        assert m(P, 2, 4, 64, P, 1, NULL) in (HIPERR, DEVICE)
