@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+PUBLISHED_SCLK_GHZ = 2.4   # the clock the published peak assumes (256 CUs x 2.4 GHz x 4096 flop)
 METRIC = "linear-logp fwd+bwd tokens/s and % bf16 MFMA peak at H4096 V151936 T512"
 CSRC = os.path.join(ROOT, "rollout_rlk_linear_amd", "csrc")
 
@@ -151,14 +152,46 @@ def microbench(torch, rlk):
 
     per, _ = timed(torch, mfma, 2, 5)
     mf = flops[0] / (min(per) * 1e-3) / 1e12
+    # both MFMA shapes with the shader clock they ran at (in-kernel s_memtime
+    # against the constant-rate wall clock)
+    clocks = torch.zeros(2 * wg, dtype=torch.int64, device=dev)
+    shapes = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        info = {}
+
+        def run():
+            info["flops"], info["khz"] = rlk.microbench_mfma_clock(sink, clocks, wg, iters, shape)
+
+        per_s, _ = timed(torch, run, 2, 5)
+        c = clocks.view(wg, 2).double().sum(dim=0).cpu()
+        sclk_ghz = float(c[0] / c[1]) * info["khz"] * 1e3 / 1e9
+        tf = info["flops"] / (min(per_s) * 1e-3) / 1e12
+        shapes[name] = {"TFLOPs": round(tf, 1), "sclk_GHz": round(sclk_ghz, 3),
+                        "frac_published": round(tf / PEAK_BF16_TFLOPS, 4),
+                        # the published peak scaled to the clock the run held
+                        "frac_of_peak_at_that_clock": round(
+                            tf / (PEAK_BF16_TFLOPS * sclk_ghz / PUBLISHED_SCLK_GHZ), 4)}
+    del clocks
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     per_r, _ = timed(torch, lambda: rlk.microbench_read(src, sink, ncu), 2, 5)
     read_gbs = n / (min(per_r) * 1e-3) / 1e9
     del src
+    # the vendor library's dense square GEMM as a second ceiling
+    g = torch.Generator(device="cpu").manual_seed(12)
+    a = torch.randn(8192, 8192, generator=g).to(torch.bfloat16).to(dev)
+    b = torch.randn(8192, 8192, generator=g).to(torch.bfloat16).to(dev)
+    per_g, _ = timed(torch, lambda: torch.matmul(a, b), 2, 5)
+    gemm_tf = 2.0 * 8192 ** 3 / (min(per_g) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    best = max(mf, gemm_tf, *(v["TFLOPs"] for v in shapes.values()))
     return {"copy_GBps": round(copy_gbs, 1), "copy_bytes": n, "read_GBps": round(read_gbs, 1),
             "read_bytes": n,
             "mfma_bf16_TFLOPs": round(mf, 1),
-            "mfma_workgroups": wg, "mfma_iters": iters}
+            "mfma_workgroups": wg, "mfma_iters": iters,
+            "mfma_shapes": shapes,
+            "hipblaslt_square_8192_bf16_TFLOPs": round(gemm_tf, 1),
+            "measured_bf16_ceiling_TFLOPs": round(best, 1)}
 
 
 def library_yardstick(torch, hidden, weight, kernels):
@@ -351,24 +384,49 @@ def workload_runs(torch, rlk, wl, read_gbs, steps):
     return res
 
 
-def cpu_baseline(case, rows: int):
-    """The float64 oracle (unchanged) on the first ``rows`` tokens of the batch."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(case, rows: int, tiny=None):
+    """The float64 oracle (unchanged) on the first ``rows`` tokens of the batch,
+    and on the whole tiny case (T=64, H=256, V=1024) when given."""
     from threadpoolctl import threadpool_info
 
     from oracle import backward, forward
 
-    h = case.hidden[:rows].contiguous()
-    y = case.targets[:rows].contiguous()
-    dl = case.dlogp[:rows].contiguous()
-    t0 = time.perf_counter()
-    forward(h, case.weight, y)
-    backward(h, case.weight, y, dl, None)
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    def run(c, n):
+        h = c.hidden[:n].contiguous()
+        y = c.targets[:n].contiguous()
+        dl = c.dlogp[:n].contiguous()
+        t0 = time.perf_counter()
+        forward(h, c.weight, y)
+        backward(h, c.weight, y, dl, None)
+        return time.perf_counter() - t0
+
+    dt = run(case, rows)
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    blas = [{k: p.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+            for p in pools if p.get("user_api") == "blas"]
     what = "the whole batch" if rows == case.T else f"the first {rows} of the {case.T} tokens"
-    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what}, full vocabulary, float64 forward + backward (all of dH and dW); "
-                      f"{dt:.1f} s wall"}
+    out = {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{what}, full vocabulary, float64 forward + backward (all of dH and dW); "
+                     f"{dt:.1f} s wall",
+           "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)), "blas": blas}
+    if tiny is not None:
+        run(tiny, tiny.T)  # warm-up: the first call pays the BLAS start-up
+        dtt = run(tiny, tiny.T)
+        out["tiny_T64_H256_V1024"] = {"value": tiny.T / dtt, "unit": "tokens/s",
+                                      "wall_s": round(dtt, 5)}
+    return out
 
 
 def main():
@@ -381,12 +439,14 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="only the T=512 step (no microbenchmarks, other workloads or clocks)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
-    ap.add_argument("--profile-case", choices=["fwd_t1", "fwd_t64", "fwd_packed_t1", "fwd_packed_t64", "read"],
+    ap.add_argument("--profile-case", choices=["fwd_t1", "fwd_t64", "fwd_packed_t1", "fwd_packed_t64", "read",
+                                               "mfma16", "mfma32"],
                     default=None,
                     help="run only this case's calls (warmup + steps), for profilers: fwd_t1 / _t64 = "
                          "the forward of 1 / 64 rows over the full vocabulary (natural layout), "
                          "fwd_packed_t1 / _t64 = the same over the packed weight with 1 / 64 rows, "
-                         "read = the 1 GiB streaming-read microbenchmark")
+                         "read = the 1 GiB streaming-read microbenchmark, mfma16 / mfma32 = the "
+                         "clocked MFMA-rate kernel in the 16x16x32 / 32x32x16 shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -424,6 +484,23 @@ def main():
         per, _ = timed(torch, lambda: rlk.microbench_read(src, sink, ncu), args.warmup, args.steps)
         print(json.dumps({"profile_case": "read", "ms": median_ci(per)}), flush=True)
         return
+    if args.profile_case in ("mfma16", "mfma32"):
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        wg, iters = 8 * ncu, 4096
+        sink = torch.zeros(4, dtype=torch.float32, device="cuda:0")
+        clocks = torch.zeros(2 * wg, dtype=torch.int64, device="cuda:0")
+        shape = 0 if args.profile_case == "mfma16" else 1
+        info = {}
+
+        def run():
+            info["flops"], info["khz"] = rlk.microbench_mfma_clock(sink, clocks, wg, iters, shape)
+
+        per, _ = timed(torch, run, args.warmup, args.steps)
+        cs = clocks.view(wg, 2).double().sum(dim=0).cpu()
+        print(json.dumps({"profile_case": args.profile_case, "ms": median_ci(per),
+                          "TFLOPs": info["flops"] / (min(per) * 1e-3) / 1e12,
+                          "sclk_GHz": float(cs[0] / cs[1]) * info["khz"] * 1e-6}), flush=True)
+        return
     if args.profile_case is not None:
         w = c.weight.to("cuda:0")
         pool = wl.pool64()
@@ -449,8 +526,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # headline pass: only the step events, no per-launch timer
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    rlk.profile_begin()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev[0].record()
@@ -459,10 +536,16 @@ def main():
         ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    prof = rlk.profile_end()
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms_total = ev[0].elapsed_time(ev[args.steps])
     ms_step = ms_total / args.steps
+    # second pass, for the per-kernel table: the library's per-launch events
+    rlk.profile_begin()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = rlk.profile_end()
+    prof_per_step = sum(ms for ms, _ in prof.values()) / args.steps
     tokens_s = T * args.steps / (ms_total / 1e3)
     flops_step = 8.0 * T * H * V
     tflops = flops_step / (ms_step / 1e3) / 1e12
@@ -512,6 +595,7 @@ def main():
         "tflops": round(tflops, 2), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "model_tflops_6thv": round(0.75 * tflops, 2),
         "wall_s_timed": round(wall, 4),
+        "kernel_pass_ms_per_step": round(prof_per_step, 4),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "roofline": roof,
@@ -525,9 +609,10 @@ def main():
         mb = microbench(torch, rlk)
         result["microbench"] = mb
         result["frac_measured_mfma"] = round(tflops / mb["mfma_bf16_TFLOPs"], 4)
+        result["frac_measured_ceiling"] = round(tflops / mb["measured_bf16_ceiling_TFLOPs"], 4)
         result["workloads"] = workload_runs(torch, rlk, wl, mb["read_GBps"], args.steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl.qwen512(), min(args.cpu_rows, T))
+        result["cpu_baseline"] = cpu_baseline(wl.qwen512(), min(args.cpu_rows, T), wl.tiny())
     else:
         result["cpu_baseline"] = None
     line = json.dumps(result)

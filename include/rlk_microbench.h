@@ -40,6 +40,19 @@ RLK_API rlk_status rlk_microbench_read(const void* src, size_t bytes, float* sin
  * cannot be elided. */
 RLK_API rlk_status rlk_microbench_mfma(float* sink, int64_t workgroups, int64_t iters, void* stream);
 
+/* The MFMA rate in either instruction shape, with the clock it ran at:
+ * shape 0 = v_mfma_f32_16x16x32_bf16 (32 independent accumulators per wave),
+ * shape 1 = v_mfma_f32_32x32x16_bf16 (16 accumulators of 16 floats); both do
+ * the flops of rlk_microbench_mfma for the same workgroups and iters. Lane 0 of
+ * wave 0 of every workgroup writes clocks[2 b] = shader-clock cycles
+ * (clock64) and clocks[2 b + 1] = wall-clock ticks (wall_clock64) between
+ * its start and its end; *wall_clock_khz (host) receives the wall clock's
+ * rate, so sum(clocks[2 b]) / sum(clocks[2 b + 1]) * rate is the effective
+ * shader clock. clocks: device, 16-byte aligned, 2 * workgroups entries. */
+RLK_API rlk_status rlk_microbench_mfma_clock(float* sink, int64_t workgroups, int64_t iters,
+                                             int shape, unsigned long long* clocks,
+                                             int64_t* wall_clock_khz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

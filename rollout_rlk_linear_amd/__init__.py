@@ -115,6 +115,9 @@ def load_library(path: str | None = None):
     lib.rlk_microbench_read.restype = ctypes.c_int
     lib.rlk_microbench_mfma.argtypes = [vp, i64, i64, vp]
     lib.rlk_microbench_mfma.restype = ctypes.c_int
+    lib.rlk_microbench_mfma_clock.argtypes = [vp, i64, i64, ctypes.c_int, vp,
+                                              ctypes.POINTER(ctypes.c_int64), vp]
+    lib.rlk_microbench_mfma_clock.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -177,6 +180,19 @@ def microbench_mfma(sink: torch.Tensor, workgroups: int, iters: int) -> float:
         raise ValueError("sink must be a device fp32 tensor of at least 4 elements")
     _check(load_library().rlk_microbench_mfma(_ptr(sink), workgroups, iters, _stream(sink.device)))
     return float(workgroups) * 4 * iters * 32 * 16384
+
+
+def microbench_mfma_clock(sink: torch.Tensor, clocks: torch.Tensor, workgroups: int, iters: int,
+                          shape: int):
+    """Enqueue the clocked MFMA-rate kernel (shape 0: 16x16x32, 1: 32x32x16);
+    clocks: device int64 [2 * workgroups]. Returns (flops, wall-clock kHz)."""
+    if not (clocks.is_cuda and clocks.dtype == torch.int64 and clocks.numel() >= 2 * workgroups):
+        raise ValueError("clocks must be a device int64 tensor of 2 * workgroups entries")
+    khz = ctypes.c_int64(0)
+    _check(load_library().rlk_microbench_mfma_clock(_ptr(sink), workgroups, iters, shape,
+                                                    _ptr(clocks), ctypes.byref(khz),
+                                                    _stream(sink.device)))
+    return float(workgroups) * 4 * iters * 32 * 16384, int(khz.value)
 
 
 def fwd_workspace_bytes(T: int, H: int, V: int) -> int:

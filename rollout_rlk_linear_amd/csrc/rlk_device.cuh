@@ -1,10 +1,11 @@
 // rlk_device.cuh — device building blocks for the gfx950 linear log-prob kernels.
 //
-// * LDS-DMA fed bf16 MFMA mainloops (v_mfma_f32_16x16x32_bf16) computing a
-//   BM x BN fp32 tile with K walked in ascending steps of 32: AsyncGemmP for
-//   two K-contiguous operands (A * B^T), AsyncGemmKN for a K-major B (A * B)
-//   and AsyncGemmKK for two K-major operands (A^T * B), the last two with
-//   fragments assembled by transposing LDS reads.
+// * LDS-DMA fed bf16 MFMA mainloops (v_mfma_f32_16x16x32_bf16, and
+//   v_mfma_f32_32x32x16_bf16 for dH) computing a BM x BN fp32 tile with K
+//   walked in ascending steps of 32: AsyncGemmP for two K-contiguous operands
+//   (A * B^T), AsyncGemmKN for a K-major B (A * B) and AsyncGemmKK for two
+//   K-major operands (A^T * B), the last two with fragments assembled by
+//   transposing LDS reads.
 // * The fixed-order reductions that make every output row independent of the
 //   batch: a 16-lane DPP tree, the (m, R, B, zy) merge algebra, bf16 RNE.
 //
@@ -15,6 +16,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace rlk {
 
@@ -371,31 +374,43 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
 // C[BM x BN] += A[BM x K] * B[K x BN] with A K-contiguous (element (r, k) at
 // A[r * lda + k]) and B K-major (element (k, n) at B[k * ldb + n]): the
 // contraction over the vocabulary, where B is W in its natural layout.
-// A is staged in 64-byte rows, pieces placed by row_slot (accumulator layout
-// as AsyncGemmP). A B stage is 32 rows k of BN columns copied
-// verbatim by LDS-DMA, the 16-byte pieces of row k permuted by XOR with
-// 2 (k % 4) + 8 ((k / 8) % 2), which spreads the transposing reads below
-// over all banks. The MFMA B fragment (lane l: column l % 16, k = 8 (l / 16)
-// .. + 7) comes from two ds_read_b64_tr_b16: inside a 16-lane group, lane i
-// returns element i % 4 of what source lanes i / 4 + 4 j (j = 0..3) point at,
-// so source lane s points at row k0 + s / 4, columns n0 + 4 (s % 4) .. + 3,
-// and lane i receives B[k0 + j][n0 + i], j = 0..3.
-// k runs over [k_begin, k_end) in ascending MFMA steps of 32; the span must
-// be a multiple of 32 and every valid row of A must hold k_end elements.
-// Rows of B at or past kb_valid, and columns at or past nb_valid in its last
-// valid row, read as zero; other columns past nb_valid read whatever follows
-// in memory and only reach output columns the caller discards.
-template <int BM, int BN, int WM, int WN, int NSTG = 4>
+// A is staged in 64-byte rows, pieces placed by row_slot. A B stage is 32
+// rows k of BN columns copied verbatim by LDS-DMA, the 16-byte pieces of row
+// k permuted by XOR with 2 (k % 4) + 8 ((k / 8) % 2), which spreads the
+// transposing reads below over all banks. B fragments come from
+// ds_read_b64_tr_b16: inside a 16-lane group, lane i returns element i % 4 of
+// what source lanes i / 4 + 4 j (j = 0..3) point at, so source lane s points
+// at row k0 + s / 4, columns n0 + 4 (s % 4) .. + 3, and lane i receives
+// B[k0 + j][n0 + i], j = 0..3; two reads make a fragment of 8 k.
+//
+// M32 selects the MFMA: false = v_mfma_f32_16x16x32_bf16 (accumulator layout
+// as AsyncGemmP); true = v_mfma_f32_32x32x16_bf16, two per 32-k stage, which
+// one wave per SIMD issues at the full matrix-core rate (the 16x16x32 form
+// needs two waves per SIMD for that): acc[i][j][e] is element
+// (row wm*WTM + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col wn*WTN + 32 j + lane % 32),
+// the A fragment of k16-step q is row lane % 32, k 16 q + 8 (lane / 32) .. + 7,
+// and the B fragment column lane % 32, the same k.
+// k runs over [k_begin, k_end) in ascending steps of 32 (in two MFMA steps
+// of 16 each with M32); the span must be a multiple of 32 and every valid
+// row of A must hold k_end elements. Rows of B at or past kb_valid, and
+// columns at or past nb_valid in its last valid row, read as zero; other
+// columns past nb_valid read whatever follows in memory and only reach output
+// columns the caller discards.
+template <int BM, int BN, int WM, int WN, int NSTG = 4, bool M32 = false>
 struct AsyncGemmKN {
   static constexpr int NW = WM * WN;
   static_assert(NW == 4, "4 waves per workgroup");
   static_assert(BN == 128 || BN == 256, "B rows of 256 or 512 bytes");
-  static_assert(BM % 16 == 0, "16-row A blocks");
+  static constexpr int FR = M32 ? 32 : 16;  // rows / columns of one MFMA block
+  static_assert(BM % FR == 0, "whole A blocks");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int MI = WTM / 16, NJ = WTN / 16;
+  static constexpr int MI = WTM / FR, NJ = WTN / FR;
+  static_assert(MI >= 1 && NJ >= 1 && WTM % FR == 0 && WTN % FR == 0, "whole MFMA blocks per wave");
   static constexpr int NST = NSTG;
   static_assert(NST == 3 || NST == 4, "3- or 4-slot ring");
   static constexpr int ROWB_A = 64;
@@ -410,17 +425,29 @@ struct AsyncGemmKN {
   static constexpr int NI = NI_A + NI_B;
   static constexpr int NI_W_MAX = (NI + NW - 1) / NW;
   static constexpr int NI_W_MIN = NI / NW;
+  static constexpr int KSUB = M32 ? 2 : 1;  // MFMA steps per 32-k stage
+  typedef typename std::conditional<M32, f32x16, f32x4>::type acc_t;
+  static constexpr int ACC_N = M32 ? 16 : 4;
 
-  f32x4 acc[MI][NJ];
+  acc_t acc[MI][NJ];
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < ACC_N; ++e) acc[i][j][e] = 0.f;
   }
 
   static __device__ __forceinline__ int bswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+  static __device__ __forceinline__ acc_t mfma(const bf16x8& a, const bf16x8& b, const acc_t& c) {
+    if constexpr (M32)
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
 
   __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
                                       int a_rows, const uint16_t* B, int64_t ldb, int kb_valid,
@@ -480,19 +507,32 @@ struct AsyncGemmKN {
       }
     };
 
-    const int foff = (lane & 15) * ROWB_A + 16 * row_slot(lane >> 4, lane & 15);
-    // transposing reads: 16-lane group g, source lane sl; read q covers rows
-    // 8 g + 4 q + sl / 4 at columns n0 + 4 (sl % 4) .. + 3
+    // A fragment offsets (MFMA step q of a stage): row lane % FR of the
+    // block, logical piece lane / 16 (16x16x32) or 2 q + lane / 32 (32x32x16)
+    uint32_t foff[KSUB];
+#pragma unroll
+    for (int q = 0; q < KSUB; ++q) {
+      const int r = lane % FR;
+      const int c = M32 ? 2 * q + (lane >> 5) : (lane >> 4);
+      foff[q] = (uint32_t)(r * ROWB_A + 16 * row_slot(c, r));
+    }
+    // transposing reads: 16-lane group g, source lane sl; read t of MFMA step
+    // q covers rows k0 + 4 t + sl / 4 at columns n0 + 4 (sl % 4) .. + 3, with
+    // (16x16x32) k0 = 8 g, n0 = the block's column; (32x32x16) k0 = 16 q +
+    // 8 (g / 2), n0 = the block's column + 16 (g % 2)
     const int g = lane >> 4, sl = lane & 15;
-    uint32_t boff[2][NJ];
+    uint32_t boff[KSUB][2][NJ];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < KSUB; ++q)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int k = 8 * g + 4 * q + (sl >> 2);
-        const int col = wn * WTN + 16 * j + 4 * (sl & 3);
-        boff[q][j] = (uint32_t)(STAGE_A + k * ROWB_B + 16 * ((col >> 3) ^ bswz(k)) + 2 * (col & 7));
-      }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int k = (M32 ? 16 * q + 8 * (g >> 1) : 8 * g) + 4 * t + (sl >> 2);
+          const int col = wn * WTN + FR * j + (M32 ? 16 * (g & 1) : 0) + 4 * (sl & 3);
+          boff[q][t][j] =
+              (uint32_t)(STAGE_A + k * ROWB_B + 16 * ((col >> 3) ^ bswz(k)) + 2 * (col & 7));
+        }
 
     auto wait_stage = [&](int want, int last) {
       const int after = last - want;
@@ -509,7 +549,7 @@ struct AsyncGemmKN {
 
     // The DMA blocks of the stage being refilled go out one per MFMA row
     // block when they divide evenly (which operand each is: compile time).
-    constexpr bool SPLIT = NI_A % NW == 0 && NI % NW == 0 && NI / NW <= MI;
+    constexpr bool SPLIT = NI_A % NW == 0 && NI % NW == 0 && NI / NW <= MI * KSUB;
     auto issue_block = [&](int ii, uint32_t dst, int k0, const i32x4& rsB) {
       if (ii < NI_A / NW)
         dma16(rsA, dst + 1024u * NW * ii, voff[ii], k0 * 2);
@@ -536,36 +576,40 @@ struct AsyncGemmKN {
       const i32x4 rsB3 = stage_rsrc_b(k3);
       unsigned char* st = lds + (s % NST) * STAGE_BYTES;
       constexpr int A0 = MI < 2 ? MI : 2;
-      bf16x8 af[MI], bfr[NJ];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[0][j]));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[1][j]));
-        bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+      for (int q = 0; q < KSUB; ++q) {
+        bf16x8 af[MI], bfr[NJ];
 #pragma unroll
-      for (int i = 0; i < A0; ++i)
-        af[i] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB_A + foff));
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + A0, 0);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        if (i + A0 < MI)
-          af[i + A0] = __builtin_bit_cast(
-              bf16x8,
-              *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * (i + A0)) * ROWB_A + foff));
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        if (i + A0 < MI) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
+        for (int j = 0; j < NJ; ++j) {
+          const s16x4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[q][0][j]));
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(st + boff[q][1][j]));
+          bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
-        if constexpr (SPLIT) {
-          if (i < NI / NW && refill) issue_block(i, dst, k3, rsB3);
+#pragma unroll
+        for (int i = 0; i < A0; ++i)
+          af[i] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + FR * i) * ROWB_A + foff[q]));
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + A0, 0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          if (i + A0 < MI)
+            af[i + A0] = __builtin_bit_cast(
+                bf16x8,
+                *reinterpret_cast<const u32x4*>(st + (wm * WTM + FR * (i + A0)) * ROWB_A + foff[q]));
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
+          if (i + A0 < MI) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NJ - 1, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
+          }
+          if constexpr (SPLIT) {
+            if (q * MI + i < NI / NW && refill) issue_block(q * MI + i, dst, k3, rsB3);
+          }
         }
       }
     }

@@ -771,12 +771,18 @@ struct SplitMap {
 // Work items (t-tile fastest, then h-tile, then split) are dealt to the 8
 // XCDs in contiguous runs, so one split's G rows and W rows are fetched into
 // one XCD's L2 and reused there.
+// The MFMA is v_mfma_f32_32x32x16_bf16 (one wave per SIMD issues it at the
+// full matrix-core rate); every dH path uses it, so the split partials have
+// the same bits whatever the tile.
+template <int BM, int BN, int WM, int WN, int NSTG>
+using DhGemm = AsyncGemmKN<BM, BN, WM, WN, NSTG, true>;
+
 template <int BM, int BN, int WM, int WN, int NSTG>
 __device__ __forceinline__ void dh_item(unsigned char* lds, const uint16_t* __restrict__ gtv,
                                         int64_t ldg, const uint16_t* __restrict__ weight, int T,
                                         int H, int u0, SplitMap sm, int tt, int ht, int s,
                                         float* __restrict__ part) {
-  using Gm = AsyncGemmKN<BM, BN, WM, WN, NSTG>;
+  using Gm = DhGemm<BM, BN, WM, WN, NSTG>;
   const int row0 = tt * BM, h0 = ht * BN;
   const int q = s / sm.n_sub, j = s - q * sm.n_sub;
   const int a_col = q * sm.Vs_pad + j * sm.split_w - u0;  // chunk buffer column
@@ -789,19 +795,21 @@ __device__ __forceinline__ void dh_item(unsigned char* lds, const uint16_t* __re
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
-  // a 16-column block is whole or absent (H is a multiple of 64): wave-uniform test
+  // a 32-column block is whole or absent (H is a multiple of 64): wave-uniform test
   const int hb = h0 + wn * Gm::WTN;
-  float* const out = part + (int64_t)s * T * H + hb + (lane & 15);
+  float* const out = part + (int64_t)s * T * H + hb + (lane & 31);
+  // accumulator element e of block (i, j): row 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
+  // column 32 j + lane % 32 (each store: 32 lanes x 4 bytes of one row)
 #pragma unroll
   for (int i = 0; i < Gm::MI; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = row0 + wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
+    for (int e = 0; e < 16; ++e) {
+      const int t = row0 + wm * Gm::WTM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       if (t >= T) continue;
       float* rowp = out + (int64_t)t * H;
 #pragma unroll
       for (int j = 0; j < Gm::NJ; ++j)
-        if (hb + 16 * j < H) rowp[16 * j] = gm.acc[i][j][r];
+        if (hb + 32 * j < H) rowp[32 * j] = gm.acc[i][j][e];
     }
   }
 }
@@ -811,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
     const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ weight, int T,
     int H, int u0, SplitMap sm, int n_splits, int split_base, int n_ttiles, int n_htiles,
     int per_xcd, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[AsyncGemmKN<BM, BN, WM, WN>::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[DhGemm<BM, BN, WM, WN, 4>::LDS_BYTES];
   const int seq = blockIdx.x >> 3;
   if (seq >= per_xcd) return;
   const int w = (blockIdx.x & 7) * per_xcd + seq;

@@ -96,10 +96,98 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(float* __restrict__ sink
   if (s == -1.2345e-30f) sink[threadIdx.x & 3] = s;
 }
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// The same back-to-back independent MFMAs in either instruction shape, with
+// the shader clock (clock64: s_memtime) and the constant-rate wall clock
+// (wall_clock64: s_memrealtime) read by lane 0 of wave 0 of every workgroup
+// before and after; their ratio is the effective shader clock of the run.
+// SHAPE 0: v_mfma_f32_16x16x32_bf16, 32 accumulators of 4 floats
+// (32 x 16384 flops a round);
+// SHAPE 1: v_mfma_f32_32x32x16_bf16, 16 accumulators of 16 floats
+// (16 x 32768 flops a round: the same flops).
+template <int SHAPE>
+__global__ __launch_bounds__(kThreads) void mfma_clock_kernel(float* __restrict__ sink, int iters,
+                                                              unsigned long long* __restrict__ clk) {
+  const int lane = threadIdx.x & 63;
+  u32x4 ra, rb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ra[e] = 0x3c003c00u ^ (uint32_t)((lane * 2654435761u + e) & 0x007f007fu);
+    rb[e] = 0x3c803c80u ^ (uint32_t)((lane * 40503u + 3 * e) & 0x007f007fu);
+  }
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ra), b = __builtin_bit_cast(bf16x8, rb);
+  const bool timer = threadIdx.x == 0;
+  unsigned long long c0 = 0, w0 = 0;
+  if (timer) {
+    c0 = clock64();
+    w0 = wall_clock64();
+  }
+  float s = 0.f;
+  if constexpr (SHAPE == 0) {
+    f32x4 acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  } else {
+    f32x16 acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += acc[j][e];
+  }
+  if (timer) {
+    // the accumulators feed s, so the reads below come after the MFMAs
+    asm volatile("" ::"v"(s));
+    const unsigned long long c1 = clock64(), w1 = wall_clock64();
+    clk[2 * blockIdx.x] = c1 - c0;
+    clk[2 * blockIdx.x + 1] = w1 - w0;
+  }
+  if (s == -1.2345e-30f) sink[threadIdx.x & 3] = s;
+}
+
 }  // namespace
 }  // namespace rlk
 
 extern "C" {
+
+RLK_API rlk_status rlk_microbench_mfma_clock(float* sink, int64_t workgroups, int64_t iters,
+                                             int shape, unsigned long long* clocks,
+                                             int64_t* wall_clock_khz, void* stream) {
+  if (!sink || (reinterpret_cast<uintptr_t>(sink) % 16) || !clocks ||
+      (reinterpret_cast<uintptr_t>(clocks) % 16) || !wall_clock_khz || workgroups < 1 ||
+      workgroups > (1 << 20) || iters < 1 || iters > (1 << 24) || (shape != 0 && shape != 1))
+    return RLK_ERR_INVALID_ARG;
+  const int s = rlk::check_device_status();
+  if (s != RLK_OK) return (rlk_status)s;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return RLK_ERR_HIP;
+  *wall_clock_khz = khz;
+  if (shape == 0)
+    hipLaunchKernelGGL(rlk::mfma_clock_kernel<0>, dim3((unsigned)workgroups), dim3(rlk::kThreads), 0,
+                       static_cast<hipStream_t>(stream), sink, (int)iters, clocks);
+  else
+    hipLaunchKernelGGL(rlk::mfma_clock_kernel<1>, dim3((unsigned)workgroups), dim3(rlk::kThreads), 0,
+                       static_cast<hipStream_t>(stream), sink, (int)iters, clocks);
+  return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
 
 RLK_API rlk_status rlk_microbench_copy(void* dst, const void* src, size_t bytes, void* stream) {
   if (!dst || !src || bytes == 0 || (bytes % 16) != 0 || bytes > (size_t(1) << 40))

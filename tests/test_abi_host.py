@@ -120,6 +120,17 @@ def test_microbench_argument_errors():
     assert raw.rlk_microbench_read(Q, 8192, NULL, 256, NULL) == INVALID
     assert raw.rlk_microbench_read(Q, 8192, P, 0, NULL) == INVALID
     assert raw.rlk_microbench_read(ctypes.c_void_p((1 << 21) + 8), 8192, P, 256, NULL) == INVALID
+    raw.rlk_microbench_mfma_clock.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
+    khz = ctypes.c_int64(0)
+    mc = raw.rlk_microbench_mfma_clock
+    assert mc(NULL, 256, 10, 0, Q, ctypes.byref(khz), NULL) == INVALID
+    assert mc(P, 256, 10, 2, Q, ctypes.byref(khz), NULL) == INVALID        # unknown shape
+    assert mc(P, 256, 10, 1, NULL, ctypes.byref(khz), NULL) == INVALID     # no clock buffer
+    assert mc(P, 256, 10, 1, Q, None, NULL) == INVALID                     # no rate output
+    assert mc(P, 0, 10, 0, Q, ctypes.byref(khz), NULL) == INVALID
+    assert mc(P, 256, 0, 0, Q, ctypes.byref(khz), NULL) == INVALID
 
 
 def test_provenance(lib):
