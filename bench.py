@@ -377,9 +377,22 @@ def workload_runs(torch, rlk, wl, read_gbs, steps):
                                          rlk.lora_bwd(x, W, A, B, dy, 2.0, ws=ws)), 3, steps)
         mf, mb = median_ci(per_f), median_ci(per_b)
         wbytes = 2 * c.N * c.K
+        # algorithmic work of the forward: every operand read once, y written once
+        fbytes = wbytes + 2 * c.r * (c.K + c.N) + 2 * c.T * c.K + 2 * c.T * c.N
+        fflops = 2 * c.T * c.K * c.N + 2 * c.T * c.r * (c.K + c.N)
+        secs = mf["median"] * 1e-3
+        ai = fflops / fbytes
+        bound = "mfma" if ai >= RIDGE else "hbm"
+        achieved = (fflops / secs / 1e12) if bound == "mfma" else (fbytes / secs / 1e9)
+        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
         lora[c.name] = {"rank": c.r, "fwd_ms": mf, "fwd_bwd_ms": mb,
-                        "fwd_W_GBps": round(wbytes / (mf["median"] * 1e-3) / 1e9, 1),
-                        "fwd_TFLOPs": round(2 * c.T * c.K * c.N / (mf["median"] * 1e-3) / 1e12, 2)}
+                        "fwd_W_GBps": round(wbytes / secs / 1e9, 1),
+                        "fwd_TFLOPs": round(2 * c.T * c.K * c.N / secs / 1e12, 2),
+                        "fwd_roofline": {"bound": bound, "bytes": fbytes, "flops": fflops,
+                                         "flop_per_byte": round(ai, 1),
+                                         "achieved": round(achieved, 1),
+                                         "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                                         "peak": peak, "frac": round(achieved / peak, 4)}}
     res["lora_gate_shapes"] = lora
     return res
 
@@ -440,13 +453,14 @@ def main():
                     help="only the T=512 step (no microbenchmarks, other workloads or clocks)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--profile-case", choices=["fwd_t1", "fwd_t64", "fwd_packed_t1", "fwd_packed_t64", "read",
-                                               "mfma16", "mfma32"],
+                                               "mfma16", "mfma32", "lora"],
                     default=None,
                     help="run only this case's calls (warmup + steps), for profilers: fwd_t1 / _t64 = "
                          "the forward of 1 / 64 rows over the full vocabulary (natural layout), "
                          "fwd_packed_t1 / _t64 = the same over the packed weight with 1 / 64 rows, "
                          "read = the 1 GiB streaming-read microbenchmark, mfma16 / mfma32 = the "
-                         "clocked MFMA-rate kernel in the 16x16x32 / 32x32x16 shape")
+                         "clocked MFMA-rate kernel in the 16x16x32 / 32x32x16 shape, lora = the "
+                         "LoRA-linear forward and backward on the runtime report's three shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -483,6 +497,14 @@ def main():
         ncu = torch.cuda.get_device_properties(0).multi_processor_count
         per, _ = timed(torch, lambda: rlk.microbench_read(src, sink, ncu), args.warmup, args.steps)
         print(json.dumps({"profile_case": "read", "ms": median_ci(per)}), flush=True)
+        return
+    if args.profile_case == "lora":
+        for lc in wl.lora_page_cases():
+            x, W, A, B, dy = (t.to("cuda:0").contiguous() for t in (lc.x, lc.W, lc.A, lc.B, lc.dy))
+            per, _ = timed(torch, lambda: (rlk.lora_fwd(x, W, A, B, 2.0),
+                                           rlk.lora_bwd(x, W, A, B, dy, 2.0)), args.warmup, args.steps)
+            print(json.dumps({"profile_case": "lora", "shape": lc.name, "fwd_bwd_ms": median_ci(per)}),
+                  flush=True)
         return
     if args.profile_case in ("mfma16", "mfma32"):
         ncu = torch.cuda.get_device_properties(0).multi_processor_count

@@ -19,12 +19,26 @@ namespace {
 
 constexpr int kLoraBM = 64;    // rows (tokens) per tile
 constexpr int kLoraBN = 128;   // output columns per tile
+constexpr int kLoraBNm = 64;   // output columns per tile when wide tiles leave CUs idle
+constexpr int kLoraBNs = 32;   // ... and when 64-column ones still do
 constexpr int kLoraMaxRank = 64;
-using LoraFwdGemm = AsyncGemmP<kLoraBM, kLoraBN, 2, 2>;
+template <int BN>
+using LoraFwdGemm = AsyncGemmP<kLoraBM, BN, 2, 2>;
 using LoraDxGemm = AsyncGemmKN<kLoraBM, kLoraBN, 2, 2, 4>;
-static_assert((kLoraBM + kLoraBN) * kLoraMaxRank * 4 <= LoraFwdGemm::LDS_BYTES &&
+static_assert((kLoraBM + kLoraBN) * kLoraMaxRank * 4 <= LoraFwdGemm<kLoraBN>::LDS_BYTES &&
+                  (kLoraBM + kLoraBNm) * kLoraMaxRank * 4 <= LoraFwdGemm<kLoraBNm>::LDS_BYTES &&
+                  (kLoraBM + kLoraBNs) * kLoraMaxRank * 4 <= LoraFwdGemm<kLoraBNs>::LDS_BYTES &&
                   (kLoraBM + kLoraBN) * kLoraMaxRank * 4 <= LoraDxGemm::LDS_BYTES,
               "the adapter operands of a tile fit the freed ring");
+
+// Splits of the forward's contraction over K: fixed by K alone (never by T,
+// so every row's arithmetic is the same whatever the batch), about one per
+// 1280 features, at most 4, each a multiple of 64.
+inline int lora_ksplit(int64_t K) {
+  for (int S = 4; S > 1; S /= 2)
+    if (K >= 1280 * S && K % (64 * S) == 0) return S;
+  return 1;
+}
 
 // out[t][j] = sum_{i < L} P[t][i] Q(j, i) in fp32 for the T x r pairs, one
 // wave per pair: lane l sums (fused multiply-adds) elements 8 l + 512 m + e,
@@ -68,10 +82,10 @@ __global__ __launch_bounds__(kThreads) void lora_rowdot_kernel(const uint16_t* _
   if (lane == 0) out[w] = acc;
 }
 
-// Epilogue of a 64 x 128 tile: out = bf16(acc + s * sum_j c[row][j] f[j][col]),
+// Epilogue of a 64 x BN tile: out = bf16(acc + s * sum_j c[row][j] f[j][col]),
 // c = the rows' rank-r codes (fp32 [T][r]), f = the adapter factor's columns
 // (bf16, element (j, col) at F[col * fcs + j * fjs]). The ring is free on entry.
-template <class Gm>
+template <int BN, class Gm>
 __device__ __forceinline__ void lora_epilogue(const Gm& gm, unsigned char* lds,
                                               const float* __restrict__ code,
                                               const uint16_t* __restrict__ F, int64_t fcs,
@@ -79,13 +93,13 @@ __device__ __forceinline__ void lora_epilogue(const Gm& gm, unsigned char* lds,
                                               int row0, int col0, uint16_t* __restrict__ out,
                                               int64_t ldo) {
   float* cs = reinterpret_cast<float*>(lds);  // [r][64]
-  float* fs = cs + kLoraBM * r;               // [r][128]
+  float* fs = cs + kLoraBM * r;               // [r][BN]
   for (int i = threadIdx.x; i < kLoraBM * r; i += kThreads) {
     const int j = i / kLoraBM, rr = i - j * kLoraBM;
     cs[i] = row0 + rr < T ? code[(int64_t)(row0 + rr) * r + j] : 0.f;
   }
-  for (int i = threadIdx.x; i < kLoraBN * r; i += kThreads) {
-    const int j = i / kLoraBN, c = i - j * kLoraBN;
+  for (int i = threadIdx.x; i < BN * r; i += kThreads) {
+    const int j = i / BN, c = i - j * BN;
     fs[i] = col0 + c < ncols ? bf16_to_f32(F[(int64_t)(col0 + c) * fcs + (int64_t)j * fjs]) : 0.f;
   }
   __syncthreads();
@@ -101,7 +115,7 @@ __device__ __forceinline__ void lora_epilogue(const Gm& gm, unsigned char* lds,
       for (int jn = 0; jn < Gm::NJ; ++jn) {
         const int col = wn * Gm::WTN + 16 * jn + (lane & 15);
         float term = 0.f;
-        for (int j = 0; j < r; ++j) term = fmaf(cs[j * kLoraBM + row], fs[j * kLoraBN + col], term);
+        for (int j = 0; j < r; ++j) term = fmaf(cs[j * kLoraBM + row], fs[j * BN + col], term);
         const float o = gm.acc[i][jn][rr] + scale * term;
         if (row0 + row < T && col0 + col < ncols)
           out[(int64_t)(row0 + row) * ldo + col0 + col] = (uint16_t)f32_to_bf16_rne(o);
@@ -109,34 +123,147 @@ __device__ __forceinline__ void lora_epilogue(const Gm& gm, unsigned char* lds,
     }
 }
 
-// y tile (64 tokens x 128 outputs): x W^T on the MFMA mainloop, then + s u B^T.
+// y tile (64 tokens x BN outputs): x W^T on the MFMA mainloop, then + s u B^T.
+// With S > 1 splits of K the tile covers K split ks and writes its fp32
+// partial to part[ks][t][n] instead (lora_fwd_reduce_kernel finishes y).
+template <int BN>
 __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const float* __restrict__ u,
     const uint16_t* __restrict__ B, int T, int K, int N, int r, float scale, int n_ttiles,
-    uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LoraFwdGemm::LDS_BYTES];
-  const int tt = (int)blockIdx.x % n_ttiles, nt = (int)blockIdx.x / n_ttiles;
-  const int row0 = tt * kLoraBM, col0 = nt * kLoraBN;
-  LoraFwdGemm gm;
+    int n_ntiles, int S, uint16_t* __restrict__ y, float* __restrict__ part) {
+  using Gm = LoraFwdGemm<BN>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
+  const int tt = (int)blockIdx.x % n_ttiles, rest = (int)blockIdx.x / n_ttiles;
+  const int nt = rest % n_ntiles, ks = rest / n_ntiles;
+  const int row0 = tt * kLoraBM, col0 = nt * BN;
+  const int Ks = K / S;
+  Gm gm;
   gm.zero();
-  gm.run(lds, x + (int64_t)row0 * K, K, T - row0, W + (int64_t)col0 * K, K, N - col0, 0, K);
-  // run() ends on a barrier: the ring is free. B's column n holds B[n][0..r-1].
-  lora_epilogue(gm, lds, u, B, r, 1, T, N, r, scale, row0, col0, y, N);
+  gm.run(lds, x + (int64_t)row0 * K, K, T - row0, W + (int64_t)col0 * K, K, N - col0, ks * Ks,
+         (ks + 1) * Ks);
+  if (S == 1) {
+    // run() ends on a barrier: the ring is free. B's column n holds B[n][0..r-1].
+    lora_epilogue<BN>(gm, lds, u, B, r, 1, T, N, r, scale, row0, col0, y, N);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave % 2, wn = wave / 2;
+  float* out = part + (int64_t)ks * T * N;
+#pragma unroll
+  for (int i = 0; i < Gm::MI; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = row0 + wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + rr;
+#pragma unroll
+      for (int jn = 0; jn < Gm::NJ; ++jn) {
+        const int col = col0 + wn * Gm::WTN + 16 * jn + (lane & 15);
+        if (row < T && col < N) out[(int64_t)row * N + col] = gm.acc[i][jn][rr];
+      }
+    }
+}
+
+// y = bf16((part_0 + part_1 + ...) + s sum_j u[t][j] B[n][j]): workgroup b
+// covers outputs 256 (b % nb) .. of row b / nb (nb = ceil(N / 256)), one a
+// thread, the adapter term as the epilogue's fused multiply-add chain.
+__global__ __launch_bounds__(kThreads) void lora_fwd_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ u, const uint16_t* __restrict__ B,
+    int T, int N, int r, int S, float scale, uint16_t* __restrict__ y) {
+  const int nb = (N + kThreads - 1) / kThreads;
+  const int t = (int)blockIdx.x / nb;
+  const int n = ((int)blockIdx.x - t * nb) * kThreads + (int)threadIdx.x;
+  if (n >= N) return;
+  const int64_t n_el = (int64_t)T * N;
+  const int64_t i = (int64_t)t * N + n;
+  float acc = part[i];
+  for (int ks = 1; ks < S; ++ks) acc = acc + part[(int64_t)ks * n_el + i];
+  const float* ut = u + (int64_t)t * r;
+  const uint16_t* Bn = B + (int64_t)n * r;
+  // the same ascending chain, its operands loaded four at a time ahead of it
+  float term = 0.f;
+  int j = 0;
+  for (; j + 4 <= r; j += 4) {
+    float uu[4], bb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uu[e] = ut[j + e];
+      bb[e] = bf16_to_f32(Bn[j + e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) term = fmaf(uu[e], bb[e], term);
+  }
+  for (; j < r; ++j) term = fmaf(ut[j], bf16_to_f32(Bn[j]), term);
+  y[i] = (uint16_t)f32_to_bf16_rne(acc + scale * term);
 }
 
 // dx tile (64 tokens x 128 input features): dy W on the transposing mainloop,
-// then + s v A with v = dy B. A's column k holds A[0..r-1][k].
+// then + s v A with v = dy B. A's column k holds A[0..r-1][k]. With S > 1
+// splits of the contraction over N (fixed by N alone) the tile covers split
+// ns and writes its fp32 partial to part[ns][t][k]; lora_dx_reduce_kernel
+// finishes dx.
 __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ W, const float* __restrict__ v,
     const uint16_t* __restrict__ A, int T, int K, int N, int r, float scale, int n_ttiles,
-    uint16_t* __restrict__ dx) {
+    int n_ktiles, int S, uint16_t* __restrict__ dx, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[LoraDxGemm::LDS_BYTES];
-  const int tt = (int)blockIdx.x % n_ttiles, kt = (int)blockIdx.x / n_ttiles;
+  const int tt = (int)blockIdx.x % n_ttiles, rest = (int)blockIdx.x / n_ttiles;
+  const int kt = rest % n_ktiles, ns = rest / n_ktiles;
   const int row0 = tt * kLoraBM, c0 = kt * kLoraBN;
+  const int Ns = N / S;
   LoraDxGemm gm;
   gm.zero();
-  gm.run(lds, dy + (int64_t)row0 * N, N, T - row0, W + c0, K, N, min(kLoraBN, K - c0), 0, N);
-  lora_epilogue(gm, lds, v, A, 1, K, T, K, r, scale, row0, c0, dx, K);
+  gm.run(lds, dy + (int64_t)row0 * N, N, T - row0, W + c0, K, N, min(kLoraBN, K - c0), ns * Ns,
+         (ns + 1) * Ns);
+  if (S == 1) {
+    lora_epilogue<kLoraBN>(gm, lds, v, A, 1, K, T, K, r, scale, row0, c0, dx, K);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave % 2, wn = wave / 2;
+  float* out = part + (int64_t)ns * T * K;
+#pragma unroll
+  for (int i = 0; i < LoraDxGemm::MI; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = row0 + wm * LoraDxGemm::WTM + 16 * i + 4 * (lane >> 4) + rr;
+#pragma unroll
+      for (int jn = 0; jn < LoraDxGemm::NJ; ++jn) {
+        const int col = c0 + wn * LoraDxGemm::WTN + 16 * jn + (lane & 15);
+        if (row < T && col < K) out[(int64_t)row * K + col] = gm.acc[i][jn][rr];
+      }
+    }
+}
+
+// dx = bf16((part_0 + part_1 + ...) + s sum_j v[t][j] A[j][k]), as
+// lora_fwd_reduce_kernel with the code v and the factor A (column k holds
+// A[0..r-1][k] at stride K).
+__global__ __launch_bounds__(kThreads) void lora_dx_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ v, const uint16_t* __restrict__ A,
+    int T, int K, int r, int S, float scale, uint16_t* __restrict__ dx) {
+  const int nb = (K + kThreads - 1) / kThreads;
+  const int t = (int)blockIdx.x / nb;
+  const int k = ((int)blockIdx.x - t * nb) * kThreads + (int)threadIdx.x;
+  if (k >= K) return;
+  const int64_t n_el = (int64_t)T * K;
+  const int64_t i = (int64_t)t * K + k;
+  float acc = part[i];
+  for (int ks = 1; ks < S; ++ks) acc = acc + part[(int64_t)ks * n_el + i];
+  const float* vt = v + (int64_t)t * r;
+  float term = 0.f;
+  int j = 0;
+  for (; j + 4 <= r; j += 4) {
+    float vv[4], aa[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vv[e] = vt[j + e];
+      aa[e] = bf16_to_f32(A[(int64_t)(j + e) * K + k]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) term = fmaf(vv[e], aa[e], term);
+  }
+  for (; j < r; ++j) term = fmaf(vt[j], bf16_to_f32(A[(int64_t)j * K + k]), term);
+  dx[i] = (uint16_t)f32_to_bf16_rne(acc + scale * term);
 }
 
 // dA[j][k] = s * (fused multiply-add chain over t ascending of v[t][j] x[t][k]).
@@ -147,9 +274,20 @@ __global__ __launch_bounds__(kThreads) void lora_da_kernel(const float* __restri
   const int k = (int)blockIdx.x * kThreads + threadIdx.x;
   const int j = (int)blockIdx.y;
   if (k >= K) return;
+  // the ascending chain, its operands loaded eight at a time ahead of it
   float acc = 0.f;
-  for (int t = 0; t < T; ++t)
-    acc = fmaf(v[(int64_t)t * r + j], bf16_to_f32(x[(int64_t)t * K + k]), acc);
+  int t = 0;
+  for (; t + 8 <= T; t += 8) {
+    float a[8], b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = v[(int64_t)(t + e) * r + j];
+      b[e] = bf16_to_f32(x[(int64_t)(t + e) * K + k]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
+  }
+  for (; t < T; ++t) acc = fmaf(v[(int64_t)t * r + j], bf16_to_f32(x[(int64_t)t * K + k]), acc);
   da[(int64_t)j * K + k] = scale * acc;
 }
 
@@ -161,9 +299,20 @@ __global__ __launch_bounds__(kThreads) void lora_db_kernel(const uint16_t* __res
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= (int64_t)N * r) return;
   const int n = (int)(i / r), j = (int)(i - (int64_t)n * r);
+  // the ascending chain, its operands loaded eight at a time ahead of it
   float acc = 0.f;
-  for (int t = 0; t < T; ++t)
-    acc = fmaf(bf16_to_f32(dy[(int64_t)t * N + n]), u[(int64_t)t * r + j], acc);
+  int t = 0;
+  for (; t + 8 <= T; t += 8) {
+    float a[8], b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = bf16_to_f32(dy[(int64_t)(t + e) * N + n]);
+      b[e] = u[(int64_t)(t + e) * r + j];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
+  }
+  for (; t < T; ++t) acc = fmaf(bf16_to_f32(dy[(int64_t)t * N + n]), u[(int64_t)t * r + j], acc);
   db[i] = scale * acc;
 }
 
@@ -179,7 +328,16 @@ rlk_status lora_shape(int64_t T, int64_t K, int64_t N, int64_t r) {
   return RLK_OK;
 }
 
-size_t lora_ws(int64_t T, int64_t r) { return (size_t(2) * T * r * 4 + 255) / 256 * 256; }
+// u and v (fp32 [T][r] each), then the split partials: the forward's
+// (fp32 [S][T][N], S = lora_ksplit(K)) or dx's (fp32 [S'][T][K], S' =
+// lora_ksplit(N)), whichever is larger.
+size_t lora_ws(int64_t T, int64_t K, int64_t N, int64_t r) {
+  const int S = lora_ksplit(K), Sx = lora_ksplit(N);
+  const size_t uv = (size_t(2) * T * r * 4 + 255) / 256 * 256;
+  const size_t pf = S > 1 ? size_t(S) * T * N * 4 : 0;
+  const size_t px = Sx > 1 ? size_t(Sx) * T * K * 4 : 0;
+  return uv + ((pf > px ? pf : px) + 255) / 256 * 256;
+}
 
 }  // namespace
 }  // namespace rlk
@@ -188,7 +346,7 @@ extern "C" {
 
 RLK_API size_t rlk_lora_linear_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
   if (T <= 0 || rlk::lora_shape(T, K, N, r) != RLK_OK) return 0;
-  return rlk::lora_ws(T, r);
+  return rlk::lora_ws(T, K, N, r);
 }
 
 RLK_API rlk_status rlk_lora_linear_fwd(const void* x, const void* weight, const void* lora_a,
@@ -202,7 +360,7 @@ RLK_API rlk_status rlk_lora_linear_fwd(const void* x, const void* weight, const 
   if (!rlk::al16(x) || !rlk::al16(weight) || !rlk::al16(lora_a) || !rlk::al16(lora_b) ||
       !rlk::al16(y) || !rlk::al16(workspace))
     return RLK_ERR_INVALID_ARG;
-  if (workspace_bytes < rlk::lora_ws(T, r)) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < rlk::lora_ws(T, K, N, r)) return RLK_ERR_WORKSPACE_TOO_SMALL;
   s = (rlk_status)rlk::check_device_status();
   if (s != RLK_OK) return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -211,12 +369,35 @@ RLK_API rlk_status rlk_lora_linear_fwd(const void* x, const void* weight, const 
   const auto* Ab = static_cast<const uint16_t*>(lora_a);
   const auto* Bb = static_cast<const uint16_t*>(lora_b);
   float* u = static_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         (size_t(2) * T * r * 4 + 255) / 256 * 256);
   hipLaunchKernelGGL(rlk::lora_rowdot_kernel<true>, dim3(rlk::cdiv_i(T * r, 4)), dim3(rlk::kThreads),
                      0, st, xb, Ab, (int)T, (int)K, (int)r, u);
   const int nt = rlk::cdiv_i(T, rlk::kLoraBM);
-  hipLaunchKernelGGL(rlk::lora_fwd_kernel, dim3(nt * rlk::cdiv_i(N, rlk::kLoraBN)),
-                     dim3(rlk::kThreads), 0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r,
-                     scale, nt, static_cast<uint16_t*>(y));
+  const int S = rlk::lora_ksplit(K);
+  uint16_t* yb = static_cast<uint16_t*>(y);
+  // narrower tiles when the wide ones would leave most compute units idle
+  // (the tile width does not change any element's arithmetic)
+  if ((int64_t)nt * rlk::cdiv_i(N, rlk::kLoraBN) * S >= 256) {
+    const int nn = rlk::cdiv_i(N, rlk::kLoraBN);
+    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBN>, dim3(nt * nn * S), dim3(rlk::kThreads),
+                       0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r, scale, nt, nn, S, yb,
+                       part);
+  } else if ((int64_t)nt * rlk::cdiv_i(N, rlk::kLoraBNm) * S >= 256) {
+    const int nn = rlk::cdiv_i(N, rlk::kLoraBNm);
+    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBNm>, dim3(nt * nn * S), dim3(rlk::kThreads),
+                       0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r, scale, nt, nn, S, yb,
+                       part);
+  } else {
+    const int nn = rlk::cdiv_i(N, rlk::kLoraBNs);
+    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBNs>, dim3(nt * nn * S), dim3(rlk::kThreads),
+                       0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r, scale, nt, nn, S, yb,
+                       part);
+  }
+  if (S > 1)
+    hipLaunchKernelGGL(rlk::lora_fwd_reduce_kernel, dim3(T * rlk::cdiv_i(N, rlk::kThreads)),
+                       dim3(rlk::kThreads), 0, st, part, u, Bb, (int)T, (int)N, (int)r, S, scale,
+                       yb);
   return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 
@@ -242,7 +423,7 @@ RLK_API rlk_status rlk_lora_linear_bwd(const void* x, const void* weight, const 
   if (!rlk::al16(x) || !rlk::al16(weight) || !rlk::al16(lora_a) || !rlk::al16(lora_b) ||
       !rlk::al16(dy) || !rlk::al16(workspace))
     return RLK_ERR_INVALID_ARG;
-  if (workspace_bytes < rlk::lora_ws(T, r)) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < rlk::lora_ws(T, K, N, r)) return RLK_ERR_WORKSPACE_TOO_SMALL;
   s = (rlk_status)rlk::check_device_status();
   if (s != RLK_OK) return s;
   const auto* xb = static_cast<const uint16_t*>(x);
@@ -261,9 +442,17 @@ RLK_API rlk_status rlk_lora_linear_bwd(const void* x, const void* weight, const 
                        (int)T, (int)K, (int)r, u);
   if (dx) {
     const int nt = rlk::cdiv_i(T, rlk::kLoraBM);
-    hipLaunchKernelGGL(rlk::lora_dx_kernel, dim3(nt * rlk::cdiv_i(K, rlk::kLoraBN)),
-                       dim3(rlk::kThreads), 0, st, dyb, Wb, v, Ab, (int)T, (int)K, (int)N, (int)r,
-                       scale, nt, static_cast<uint16_t*>(dx));
+    const int nk = rlk::cdiv_i(K, rlk::kLoraBN);
+    const int Sx = rlk::lora_ksplit(N);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           (size_t(2) * T * r * 4 + 255) / 256 * 256);
+    hipLaunchKernelGGL(rlk::lora_dx_kernel, dim3(nt * nk * Sx), dim3(rlk::kThreads), 0, st, dyb,
+                       Wb, v, Ab, (int)T, (int)K, (int)N, (int)r, scale, nt, nk, Sx,
+                       static_cast<uint16_t*>(dx), part);
+    if (Sx > 1)
+      hipLaunchKernelGGL(rlk::lora_dx_reduce_kernel, dim3(T * rlk::cdiv_i(K, rlk::kThreads)),
+                         dim3(rlk::kThreads), 0, st, part, v, Ab, (int)T, (int)K, (int)r, Sx, scale,
+                         static_cast<uint16_t*>(dx));
   }
   if (da)
     hipLaunchKernelGGL(rlk::lora_da_kernel, dim3(rlk::cdiv_i(K, rlk::kThreads), (unsigned)r),

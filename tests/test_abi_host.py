@@ -288,7 +288,12 @@ def test_lora_bwd_argument_errors(lib, kw, code):
 
 def test_lora_workspace_and_empty_forward(lib):
     f = lib.rlk_lora_linear_workspace_bytes
-    assert f(33, 5120, 5120, 16) == 4352          # u and v: 2 x 33 x 16 fp32, rounded to 256
+    # u and v: 2 x 33 x 16 fp32, rounded to 256; K = 5120 splits the forward's
+    # contraction in 4: partials 4 x 33 x 5120 fp32
+    assert f(33, 5120, 5120, 16) == 4352 + 4 * 33 * 5120 * 4
+    assert f(33, 1024, 2048, 16) == 4352          # K, N < 2560: no split
+    # dx's contraction over N = 8192 splits in 4: partials 4 x 33 x 1024 fp32
+    assert f(33, 1024, 8192, 16) == 4352 + 4 * 33 * 1024 * 4
     assert f(0, 64, 64, 16) == 0 and f(4, 96, 64, 16) == 0
     assert lora_fwd(lib, T=0, x=NULL, y=NULL, ws=NULL, nws=0) == OK
 

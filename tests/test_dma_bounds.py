@@ -94,8 +94,8 @@ def model_gemm_p(BM, BN, lda, ldb, a_rows, b_rows, k_begin, k_end, rows_in_scala
 
 
 # (BM, BN): fwd_tile and the large-batch recompute, the small-batch
-# recompute, the LoRA forward
-GEMM_P = [(256, 256), (32, 128), (64, 128)]
+# recompute, the LoRA forward (wide and narrow tiles)
+GEMM_P = [(256, 256), (32, 128), (64, 128), (64, 32)]
 
 
 @pytest.mark.parametrize("BM,BN", GEMM_P)
@@ -106,6 +106,14 @@ def test_gemm_p_reads_only_valid_rows(BM, BN, a_rows, b_rows, H):
     fa, fb = model_gemm_p(BM, BN, H, H, a_rows, b_rows, 0, H)
     check_k_contiguous(fa, min(a_rows, BM), H, 0, H, f"A {BM}x{BN} rows={a_rows}")
     check_k_contiguous(fb, min(b_rows, BN), H, 0, H, f"B {BM}x{BN} rows={b_rows}")
+
+
+@pytest.mark.parametrize("k_begin,k_end", [(0, 128), (128, 256), (64, 192)])
+def test_gemm_p_k_split_reads_only_its_range(k_begin, k_end):
+    # the LoRA forward's split contraction: k over [k_begin, k_end) of H = 256
+    fa, fb = model_gemm_p(64, 32, 256, 256, 33, 20, k_begin, k_end)
+    check_k_contiguous(fa, 33, 256, k_begin, k_end, "A split")
+    check_k_contiguous(fb, 20, 256, k_begin, k_end, "B split")
 
 
 def test_gemm_p_planted_scalar_row_offsets_are_caught():

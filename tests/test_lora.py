@@ -104,6 +104,30 @@ def test_rows_independent_bitwise():
     assert bits_equal(yp, y[p])
 
 
+@pytest.mark.parametrize("N,K,T,sub", [(4096, 4096, 600, [(0, 1), (7, 40), (300, 364)]),
+                                       (256, 8192, 70, [(0, 3), (64, 70)]),
+                                       (8192, 2560, 20, [(0, 1), (5, 9)])])
+def test_split_k_and_tile_width_keep_rows_bitwise(N, K, T, sub):
+    # K >= 2560 splits the forward's contraction (2 splits at 4096, 4 at 8192:
+    # fixed by K alone) and N >= 2560 splits dx's (over N, fixed by N alone).
+    # The first shape has enough tiles for 128-column forward tiles, its
+    # sub-batches run 64- or 32-column ones; every row's bits must agree, and
+    # the values stay correctly rounded up to the accumulation bound.
+    c = wl.lora_case(N, K, T, 70 + K // 1024, r=16)
+    x, W, A, B, dy, y, dx, _, _ = run(c, 1.5)
+    f = lora_forward(c.x, c.W, c.A, c.B, 1.5)
+    rounding_check(y, f["y"], abs_terms_y(c, 1.5), K + 16 + 4, f"y N={N} K={K}")
+    g = lora_backward(c.x, c.W, c.A, c.B, c.dy, 1.5)
+    rounding_check(dx, g["dx"], abs_terms_dx(c, 1.5), N + 16 + 4, f"dx N={N} K={K}")
+    for r0, r1 in sub:
+        ys = rlk.lora_fwd(x[r0:r1].contiguous(), W, A, B, 1.5)
+        dxs, _, _ = rlk.lora_bwd(x[r0:r1].contiguous(), W, A, B, dy[r0:r1].contiguous(), 1.5,
+                                 want_da=False, want_db=False)
+        torch.cuda.synchronize()
+        assert bits_equal(ys, y[r0:r1]), f"y rows {r0}:{r1} (N={N} K={K})"
+        assert bits_equal(dxs, dx[r0:r1]), f"dx rows {r0}:{r1} (N={N} K={K})"
+
+
 def test_repeatable_and_base_frozen():
     c = wl.lora_page_cases()[2]  # N5120 K5120 T33
     x, W, A, B, dy = (dev(t) for t in (c.x, c.W, c.A, c.B, c.dy))
