@@ -241,28 +241,36 @@ __device__ __forceinline__ void barrier_only() {
 // k-steps are staged in pairs: a slot holds 128 bytes of each operand row
 // (two k-steps), so each group of eight 16-byte DMA pieces of a row is one
 // whole 128-byte line and every L2 request carries a full line (with
-// 64-byte rows each line takes two requests; with W streaming from HBM the
-// number of requests in flight per CU is what bounds the copy rate). Two
-// slots: the pair after the one being multiplied is in flight, its DMA
-// blocks issued between the first k-step's MFMAs. The 16-byte pieces of row
-// r are rotated by r (slot = (piece + r) mod 8), which keeps the 16-row
-// fragment reads of both k-steps free of bank conflicts. Within a k-step all B fragments and two A
-// fragments are read first, then A fragment i+2 is read while the MFMAs of
-// row block i run (scheduling group barriers pin the order).
-template <int BM, int BN, int WM, int WN>
+// 64-byte rows each line takes two requests). A has a ring of two pair slots
+// and B one of NSB (2 or 3): with 3, B's pair p + 2 is in flight while pair
+// p is multiplied, so the operand that streams from HBM (W) has twice the
+// lookahead of the one that stays in L2 (hidden) within the same LDS (for the
+// 256 x 256 forward the staging alone runs at 13.4 instead of 11.6 TB/s, but
+// the whole kernel is no faster, so the kernels use 2). The DMA blocks of a
+// pair go out between the first k-step's MFMAs,
+// A's pair p + 1 before B's pair p + NSB - 1, so that in-order completion
+// lets the wait for pair p leave B's newest pair in flight. The 16-byte
+// pieces of row r are rotated by r (slot = (piece + r) mod 8), which keeps
+// the 16-row fragment reads of both k-steps free of bank conflicts. Within a
+// k-step all B fragments and two A fragments are read first, then A fragment
+// i+2 is read while the MFMAs of row block i run (scheduling group barriers
+// pin the order).
+template <int BM, int BN, int WM, int WN, int NSB = 2>
 struct AsyncGemmP {
   static constexpr int NW = WM * WN;
   static_assert(NW == 4, "4 waves per tile");
   static_assert(BM % 8 == 0 && BN % 8 == 0, "8-row DMA blocks");
+  static_assert(NSB == 2 || NSB == 3, "2 or 3 pair slots for B");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NJ = WTN / 16;
   static constexpr int ROWB = 128;
-  static constexpr int SLOT_BYTES = (BM + BN) * ROWB;
-  static constexpr int LDS_BYTES = 2 * SLOT_BYTES;
+  static constexpr int SLOT_A = BM * ROWB, SLOT_B = BN * ROWB;
+  static constexpr int LDS_BYTES = 2 * SLOT_A + NSB * SLOT_B;
   static constexpr int NI_A = BM / 8, NI_B = BN / 8;  // 1 KB blocks = 8 rows
   static constexpr int NI = NI_A + NI_B;
   static_assert(NI_A % NW == 0 && NI % NW == 0, "DMA blocks divide among the waves");
   static constexpr int NB = NI / NW;  // blocks per wave per pair
+  static constexpr int NB_A = NI_A / NW, NB_B = NI_B / NW;
   // 128-byte staged rows: logical piece c of row r sits at slot (c + r) mod 8
   // (conflict-free 16-byte fragment reads for both k-steps of the pair)
   static __device__ __forceinline__ int slot(int c, int r) { return (c + r) & 7; }
@@ -290,27 +298,34 @@ struct AsyncGemmP {
     const int br = b_rows < 0 ? 0 : (b_rows > BN ? BN : b_rows);
     const i32x4 rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
     const i32x4 rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
-    // DMA: block j holds rows 8 j .. 8 j + 7 of the slot (A rows, then B rows);
-    // lane -> row 8 j + lane / 8, physical piece lane % 8, which holds the
-    // logical piece piece_at(lane % 8, row). Block wave + NW ii is row 8 wave +
-    // lane / 8 plus 32 ii rows (same row % 16). The buffer range check covers
-    // the vector offset only (the scalar offset is added after it), so the
-    // whole row offset, 32 ii rows included, travels in the vector offset and
-    // only the k offset in the scalar one: a row at or past a_rows / b_rows
-    // then fails the check and is never fetched.
+    // DMA: block j of an operand's slot holds its rows 8 j .. 8 j + 7; lane ->
+    // row 8 j + lane / 8, physical piece lane % 8, which holds the logical
+    // piece piece_at(lane % 8, row). Block wave + NW ii is row 8 wave + lane / 8
+    // plus 32 ii rows (same row % 16). The buffer range check covers the vector
+    // offset only (the scalar offset is added after it), so the whole row
+    // offset, 32 ii rows included, travels in the vector offset and only the k
+    // offset in the scalar one: a row at or past a_rows / b_rows then fails the
+    // check and is never fetched.
     const int row0 = 8 * wave + (lane >> 3);
     const int piece = piece_at(lane & 7, row0 & 15);
     const int voffA = (int)(row0 * lda * 2) + 16 * piece;
     const int voffB = (int)(row0 * ldb * 2) + 16 * piece;
-    constexpr int NB_A = NI_A / NW;
-    auto issue_block = [&](int ii, uint32_t dst, int koff) {
-      if (ii < NB_A)
-        dma16(rsA, dst + 1024u * NW * ii, voffA + (int)(ii * 64 * lda), koff);
-      else
-        dma16(rsB, dst + 1024u * NW * ii, voffB + (int)((ii - NB_A) * 64 * ldb), koff);
+    // A pair past the last reads through an empty resource: its blocks land
+    // zeros in a slot nobody reads and touch no memory, so the refill needs no
+    // branch inside the MFMA sequence.
+    const i32x4 rsNull = make_rsrc(A, 0u);
+    auto a_dst = [&](int p) { return lds0 + (uint32_t)((p & 1) * SLOT_A) + 1024u * wave; };
+    auto b_dst = [&](int p) {
+      return lds0 + (uint32_t)(2 * SLOT_A + (p % NSB) * SLOT_B) + 1024u * wave;
     };
-    auto slot_dst = [&](int p) {
-      return lds0 + (uint32_t)((p & 1) * SLOT_BYTES) + 1024u * (uint32_t)wave;
+    // block ii < NB_A: A's block ii (address a, k offset ka, resource ra);
+    // else B's block ii - NB_A
+    auto issue_block = [&](int ii, uint32_t a, int ka, const i32x4& ra, uint32_t b, int kb,
+                           const i32x4& rb) {
+      if (ii < NB_A)
+        dma16(ra, a + 1024u * NW * ii, voffA + (int)(ii * 64 * lda), ka);
+      else
+        dma16(rb, b + 1024u * NW * (ii - NB_A), voffB + (int)((ii - NB_A) * 64 * ldb), kb);
     };
     // fragment offsets of this lane in a slot for half h (k-step 2 p + h):
     // row l % 16 of the block, logical piece 4 h + l / 16
@@ -318,15 +333,35 @@ struct AsyncGemmP {
     const uint32_t foff0 = fr * ROWB + 16 * slot(lane >> 4, fr);
     const uint32_t foff1 = fr * ROWB + 16 * slot(4 + (lane >> 4), fr);
 
+    // prologue, in the order pairs are needed: B 0, A 0, then B 1 (3 slots)
+    {
+      const int kb0 = k_begin * 2;
 #pragma unroll
-    for (int ii = 0; ii < NB; ++ii) issue_block(ii, slot_dst(0), k_begin * 2);
+      for (int ii = NB_A; ii < NB; ++ii) issue_block(ii, 0, 0, rsNull, b_dst(0), kb0, rsB);
+#pragma unroll
+      for (int ii = 0; ii < NB_A; ++ii) issue_block(ii, a_dst(0), kb0, rsA, 0, 0, rsNull);
+      if constexpr (NSB == 3) {
+        const i32x4 rb1 = npairs > 1 ? rsB : rsNull;
+#pragma unroll
+        for (int ii = NB_A; ii < NB; ++ii)
+          issue_block(ii, 0, 0, rsNull, b_dst(1), kb0 + 128, rb1);
+      }
+    }
     for (int p = 0; p < npairs; ++p) {
-      wait_vmcnt<0>();  // this wave's part of pair p has landed
-      barrier_only();   // everyone's has; the other slot (pair p - 1) is free
-      const bool refill = p + 1 < npairs;
-      const uint32_t dst = slot_dst(p + 1);
-      const int koff = (k_begin + 64 * (p + 1)) * 2;
-      const unsigned char* st = lds + (p & 1) * SLOT_BYTES;
+      // this wave's part of pairs p of A and B has landed: with 3 B slots
+      // everything but B's pair p + 1 (issued after A's pair p), if any
+      if (NSB == 3 && p + 1 < npairs)
+        wait_vmcnt<NB_B>();
+      else
+        wait_vmcnt<0>();
+      barrier_only();  // everyone's has; the slots of A's pair p - 1 and B's p - 1 are free
+      const int pa = p + 1, pb = p + NSB - 1;  // pairs refilled during this one
+      const uint32_t da = a_dst(pa), db = b_dst(pb);
+      const int ka = (k_begin + 64 * pa) * 2, kb = (k_begin + 64 * pb) * 2;
+      const i32x4 ra = pa < npairs ? rsA : rsNull;
+      const i32x4 rb = pb < npairs ? rsB : rsNull;
+      const unsigned char* sa = lds + (p & 1) * SLOT_A;
+      const unsigned char* sb = lds + 2 * SLOT_A + (p % NSB) * SLOT_B;
 #pragma unroll 1
       for (int h = 0; h < 2; ++h) {
         constexpr int A0 = MI < 2 ? MI : 2;
@@ -335,18 +370,18 @@ struct AsyncGemmP {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           bfr[j] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(st + (BM + wn * WTN + 16 * j) * ROWB + fo));
+              bf16x8, *reinterpret_cast<const u32x4*>(sb + (wn * WTN + 16 * j) * ROWB + fo));
 #pragma unroll
         for (int i = 0; i < A0; ++i)
           af[i] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * i) * ROWB + fo));
+              bf16x8, *reinterpret_cast<const u32x4*>(sa + (wm * WTM + 16 * i) * ROWB + fo));
         __builtin_amdgcn_sched_group_barrier(0x100, NJ + A0, 0);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           if (i + A0 < MI)
             af[i + A0] = __builtin_bit_cast(
                 bf16x8,
-                *reinterpret_cast<const u32x4*>(st + (wm * WTM + 16 * (i + A0)) * ROWB + fo));
+                *reinterpret_cast<const u32x4*>(sa + (wm * WTM + 16 * (i + A0)) * ROWB + fo));
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
@@ -357,10 +392,11 @@ struct AsyncGemmP {
           } else {
             __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
           }
-          // the next pair's DMA blocks go out during the first k-step's MFMAs
-          if (h == 0 && refill) {
+          // the refill's DMA blocks go out during the first k-step's MFMAs
+          if (h == 0) {
 #pragma unroll
-            for (int ii = (i * NB) / MI; ii < ((i + 1) * NB) / MI; ++ii) issue_block(ii, dst, koff);
+            for (int ii = (i * NB) / MI; ii < ((i + 1) * NB) / MI; ++ii)
+              issue_block(ii, da, ka, ra, db, kb, rb);
           }
         }
       }

@@ -84,11 +84,12 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int Vs, int Gs, int64_t vocab_start, int G,
     int n_ttiles, float4* __restrict__ part) {
-  using Gm = AsyncGemmP<BM, GROUP, WM, WN>;
+  // the targets wait in a register until the ring is free (a third W pair
+  // slot, which fills the LDS, measured no faster)
+  using Gm = AsyncGemmP<BM, GROUP, WM, WN, 2>;
   static_assert(WN == 2 && Gm::WTN == 128 && Gm::NJ == 8, "one 128-column chunk per wave");
-  static_assert(BM * 2 * 16 <= Gm::LDS_BYTES, "chunk records fit in the stages");
+  static_assert(BM * 2 * 16 + BM * 4 <= Gm::LDS_BYTES, "chunk records and targets fit the ring");
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
-  __shared__ int ycol[BM];
 
   int g, tt;
   xcd_decode(blockIdx.x, n_ttiles, g, tt);
@@ -98,22 +99,24 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
   const int col0 = (g / Gs) * Vs + lg * GROUP;
   const int vlim = min(GROUP, Vs - lg * GROUP);  // valid columns of the group
   const int tid = threadIdx.x;
+  int my_yc = -1;  // target column of row row0 + tid in the group, or -1
   if (tid < BM) {
     const int t = row0 + tid;
-    int yc = -1;
     if (t < T) {
       const int64_t y = (int64_t)targets[t] - vocab_start - col0;
-      if (y >= 0 && y < vlim) yc = (int)y;
+      if (y >= 0 && y < vlim) my_yc = (int)y;
     }
-    ycol[tid] = yc;
   }
 
   Gm gm;
   gm.zero();
   gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, vlim, 0, H);
-  // run() ends on a barrier: the LDS stages are free and ycol is visible.
+  // run() ends on a barrier: the LDS ring is free.
+  float4* rec = reinterpret_cast<float4*>(lds);               // [BM][2 chunks] {m, R, B, zy}
+  int* ycol = reinterpret_cast<int*>(lds + BM * 2 * 16);      // [BM]
+  if (tid < BM) ycol[tid] = my_yc;
+  __syncthreads();
 
-  float4* rec = reinterpret_cast<float4*>(lds);  // [BM][2 chunks] {m, R, B, zy}
   const int lane = tid & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
