@@ -201,19 +201,38 @@ __device__ __forceinline__ int row_piece(int s, int r) { return (s - (r >> 1)) &
 // track these LDS writes: its own conservative waits (vmcnt(0) before every
 // LDS read) would drain the prefetch pipeline. Ordering is the caller's:
 // explicit vmcnt waits and barriers (all with memory clobbers).
+// The compiler's hazard checks do not look inside inline asm, so the asm
+// keeps two gfx9 rules itself: M0 written by the SALU needs 1 wait state
+// before the LDS-DMA reads it, and an SGPR written by a VALU instruction
+// needs 5 before a buffer instruction reads it. The descriptor and offsets
+// pass through readfirstlane (a no-op where the compiler knows them to be
+// uniform); where it does not, it parks them in VGPRs and reads them back
+// with a v_readfirstlane just before the asm. SETTLE = true (s_nop 4, 5 wait
+// states in all) is for the call sites where it does that; the test suite
+// scans the built code for the pattern, so a site that needs it and lacks it
+// does not go unnoticed.
+template <bool SETTLE = false>
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t addr, int voff, int soff) {
-  // the descriptor is wave-uniform; readfirstlane keeps it in SGPRs where the
-  // compiler cannot prove that itself (a no-op where it can)
   const i32x4 rs = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
                     __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane((int)addr)), "v"(voff), "s"(rs),
-        "s"(__builtin_amdgcn_readfirstlane(soff))
-      : "memory", "m0");
+  if constexpr (SETTLE)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane((int)addr)), "v"(voff), "s"(rs),
+          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane((int)addr)), "v"(voff), "s"(rs),
+          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory", "m0");
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
@@ -525,9 +544,9 @@ struct AsyncGemmKN {
 #pragma unroll
         for (int ii = 0; ii < NI / NW; ++ii) {
           if (ii < NI_A / NW)
-            dma16(rsA, st + (wave + NW * ii) * 1024, voff[ii], k0 * 2);
+            dma16<true>(rsA, st + (wave + NW * ii) * 1024, voff[ii], k0 * 2);
           else
-            dma16(rsB, st + (wave + NW * ii) * 1024, voff[ii], 0);
+            dma16<true>(rsB, st + (wave + NW * ii) * 1024, voff[ii], 0);
         }
       } else {
 #pragma unroll
@@ -535,9 +554,9 @@ struct AsyncGemmKN {
           const int j = wave + NW * ii;
           if (j < NI) {
             if (j < NI_A)
-              dma16(rsA, st + j * 1024, voff[ii], k0 * 2);
+              dma16<true>(rsA, st + j * 1024, voff[ii], k0 * 2);
             else
-              dma16(rsB, st + j * 1024, voff[ii], 0);
+              dma16<true>(rsB, st + j * 1024, voff[ii], 0);
           }
         }
       }
@@ -586,9 +605,15 @@ struct AsyncGemmKN {
     // The DMA blocks of the stage being refilled go out one per MFMA row
     // block when they divide evenly (which operand each is: compile time).
     constexpr bool SPLIT = NI_A % NW == 0 && NI % NW == 0 && NI / NW <= MI * KSUB;
+    // the first block of each operand in a stage settles the descriptor's
+    // SGPRs (the compiler reads them back from VGPRs once per stage)
     auto issue_block = [&](int ii, uint32_t dst, int k0, const i32x4& rsB) {
-      if (ii < NI_A / NW)
+      if (ii == 0)
+        dma16<true>(rsA, dst, voff[0], k0 * 2);
+      else if (ii < NI_A / NW)
         dma16(rsA, dst + 1024u * NW * ii, voff[ii], k0 * 2);
+      else if (ii == NI_A / NW)
+        dma16<true>(rsB, dst + 1024u * NW * ii, voff[ii], 0);
       else
         dma16(rsB, dst + 1024u * NW * ii, voff[ii], 0);
     };
