@@ -434,10 +434,10 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 // C[BM x BN] += A[BM x K] * B[K x BN] with A K-contiguous (element (r, k) at
 // A[r * lda + k]) and B K-major (element (k, n) at B[k * ldb + n]): the
 // contraction over the vocabulary, where B is W in its natural layout.
-// A is staged in 64-byte rows, pieces placed by row_slot. A B stage is 32
+// A is staged in 64-byte rows, pieces placed by a_slot. A B stage is 32
 // rows k of BN columns copied verbatim by LDS-DMA, the 16-byte pieces of row
-// k permuted by XOR with 2 (k % 4) + 8 ((k / 8) % 2), which spreads the
-// transposing reads below over all banks. B fragments come from
+// k permuted by XOR with bswz(k), which spreads the transposing reads below
+// over all banks. B fragments come from
 // ds_read_b64_tr_b16: inside a 16-lane group, lane i returns element i % 4 of
 // what source lanes i / 4 + 4 j (j = 0..3) point at, so source lane s points
 // at row k0 + s / 4, columns n0 + 4 (s % 4) .. + 3, and lane i receives
@@ -495,7 +495,23 @@ struct AsyncGemmKN {
         for (int e = 0; e < ACC_N; ++e) acc[i][j][e] = 0.f;
   }
 
-  static __device__ __forceinline__ int bswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+  // Piece placements, measured with the LDS bank-conflict counter (cycles
+  // per read, 0 = none). B (K-major, transposing reads): piece p of row k at
+  // p ^ bswz(k); the 16x16x32 reads (rows k0 + 8 g + 0..3) take
+  // 2 (k % 4) + 8 ((k / 8) % 2): 0; the 32x32x16 reads (rows k0 + 0..3 and
+  // k0 + 8..11, two 32-byte column groups) take 4 (k % 4): 0, where the
+  // 16x16 placement costs 2. A (64-byte rows, 16-byte reads): the 16-row
+  // reads take row_slot (rotation by r / 2): 0; the 32-row reads take a
+  // rotation by r / 4: 0, where row_slot costs 4.
+  static __device__ __forceinline__ int bswz(int k) {
+    return M32 ? 4 * (k & 3) : 2 * (k & 3) + 8 * ((k >> 3) & 1);
+  }
+  static __device__ __forceinline__ int a_slot(int c, int r) {
+    return M32 ? (c + (r >> 2)) & 3 : row_slot(c, r);
+  }
+  static __device__ __forceinline__ int a_piece(int s, int r) {
+    return M32 ? (s - (r >> 2)) & 3 : row_piece(s, r);
+  }
 
   static __device__ __forceinline__ acc_t mfma(const bf16x8& a, const bf16x8& b, const acc_t& c) {
     if constexpr (M32)
@@ -517,7 +533,7 @@ struct AsyncGemmKN {
     const uint32_t lds0 = lds_addr(lds);
 
     const int drow = lane >> 2;
-    const int dpiece = row_piece(lane & 3, lane >> 2);
+    const int dpiece = a_piece(lane & 3, lane >> 2);
     const int brow = lane / PPR, bslot = lane % PPR;
     int voff[NI_W_MAX];
 #pragma unroll
@@ -569,7 +585,7 @@ struct AsyncGemmKN {
     for (int q = 0; q < KSUB; ++q) {
       const int r = lane % FR;
       const int c = M32 ? 2 * q + (lane >> 5) : (lane >> 4);
-      foff[q] = (uint32_t)(r * ROWB_A + 16 * row_slot(c, r));
+      foff[q] = (uint32_t)(r * ROWB_A + 16 * a_slot(c, r));
     }
     // transposing reads: 16-lane group g, source lane sl; read t of MFMA step
     // q covers rows k0 + 4 t + sl / 4 at columns n0 + 4 (sl % 4) .. + 3, with
