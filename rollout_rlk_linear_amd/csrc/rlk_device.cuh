@@ -304,9 +304,48 @@ struct AsyncGemmP {
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // The first pairs of a run (B's pair 0, A's pair 0, then B's pair 1 with 3
+  // slots), issued on their own: a persistent caller issues the next tile's
+  // while it finishes the current one (its epilogue must then keep out of
+  // A's and B's pair-0 slots, and B's pair-1 slot with 3), and passes
+  // prefetched = true to run().
+  __device__ __forceinline__ void prologue(unsigned char* lds, const uint16_t* A, int64_t lda,
+                                           int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
+                                           int k_begin, int k_end) {
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int npairs = (k_end - k_begin) / 64;
+    if (npairs <= 0) return;
+    const uint32_t lds0 = lds_addr(lds);
+    const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
+    const int br = b_rows < 0 ? 0 : (b_rows > BN ? BN : b_rows);
+    const i32x4 rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
+    const i32x4 rsB = make_rsrc(B, (uint32_t)(br * ldb * 2));
+    const i32x4 rsNull = make_rsrc(A, 0u);
+    const int row0 = 8 * wave + (lane >> 3);
+    const int piece = piece_at(lane & 7, row0 & 15);
+    const int voffA = (int)(row0 * lda * 2) + 16 * piece;
+    const int voffB = (int)(row0 * ldb * 2) + 16 * piece;
+    const int kb0 = k_begin * 2;
+#pragma unroll
+    for (int ii = 0; ii < NB_B; ++ii)
+      dma16(rsB, lds0 + (uint32_t)(2 * SLOT_A) + 1024u * wave + 1024u * NW * ii,
+            voffB + (int)(ii * 64 * ldb), kb0);
+#pragma unroll
+    for (int ii = 0; ii < NB_A; ++ii)
+      dma16(rsA, lds0 + 1024u * wave + 1024u * NW * ii, voffA + (int)(ii * 64 * lda), kb0);
+    if constexpr (NSB == 3) {
+      const i32x4 rb1 = npairs > 1 ? rsB : rsNull;
+#pragma unroll
+      for (int ii = 0; ii < NB_B; ++ii)
+        dma16(rb1, lds0 + (uint32_t)(2 * SLOT_A + SLOT_B) + 1024u * wave + 1024u * NW * ii,
+              voffB + (int)(ii * 64 * ldb), kb0 + 128);
+    }
+  }
+
   __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
                                       int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
-                                      int k_begin, int k_end) {
+                                      int k_begin, int k_end, bool prefetched = false) {
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int wm = wave % WM, wn = wave / WM;
@@ -353,19 +392,7 @@ struct AsyncGemmP {
     const uint32_t foff1 = fr * ROWB + 16 * slot(4 + (lane >> 4), fr);
 
     // prologue, in the order pairs are needed: B 0, A 0, then B 1 (3 slots)
-    {
-      const int kb0 = k_begin * 2;
-#pragma unroll
-      for (int ii = NB_A; ii < NB; ++ii) issue_block(ii, 0, 0, rsNull, b_dst(0), kb0, rsB);
-#pragma unroll
-      for (int ii = 0; ii < NB_A; ++ii) issue_block(ii, a_dst(0), kb0, rsA, 0, 0, rsNull);
-      if constexpr (NSB == 3) {
-        const i32x4 rb1 = npairs > 1 ? rsB : rsNull;
-#pragma unroll
-        for (int ii = NB_A; ii < NB; ++ii)
-          issue_block(ii, 0, 0, rsNull, b_dst(1), kb0 + 128, rb1);
-      }
-    }
+    if (!prefetched) prologue(lds, A, lda, a_rows, B, ldb, b_rows, k_begin, k_end);
     for (int p = 0; p < npairs; ++p) {
       // this wave's part of pairs p of A and B has landed: with 3 B slots
       // everything but B's pair p + 1 (issued after A's pair p), if any

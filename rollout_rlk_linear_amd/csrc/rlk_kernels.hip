@@ -79,90 +79,138 @@ __device__ __forceinline__ ChunkStats chunk_stats(const float (&z)[8]) {
 
 // Group g of the call is group g % Gs of virtual slice g / Gs: columns
 // (g / Gs) Vs + 256 (g % Gs) onward, at most 256 and not past the slice.
+// A persistent grid (a multiple of 8 workgroups, one per CU) walks the
+// (group, T-tile) items b, b + grid, ... in xcd_decode's order, so an item
+// stays on the XCD of its workgroup. The next item's first pairs are issued
+// as soon as the current item's mainloop ends, and land while its chunk
+// statistics are computed: the epilogue works in B's pair-1 slot, which that
+// prologue leaves alone. Items whose group is past G (the padding of the
+// 8-way deal) are skipped.
+struct FwdItem {
+  int g, row0, col0, vlim;
+};
+__device__ __forceinline__ FwdItem fwd_item(int it, int n_ttiles, int BM, int Gs, int Vs) {
+  int g, tt;
+  xcd_decode(it, n_ttiles, g, tt);
+  const int lg = g % Gs;
+  return FwdItem{g, tt * BM, (g / Gs) * Vs + lg * GROUP, min(GROUP, Vs - lg * GROUP)};
+}
+
 template <int BM, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int Vs, int Gs, int64_t vocab_start, int G,
-    int n_ttiles, float4* __restrict__ part) {
-  // the targets wait in a register until the ring is free (a third W pair
-  // slot, which fills the LDS, measured no faster)
+    int n_ttiles, int n_items, float4* __restrict__ part) {
   using Gm = AsyncGemmP<BM, GROUP, WM, WN, 2>;
   static_assert(WN == 2 && Gm::WTN == 128 && Gm::NJ == 8, "one 128-column chunk per wave");
-  static_assert(BM * 2 * 16 + BM * 4 <= Gm::LDS_BYTES, "chunk records and targets fit the ring");
+  static_assert(BM * 2 * 16 + BM * 4 <= Gm::SLOT_B, "chunk records and targets fit B's pair-1 slot");
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
+  float4* rec = reinterpret_cast<float4*>(lds + 2 * Gm::SLOT_A + Gm::SLOT_B);  // [BM][2 chunks]
+  int* ycol = reinterpret_cast<int*>(lds + 2 * Gm::SLOT_A + Gm::SLOT_B + BM * 2 * 16);  // [BM]
 
-  int g, tt;
-  xcd_decode(blockIdx.x, n_ttiles, g, tt);
-  if (g >= G) return;
-  const int row0 = tt * BM;
-  const int lg = g % Gs;
-  const int col0 = (g / Gs) * Vs + lg * GROUP;
-  const int vlim = min(GROUP, Vs - lg * GROUP);  // valid columns of the group
+  const int stride = gridDim.x;  // a multiple of 8: items keep their XCD
+  auto next_item = [&](int it) {
+    while (it < n_items && fwd_item(it, n_ttiles, BM, Gs, Vs).g >= G) it += stride;
+    return it;
+  };
+  // target of row row0 + tid (loaded early), then its column in the
+  // item's group or -1
   const int tid = threadIdx.x;
-  int my_yc = -1;  // target column of row row0 + tid in the group, or -1
-  if (tid < BM) {
-    const int t = row0 + tid;
-    if (t < T) {
-      const int64_t y = (int64_t)targets[t] - vocab_start - col0;
-      if (y >= 0 && y < vlim) my_yc = (int)y;
+  auto target_of = [&](const FwdItem& f) {
+    const int t = f.row0 + tid;
+    return (tid < BM && t < T) ? targets[t] : -1;
+  };
+  auto target_col = [&](const FwdItem& f, int32_t y32) {
+    int yc = -1;
+    if (tid < BM && f.row0 + tid < T) {
+      const int64_t y = (int64_t)y32 - vocab_start - f.col0;
+      if (y >= 0 && y < f.vlim) yc = (int)y;
     }
-  }
+    return yc;
+  };
 
+  int it = next_item(blockIdx.x);
+  if (it >= n_items) return;
+  FwdItem cur = fwd_item(it, n_ttiles, BM, Gs, Vs);
+  int my_yc = target_col(cur, target_of(cur));
   Gm gm;
-  gm.zero();
-  gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, vlim, 0, H);
-  // run() ends on a barrier: the LDS ring is free.
-  float4* rec = reinterpret_cast<float4*>(lds);               // [BM][2 chunks] {m, R, B, zy}
-  int* ycol = reinterpret_cast<int*>(lds + BM * 2 * 16);      // [BM]
-  if (tid < BM) ycol[tid] = my_yc;
-  __syncthreads();
-
+  gm.prologue(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0, weight + (int64_t)cur.col0 * H,
+              H, cur.vlim, 0, H);
   const int lane = tid & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
   const int cbase = wn * 128;  // this wave's chunk within the group
-  if (cbase < vlim) {
-    bool cvalid[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cvalid[j] = cbase + 16 * j + (lane & 15) < vlim;
 #pragma unroll 1
-    for (int i = 0; i < Gm::MI; ++i) {
-      f32x4 blk[8];
-      acc_row_block<0>(gm.acc, i, blk);
-      int yc[4];
+  for (;;) {
+    const int nit = next_item(it + stride);
+    const FwdItem nxt = nit < n_items ? fwd_item(nit, n_ttiles, BM, Gs, Vs) : cur;
+    int32_t ny = target_of(nxt);  // in flight during the mainloop
+    gm.zero();
+    gm.run(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0, weight + (int64_t)cur.col0 * H, H,
+           cur.vlim, 0, H, /*prefetched=*/true);
+    // run() ends with every load drained: the next target is settled here, so
+    // the compiler's wait for it never meets the next prologue's DMA
+    asm volatile("" : "+v"(ny));
+    const int nyc = target_col(nxt, ny);
+    if (nit < n_items)
+      gm.prologue(lds, hidden + (int64_t)nxt.row0 * H, H, T - nxt.row0,
+                  weight + (int64_t)nxt.col0 * H, H, nxt.vlim, 0, H);
+
+    // chunk statistics of the current item (LDS: B's pair-1 slot only)
+    if (tid < BM) ycol[tid] = my_yc;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_only();
+    const int vlim = cur.vlim;
+    if (cbase < vlim) {
+      bool cvalid[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yc[r] = ycol[wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r] - cbase;
-      // straight-line over the four rows (no branches: rows interleave)
+      for (int j = 0; j < 8; ++j) cvalid[j] = cbase + 16 * j + (lane & 15) < vlim;
+#pragma unroll 1
+      for (int i = 0; i < Gm::MI; ++i) {
+        f32x4 blk[8];
+        acc_row_block<0>(gm.acc, i, blk);
+        int yc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
-        float z[8];
+        for (int r = 0; r < 4; ++r)
+          yc[r] = ycol[wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r] - cbase;
+        // straight-line over the four rows (no branches: rows interleave)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) z[j] = cvalid[j] ? blk[j][r] : neg_inf();
-        const ChunkStats c = chunk_stats(z);
-        // target logit: held by one lane of the 16 (if in this chunk), spread by a max
-        const bool yin = yc[r] >= 0 && yc[r] < 128;
-        const int jt = yc[r] >> 4;
-        float zl = neg_inf();
+        for (int r = 0; r < 4; ++r) {
+          const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
+          float z[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) zl = (j == jt) ? z[j] : zl;
-        zl = (yin && (yc[r] & 15) == (lane & 15)) ? zl : neg_inf();
-        const float zy = row16_max(zl);
-        // all 16 lanes hold the same record and store it to the same slot
-        rec[rl * 2 + wn] = make_float4(c.m, c.R, c.B, zy);
+          for (int j = 0; j < 8; ++j) z[j] = cvalid[j] ? blk[j][r] : neg_inf();
+          const ChunkStats c = chunk_stats(z);
+          // target logit: held by one lane of the 16 (if in this chunk), spread by a max
+          const bool yin = yc[r] >= 0 && yc[r] < 128;
+          const int jt = yc[r] >> 4;
+          float zl = neg_inf();
+#pragma unroll
+          for (int j = 0; j < 8; ++j) zl = (j == jt) ? z[j] : zl;
+          zl = (yin && (yc[r] & 15) == (lane & 15)) ? zl : neg_inf();
+          const float zy = row16_max(zl);
+          // all 16 lanes hold the same record and store it to the same slot
+          rec[rl * 2 + wn] = make_float4(c.m, c.R, c.B, zy);
+        }
       }
     }
-  }
-  __syncthreads();
-  if (tid < BM && row0 + tid < T) {
-    const float4 a = rec[tid * 2];
-    Part acc{a.x, a.y, a.z, a.w};
-    if (128 < vlim) {
-      const float4 b = rec[tid * 2 + 1];
-      acc = part_merge(acc, Part{b.x, b.y, b.z, b.w});
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_only();
+    if (tid < BM && cur.row0 + tid < T) {
+      const float4 a = rec[tid * 2];
+      Part acc{a.x, a.y, a.z, a.w};
+      if (128 < vlim) {
+        const float4 b = rec[tid * 2 + 1];
+        acc = part_merge(acc, Part{b.x, b.y, b.z, b.w});
+      }
+      part[(int64_t)(cur.row0 + tid) * G + cur.g] = make_float4(acc.m, acc.R, acc.B, acc.zy);
     }
-    part[(int64_t)(row0 + tid) * G + g] = make_float4(acc.m, acc.R, acc.B, acc.zy);
+    if (nit >= n_items) break;
+    it = nit;
+    cur = nxt;
+    my_yc = nyc;
   }
+  wait_vmcnt<0>();
 }
 
 // ------------------------------------------------- small-batch stream ----
@@ -918,7 +966,7 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 #define RLK_FWD_TILE(BM, WM, WN)                                                              \
   template __global__ void fwd_tile_kernel<BM, WM, WN>(                                       \
       const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__, \
-      int, int, int, int, int64_t, int, int, float4* __restrict__);
+      int, int, int, int, int64_t, int, int, int, float4* __restrict__);
 #define RLK_RECOMPUTE(BM, BN, WM, WN)                                                          \
   template __global__ void bwd_recompute_kernel<BM, BN, WM, WN>(                               \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
@@ -985,9 +1033,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
     }
   } else {
     const int nt = cdiv(a.T, 256);
-    const int G8 = cdiv(G, 8) * 8;
-    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2>), G8 * nt, st, a.hidden, a.weight,
-               a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, a.part);
+    const int n_items = cdiv(G, 8) * 8 * nt;
+    const int n_cu = a.n_cu > 0 ? a.n_cu : 256;
+    const int grid = min(cdiv(n_cu, 8) * 8, n_items);  // a multiple of 8
+    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2>), grid, st, a.hidden, a.weight,
+               a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, n_items, a.part);
   }
   RLK_LAUNCH(K_FWD_COMBINE, fwd_combine_kernel, a.T, st, a.part, a.targets,
              a.T, G, sl.P, sl.Gs, sl.Vs, units, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
