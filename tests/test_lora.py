@@ -11,6 +11,8 @@ accumulation bound of the float64 value (and equal to its correct rounding
 for >= 99% of the elements); dA and dB within 1e-5. Row independence and repeatability are checked bit for bit.
 """
 
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 import torch
@@ -166,3 +168,31 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert dx.shape == (0, 64)
     assert torch.count_nonzero(da) == 0 and torch.count_nonzero(db) == 0
+
+
+@pytest.mark.parametrize("N,K,T", [(5120, 5120, 33), (576, 2560, 1), (4160, 2560, 17),
+                                   (2048, 4096, 48), (1024, 8192, 64), (20480, 2560, 9)])
+def test_small_batch_split_forward_matches_tiles_bitwise(N, K, T):
+    # A batch of at most 64 rows whose contraction is split (K >= 2560; one
+    # 64-row tile, several split partials reduced in order) must give the same
+    # bits as the same rows inside a batch of more than 64 rows (two tiles);
+    # the small batch is also checked element-wise against float64, and its
+    # result must not depend on what the workspace held before (every split
+    # partial of every valid element is written before it is read).
+    big = wl.lora_case(N, K, T + 65, 90 + T, r=16)
+    x, W, A, B = (dev(t) for t in (big.x, big.W, big.A, big.B))
+    y_big = rlk.lora_fwd(x, W, A, B, 1.25)
+    torch.cuda.synchronize()
+    for r0 in (0, 65):
+        xs = x[r0:r0 + T].contiguous()
+        ys = rlk.lora_fwd(xs, W, A, B, 1.25)
+        torch.cuda.synchronize()
+        assert bits_equal(ys, y_big[r0:r0 + T]), f"rows {r0}:{r0 + T} (N={N} K={K})"
+    small = SimpleNamespace(x=big.x[65:65 + T], W=big.W, A=big.A, B=big.B)
+    f = lora_forward(small.x, small.W, small.A, small.B, 1.25)
+    rounding_check(ys, f["y"], abs_terms_y(small, 1.25), K + 16 + 4, f"y N={N} K={K} T={T}")
+    nws = rlk.load_library().rlk_lora_linear_workspace_bytes(T, K, N, 16)
+    ws = torch.full((nws // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    yn = rlk.lora_fwd(xs, W, A, B, 1.25, ws=ws.view(torch.uint8))
+    torch.cuda.synchronize()
+    assert bits_equal(yn, ys), "a stale workspace changed the result"
