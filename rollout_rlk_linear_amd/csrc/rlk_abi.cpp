@@ -400,11 +400,13 @@ RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
   const rlk::BwdPlan plan = rlk::bwd_plan(T, H, sl, dhidden != nullptr);
   if (workspace_bytes < plan.total) return RLK_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 256)) return RLK_ERR_INVALID_ARG;
-  s = check_device();
+  int n_cu = 0;
+  s = check_device(&n_cu);
   if (s != RLK_OK) return s;
 
   char* ws = static_cast<char*>(workspace);
   rlk::BwdArgs a{};
+  a.n_cu = n_cu;
   a.hidden = static_cast<const uint16_t*>(hidden);
   a.weight = static_cast<const uint16_t*>(weight);
   a.targets = targets;

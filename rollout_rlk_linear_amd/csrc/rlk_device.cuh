@@ -343,9 +343,17 @@ struct AsyncGemmP {
     }
   }
 
+  // YOUNG > 0 with young_pending: the caller issued the prologue, then at
+  // least YOUNG more vector-memory operations of its own in every wave (e.g.
+  // the previous tile's stores), which need not have completed for pair 0:
+  // with in-order completion, YOUNG pending operations at most mean that
+  // everything older, the prologue included, has landed.
+  template <int YOUNG = 0>
   __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
                                       int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
-                                      int k_begin, int k_end, bool prefetched = false) {
+                                      int k_begin, int k_end, bool prefetched = false,
+                                      bool young_pending = false) {
+    static_assert(YOUNG >= 0 && YOUNG + NB_B < 64, "vmcnt range");
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int wm = wave % WM, wn = wave / WM;
@@ -396,10 +404,16 @@ struct AsyncGemmP {
     for (int p = 0; p < npairs; ++p) {
       // this wave's part of pairs p of A and B has landed: with 3 B slots
       // everything but B's pair p + 1 (issued after A's pair p), if any
-      if (NSB == 3 && p + 1 < npairs)
+      if (YOUNG > 0 && p == 0 && prefetched && young_pending) {
+        if (NSB == 3 && p + 1 < npairs)
+          wait_vmcnt<NB_B + YOUNG>();
+        else
+          wait_vmcnt<YOUNG>();
+      } else if (NSB == 3 && p + 1 < npairs) {
         wait_vmcnt<NB_B>();
-      else
+      } else {
         wait_vmcnt<0>();
+      }
       barrier_only();  // everyone's has; the slots of A's pair p - 1 and B's p - 1 are free
       const int pa = p + 1, pb = p + NSB - 1;  // pairs refilled during this one
       const uint32_t da = a_dst(pa), db = b_dst(pb);

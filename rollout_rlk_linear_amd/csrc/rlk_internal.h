@@ -113,6 +113,7 @@ struct BwdArgs {
   float4* rowc;
   uint16_t* gtv;  // [Tp][ldg] logit gradient of one chunk, rows t (dH and dW operand)
   float* part;
+  int n_cu;  // compute units of the device (persistent recompute grid)
 };
 
 // Kernel ids for the optional per-launch event timer (rlk_profile_*).

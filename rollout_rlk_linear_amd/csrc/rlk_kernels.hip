@@ -617,93 +617,176 @@ __device__ __forceinline__ void padded_col(int u, int Vs, int Vs_pad, int& row, 
   valid = Vs - l;
 }
 
-// G for one (T-tile, BN-column tile) of the chunk, rounded to bf16 into an
-// LDS tile [t][v], then stored as gtv[t][lt*BN + c] (rows t < T, 16-byte row
-// pieces; the tile's columns past its slice's end are zeros, which covers
-// dH's k-range at the end of every split; dW's tiles end on them too). Both
-// dH and dW read G from there. Each element depends on its logit and its
-// row's constants only, so the column width of the tile does not change a
-// bit. Tiles cover the chunk's padded columns [u0, u0 + n_tiles BN).
+// G for the (T-tile, BN-column tile) items of the chunk, rounded to bf16 and
+// stored as gtv[t][lt*BN + c] (rows t < T, 16-byte row pieces; the tile's
+// columns past its slice's end are zeros, which covers dH's k-range at the
+// end of every split; dW's tiles end on them too). Both dH and dW read G
+// from there. Each element depends on its logit and its row's constants
+// only, so the column width of the tile does not change a bit. Items cover
+// the chunk's padded columns [u0, u0 + n_tiles BN).
+// A persistent grid (a multiple of 8 workgroups; for 256-row tiles one per
+// CU, for the small batch's 32-row tiles one per item) walks the items
+// b, b + grid, ... in xcd_decode's order, so an item stays on the
+// XCD of its workgroup. The next item's first pair is issued as soon as the
+// current mainloop ends and lands while the current tile's G is formed: the
+// epilogue works only in A's and B's pair-1 slots, 32 rows a round (row
+// block i of both wave rows) staged as [t][v] so that the stores are whole
+// 16-byte row pieces, the rounds alternating between the two slots, and the
+// rows' constants (loaded from rowc during the mainloop) beside the first
+// round's buffer. When every wave issued all of a tile's stores, the next
+// mainloop's first wait leaves them in flight.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
-    int u0, int Vs, int Vs_pad, int n_tiles, int n_ttiles, const float4* __restrict__ rowc,
-    uint16_t* __restrict__ gtv, int64_t ldg) {
+    int u0, int Vs, int Vs_pad, int n_tiles, int n_ttiles, int n_items,
+    const float4* __restrict__ rowc, uint16_t* __restrict__ gtv, int64_t ldg) {
   using Gm = AsyncGemmP<BM, BN, WM, WN>;
-  constexpr int LDG_S = BN + 8;  // [t][v] staging row (bf16), 16 B longer than the tile's
-  constexpr int STG = BM * LDG_S * 2;
-  constexpr int LDSB = Gm::LDS_BYTES > STG ? Gm::LDS_BYTES : STG;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
-  uint16_t* stg = reinterpret_cast<uint16_t*>(lds);
+  static_assert(WM == 2, "a round is row block i of both wave rows: 32 rows");
+  constexpr int LDG_S = BN + 8;           // staged row (bf16), 16 B longer than the tile's
+  constexpr int RBYTES = 32 * LDG_S * 2;  // one round
+  constexpr int TPR = BN / 8;             // threads per staged row, 16 bytes each
+  constexpr int RPP = kThreads / TPR;     // rows per store pass
+  static_assert(kThreads % TPR == 0 && 32 % RPP == 0, "whole rows per pass, whole passes per round");
+  constexpr int STORES = Gm::MI * (32 / RPP);  // store instructions of each wave for a whole tile
+  constexpr bool DBL = Gm::MI > 1;             // rounds alternate between A's and B's pair-1 slots
+  constexpr int OFF_A1 = Gm::SLOT_A, OFF_B1 = 2 * Gm::SLOT_A + Gm::SLOT_B;
+  // row constants: two [BM] float4 arrays, row rl at slot perm(rl), which puts
+  // the rows 4 apart that one read instruction takes (rows b + 4 g + r,
+  // g = lane / 16) in adjacent 16-byte slots
+  constexpr int OFF_TAB = OFF_A1 + (DBL ? RBYTES : 0);
+  static_assert(RBYTES <= Gm::SLOT_B, "a round fits B's pair-1 slot");
+  static_assert(OFF_TAB + BM * 32 <= OFF_A1 + Gm::SLOT_A, "a round and the constants fit A's");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
+  float4* tab0 = reinterpret_cast<float4*>(lds + OFF_TAB);
+  float4* tab1 = tab0 + BM;
+  auto perm = [](int rl) { return (rl & ~15) | ((rl & 3) << 2) | ((rl >> 2) & 3); };
 
-  int lg, tt;
-  xcd_decode(blockIdx.x, n_ttiles, lg, tt);
-  if (lg >= n_tiles) return;
-  const int row0 = tt * BM;
-  int col0, vlim;  // call-local vocabulary row of the tile's first column; valid columns
-  padded_col(u0 + lg * BN, Vs, Vs_pad, col0, vlim);
+  struct Item {
+    int row0, lg, col0, vlim;  // col0: call-local vocabulary row of the first column; vlim: valid columns
+  };
+  auto item_of = [&](int it) {
+    int lg, tt;
+    xcd_decode(it, n_ttiles, lg, tt);
+    Item r;
+    r.row0 = tt * BM;
+    r.lg = lg;
+    padded_col(u0 + lg * BN, Vs, Vs_pad, r.col0, r.vlim);
+    return r;
+  };
+  const int stride = gridDim.x;  // a multiple of 8: items keep their XCD
+  auto next_item = [&](int it) {
+    for (; it < n_items; it += stride) {
+      int lg, tt;
+      xcd_decode(it, n_ttiles, lg, tt);
+      if (lg < n_tiles) break;
+    }
+    return it;
+  };
   const int tid = threadIdx.x;
-
+  int it = next_item(blockIdx.x);
+  if (it >= n_items) return;
+  Item cur = item_of(it);
   Gm gm;
-  gm.zero();
   // a tile wholly in its slice's padding (vlim <= 0) fetches no W row
-  gm.run(lds, hidden + (int64_t)row0 * H, H, T - row0, weight + (int64_t)col0 * H, H, vlim, 0, H);
-
+  gm.prologue(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0,
+              weight + (int64_t)cur.col0 * H, H, cur.vlim, 0, H);
   const int lane = tid & 63;
   const int wave = wave_id();
   const int wm = wave % WM, wn = wave / WM;
-  // logit gradient, rounded to bf16, into the [t][v] staging tile
-  bool cvalid[Gm::NJ];
-#pragma unroll
-  for (int j = 0; j < Gm::NJ; ++j) cvalid[j] = wn * Gm::WTN + 16 * j + (lane & 15) < vlim;
+  bool young = false;  // every wave has issued all of the previous tile's stores
 #pragma unroll 1
-  for (int i = 0; i < Gm::MI; ++i) {
-    f32x4 blk[Gm::NJ];
-    acc_row_block<0>(gm.acc, i, blk);
+  for (;;) {
+    // row constants of this tile (thread tid: row row0 + tid; rows past T
+    // take row T - 1 and are zeroed below), in flight during the mainloop
+    float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
+    if (tid < BM) {
+      const int t = cur.row0 + tid < T ? cur.row0 + tid : T - 1;
+      c0 = rowc[2 * t];
+      c1 = rowc[2 * t + 1];
+    }
+    gm.zero();
+    gm.template run<STORES>(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0,
+                            weight + (int64_t)cur.col0 * H, H, cur.vlim, 0, H,
+                            /*prefetched=*/true, young);
+    // run() ends with every load drained: the constants are settled here, so
+    // the compiler's wait for them never meets the next prologue's DMA
+    asm volatile("" : "+v"(c0.x), "+v"(c0.y), "+v"(c0.z), "+v"(c0.w), "+v"(c1.x), "+v"(c1.y),
+                 "+v"(c1.z), "+v"(c1.w));
+    const int nit = next_item(it + stride);
+    const bool more = nit < n_items;
+    const Item nxt = more ? item_of(nit) : cur;
+    if (more)
+      gm.prologue(lds, hidden + (int64_t)nxt.row0 * H, H, T - nxt.row0,
+                  weight + (int64_t)nxt.col0 * H, H, nxt.vlim, 0, H);
+
+    // ---- G of the current tile (LDS: A's and B's pair-1 slots only)
+    if (tid < BM) {
+      tab0[perm(tid)] = c0;
+      tab1[perm(tid)] = c1;
+    }
+    bool cvalid[Gm::NJ];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;
-      const int t = row0 + rl;
-      const bool rv = t < T;
-      const int tc = rv ? t : T - 1;  // rows past T load row T-1 and are zeroed below
-      const float4 c0 = rowc[2 * tc];
-      const float4 c1 = rowc[2 * tc + 1];
-      const float m = c0.x, L = c0.y, Hb = c0.z, dl = c0.w, de = c1.x;
-      const int yloc = __float_as_int(c1.y) - col0;
-      const float Rn = c1.z;  // R / (1 + R) = 1 - p at the row maximum
+    for (int j = 0; j < Gm::NJ; ++j) cvalid[j] = wn * Gm::WTN + 16 * j + (lane & 15) < cur.vlim;
+    const int c8 = (tid % TPR) * 8;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_only();  // the constants are in
+#pragma unroll 1
+    for (int i = 0; i < Gm::MI; ++i) {
+      // round i's buffer last held round i - 2, which every wave read out
+      // before the barrier of round i - 1
+      uint16_t* stg = reinterpret_cast<uint16_t*>(lds + ((DBL && (i & 1) == 0) ? OFF_A1 : OFF_B1));
+      f32x4 blk[Gm::NJ];
+      acc_row_block<0>(gm.acc, i, blk);
 #pragma unroll
-      for (int j = 0; j < Gm::NJ; j += 2) {
-        float gv[2];
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * Gm::WTM + 16 * i + 4 * (lane >> 4) + r;  // tile row
+        const int rr = wm * 16 + 4 * (lane >> 4) + r;                // round row
+        const bool rv = cur.row0 + rl < T;
+        const float4 q0 = tab0[perm(rl)];
+        const float4 q1 = tab1[perm(rl)];
+        const float m = q0.x, L = q0.y, Hb = q0.z, dl = q0.w, de = q1.x;
+        const int yloc = __float_as_int(q1.y) - cur.col0;
+        const float Rn = q1.z;  // R / (1 + R) = 1 - p at the row maximum
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int cl = wn * Gm::WTN + 16 * (j + u) + (lane & 15);
-          const float zd = blk[j + u][r] - m;
-          const float p = exp_fast(zd - L);
-          // [v == y] - p; at the target, 1 - p is exactly R/(1+R) when z_y is
-          // the row maximum (zd == 0) and has no cancellation otherwise (p <= 1/2)
-          const float omp = (zd == 0.f) ? Rn : 1.f - p;
-          const float onehot_term = (cl == yloc) ? omp : -p;
-          const float g = dl * onehot_term - de * (p * (zd + Hb));
-          gv[u] = (rv && cvalid[j + u]) ? g : 0.f;
+        for (int j = 0; j < Gm::NJ; j += 2) {
+          float gv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int cl = wn * Gm::WTN + 16 * (j + u) + (lane & 15);
+            const float zd = blk[j + u][r] - m;
+            const float p = exp_fast(zd - L);
+            // [v == y] - p; at the target, 1 - p is exactly R/(1+R) when z_y is
+            // the row maximum (zd == 0) and has no cancellation otherwise (p <= 1/2)
+            const float omp = (zd == 0.f) ? Rn : 1.f - p;
+            const float onehot_term = (cl == yloc) ? omp : -p;
+            const float g = dl * onehot_term - de * (p * (zd + Hb));
+            gv[u] = (rv && cvalid[j + u]) ? g : 0.f;
+          }
+          const uint32_t pk = pack_bf16x2(gv[0], gv[1]);
+          const int cl0 = wn * Gm::WTN + 16 * j + (lane & 15);
+          stg[rr * LDG_S + cl0] = (uint16_t)pk;
+          stg[rr * LDG_S + cl0 + 16] = (uint16_t)(pk >> 16);
         }
-        const uint32_t pk = pack_bf16x2(gv[0], gv[1]);
-        const int cl0 = wn * Gm::WTN + 16 * j + (lane & 15);
-        stg[rl * LDG_S + cl0] = (uint16_t)pk;
-        stg[rl * LDG_S + cl0 + 16] = (uint16_t)(pk >> 16);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier_only();
+      // the round's rows: round row k is tile row (k / 16) WTM + 16 i + k % 16
+#pragma unroll
+      for (int k0 = 0; k0 < 32; k0 += RPP) {
+        const int k = k0 + tid / TPR;
+        const int t = cur.row0 + (k >> 4) * Gm::WTM + 16 * i + (k & 15);
+        if (t < T) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + k * LDG_S + c8);
+          *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)cur.lg * BN + c8) = v;
+        }
       }
     }
+    young = cur.row0 + BM <= T;
+    if (!more) break;
+    it = nit;
+    cur = nxt;
   }
-  __syncthreads();
-  // gtv rows: BN / 8 threads per row, 16 B each
-  constexpr int TPR = BN / 8;
-  static_assert(kThreads % TPR == 0, "whole rows per pass");
-  const int c8 = (tid % TPR) * 8;
-  for (int rl = tid / TPR; rl < BM; rl += kThreads / TPR) {
-    const int t = row0 + rl;
-    if (t >= T) break;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * LDG_S + c8);
-    *reinterpret_cast<u32x4*>(gtv + (int64_t)t * ldg + (int64_t)lg * BN + c8) = v;
-  }
+  wait_vmcnt<0>();
 }
 
 // dW[chunk_v0 + v, h] = sum_t G[t, v] h[t, h], read straight from gtv [t][v]
@@ -970,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 #define RLK_RECOMPUTE(BM, BN, WM, WN)                                                          \
   template __global__ void bwd_recompute_kernel<BM, BN, WM, WN>(                               \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
-      int, const float4* __restrict__, uint16_t* __restrict__, int64_t);
+      int, int, const float4* __restrict__, uint16_t* __restrict__, int64_t);
 #define RLK_DH(BM, BN, WM, WN)                                                                \
   template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                       \
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, SplitMap, \
@@ -1068,6 +1151,8 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
              a.dentropy, a.targets, T, a.vocab_start, a.rowc);
   const bool small = T <= kSmallT;
   const int bm = small ? 32 : 256;
+  // persistent recompute: a multiple of 8 workgroups, one per CU for 256-row tiles
+  const int grid_cap = cdiv(a.n_cu > 0 ? a.n_cu : 256, 8) * 8;
   const int nt = cdiv(T, bm);
   const int nht = cdiv(H, 256);
   const SplitMap sm{p.Vs, p.Vs_pad, p.n_sub, p.split_w};
@@ -1081,12 +1166,18 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
       // many workgroups, so the last round is fuller
       constexpr int BN = 128;
       const int ntl = width / BN;
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, BN, 2, 2>), cdiv(ntl, 8) * 8 * nt, st,
-                 a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, a.rowc, a.gtv, p.ldg);
+      const int n_items = cdiv(ntl, 8) * 8 * nt;
+      // one item per workgroup (up to four resident per CU with 40 KB of LDS
+      // each): for these short tiles that beats a persistent walk
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, BN, 2, 2>), n_items,
+                 st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.rowc,
+                 a.gtv, p.ldg);
     } else {
       const int ntl = width / 256;
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2>), cdiv(ntl, 8) * 8 * nt, st,
-                 a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, a.rowc, a.gtv, p.ldg);
+      const int n_items = cdiv(ntl, 8) * 8 * nt;
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2>), min(grid_cap, n_items),
+                 st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.rowc,
+                 a.gtv, p.ldg);
     }
     const int nvt = width / 256;
     const int nhw = cdiv(H, kDwBN);
