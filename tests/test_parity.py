@@ -314,6 +314,35 @@ def test_qwen512_backward_entropy_sampled(qwen):
     check_column_sum(dw, "qwen512 (entropy term)")
 
 
+def test_persistent_recompute_whole_and_partial_tiles():
+    # T = 600 gives T-tiles of 256, 256 and 88 rows and V = 40000 gives 480
+    # recompute items for a grid of 256 workgroups, so a workgroup's two tiles
+    # are of different T-tiles: a whole tile after a partial one and the other
+    # way round. The next mainloop may start with the previous tile's G stores
+    # still in flight only after a whole tile; every path must give the
+    # oracle's gradients, and dH rows the bits of a 256-row call.
+    c = wl.make_case("recompute_mix", 600, 128, 40000, seed=77, rms=True)
+    d = case_to_device(c)
+    o = run_fwd(d)
+    dh, dw = rlk.bwd(d["hidden"], d["weight"], d["targets"], o["stats"], d["dlogp"], None)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(78)
+    drow = np.unique(np.concatenate([torch.randperm(c.T, generator=g)[:40].numpy(),
+                                     np.array([0, 255, 256, 511, 512, 599])]))
+    vrows = np.unique(np.concatenate([torch.randperm(c.V, generator=g)[:96].numpy(),
+                                      c.targets[drow].numpy(), np.array([0, c.V - 1])]))
+    rb = backward(c.hidden, c.weight, c.targets, c.dlogp, None, dh_rows=drow, dw_rows=vrows,
+                  with_abs=True)
+    check_backward(dh[torch.from_numpy(drow).cuda()], dw[torch.from_numpy(vrows).cuda()], rb,
+                   c.T, c.V, "T600 V40000 rows")
+    check_column_sum(dw, "T600 V40000")
+    sub = {k: v[:256].contiguous() for k, v in d.items() if k in ("hidden", "targets", "dlogp")}
+    o2 = rlk.fwd(sub["hidden"], d["weight"], sub["targets"])
+    dh2, _ = rlk.bwd(sub["hidden"], d["weight"], sub["targets"], o2["stats"], sub["dlogp"], None)
+    torch.cuda.synchronize()
+    assert bits_equal(dh2, dh[:256]), "dH rows of the first 256 tokens differ from a 256-row call"
+
+
 # ------------------------------------------ full size: T = 5208 (full step)
 
 @pytest.mark.slow
