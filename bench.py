@@ -117,6 +117,44 @@ def timed(torch, fn, warmup, steps):
     return per, ev[0].elapsed_time(ev[steps])
 
 
+def graph_timed(torch, fn, outs, inner, reps):
+    """GPU-side time per call (ms) of a short call: `inner` calls captured in
+    one graph and replayed `reps` times, each replay timed by HIP events. Calls
+    this short are issued faster by the GPU than by the Python loop that
+    launches them, so per-call events from an eager loop would time the host.
+    Every replay's outputs (the tensors in `outs`, written in place) must equal
+    the eager call's bits. Returns (per-call times, bits equal on every replay)."""
+    fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(inner):
+                fn()
+    torch.cuda.synchronize()
+    per, same = [], True
+    for _ in range(reps):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / inner)
+        same = same and all(torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else
+                                        o.view(torch.int32), r.view(torch.int16)
+                                        if r.dtype == torch.bfloat16 else r.view(torch.int32))
+                            for o, r in zip(outs, ref))
+    del g
+    return per, same
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "cu_count": p.multi_processor_count,
@@ -372,9 +410,20 @@ def workload_runs(torch, rlk, wl, read_gbs, steps):
         yb = torch.empty(c.T, c.N, dtype=torch.bfloat16, device="cuda:0")
         ws = torch.empty(max(256, rlk.load_library().rlk_lora_linear_workspace_bytes(
             c.T, c.K, c.N, c.r)), dtype=torch.uint8, device="cuda:0")
-        per_f, _ = timed(torch, lambda: rlk.lora_fwd(x, W, A, B, 2.0, out=yb, ws=ws), 3, steps)
-        per_b, _ = timed(torch, lambda: (rlk.lora_fwd(x, W, A, B, 2.0, out=yb, ws=ws),
-                                         rlk.lora_bwd(x, W, A, B, dy, 2.0, ws=ws)), 3, steps)
+        dxb = torch.empty(c.T, c.K, dtype=torch.bfloat16, device="cuda:0")
+        dab = torch.empty(c.r, c.K, dtype=torch.float32, device="cuda:0")
+        dbb = torch.empty(c.N, c.r, dtype=torch.float32, device="cuda:0")
+
+        def fwd_bwd():
+            rlk.lora_fwd(x, W, A, B, 2.0, out=yb, ws=ws)
+            rlk.lora_bwd(x, W, A, B, dy, 2.0, ws=ws, out=(dxb, dab, dbb))
+
+        # eager per-call events (host-paced for calls this short), then the
+        # GPU-side time from replayed graphs, which the roofline uses
+        per_fe, _ = timed(torch, lambda: rlk.lora_fwd(x, W, A, B, 2.0, out=yb, ws=ws), 3, steps)
+        per_f, same_f = graph_timed(torch, lambda: rlk.lora_fwd(x, W, A, B, 2.0, out=yb, ws=ws),
+                                    [yb], 20, steps)
+        per_b, same_b = graph_timed(torch, fwd_bwd, [yb, dxb, dab, dbb], 20, steps)
         mf, mb = median_ci(per_f), median_ci(per_b)
         wbytes = 2 * c.N * c.K
         # algorithmic work of the forward: every operand read once, y written once
@@ -386,6 +435,9 @@ def workload_runs(torch, rlk, wl, read_gbs, steps):
         achieved = (fflops / secs / 1e12) if bound == "mfma" else (fbytes / secs / 1e9)
         peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
         lora[c.name] = {"rank": c.r, "fwd_ms": mf, "fwd_bwd_ms": mb,
+                        "timing": "graph of 20 calls replayed (GPU-side time per call)",
+                        "graph_replays_bit_equal": bool(same_f and same_b),
+                        "fwd_ms_eager_per_call_events": median_ci(per_fe),
                         "fwd_W_GBps": round(wbytes / secs / 1e9, 1),
                         "fwd_TFLOPs": round(2 * c.T * c.K * c.N / secs / 1e12, 2),
                         "fwd_roofline": {"bound": bound, "bytes": fbytes, "flops": fflops,

@@ -503,6 +503,8 @@ def lora_fwd(x, W, A, B, scale: float = 1.0, out: torch.Tensor | None = None, ws
     """y = x W^T + scale (x A^T) B^T through ``rlk_lora_linear_fwd`` (bf16 [T,N])."""
     lib = load_library()
     T, K, N, r = _lora_check(x, W, A, B)
+    if out is not None:
+        _lora_out(out, (T, N), torch.bfloat16, x.device, "out")
     y = out if out is not None else torch.empty(T, N, dtype=torch.bfloat16, device=x.device)
     nws = lib.rlk_lora_linear_workspace_bytes(T, K, N, r)
     ws = ws if ws is not None and ws.numel() >= nws else _workspace(nws, x.device)
@@ -511,18 +513,34 @@ def lora_fwd(x, W, A, B, scale: float = 1.0, out: torch.Tensor | None = None, ws
     return y
 
 
+def _lora_out(t, shape, dtype, device, what):
+    if (not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device
+            or not t.is_contiguous() or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor {list(shape)} on {device}")
+
+
 def lora_bwd(x, W, A, B, dy, scale: float = 1.0, *, want_dx=True, want_da=True, want_db=True,
-             ws=None):
+             ws=None, out=None):
     """(dx bf16 [T,K], dA fp32 [r,K], dB fp32 [N,r]) through ``rlk_lora_linear_bwd``;
-    None where not wanted. W is frozen: no gradient."""
+    None where not wanted. W is frozen: no gradient. ``out``: optional
+    (dx, dA, dB) tensors of those shapes to write into (each of them used only
+    where wanted)."""
     lib = load_library()
     T, K, N, r = _lora_check(x, W, A, B)
     if dy.dtype != torch.bfloat16 or not dy.is_cuda or not dy.is_contiguous() or dy.shape != (T, N):
         raise ValueError("dy must be a contiguous bfloat16 device tensor [T, N]")
     dev = x.device
-    dx = torch.empty(T, K, dtype=torch.bfloat16, device=dev) if want_dx else None
-    da = torch.empty(r, K, dtype=torch.float32, device=dev) if want_da else None
-    db = torch.empty(N, r, dtype=torch.float32, device=dev) if want_db else None
+    if out is not None:
+        odx, oda, odb = out
+        _lora_out(odx, (T, K), torch.bfloat16, dev, "out dx")
+        _lora_out(oda, (r, K), torch.float32, dev, "out dA")
+        _lora_out(odb, (N, r), torch.float32, dev, "out dB")
+    dx = (odx if out is not None else torch.empty(T, K, dtype=torch.bfloat16, device=dev)) \
+        if want_dx else None
+    da = (oda if out is not None else torch.empty(r, K, dtype=torch.float32, device=dev)) \
+        if want_da else None
+    db = (odb if out is not None else torch.empty(N, r, dtype=torch.float32, device=dev)) \
+        if want_db else None
     nws = lib.rlk_lora_linear_workspace_bytes(T, K, N, r)
     ws = ws if ws is not None and ws.numel() >= nws else _workspace(nws, dev)
     _check(lib.rlk_lora_linear_bwd(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(dy), T, K, N, r,

@@ -44,12 +44,11 @@ inline int lora_ksplit(int64_t K) {
 // wave per pair: lane l sums (fused multiply-adds) elements 8 l + 512 m + e,
 // m and e ascending, then a 64-lane xor tree; every lane ends with the same
 // bits. Q(j, i) = Q[j][i] (QROW: A [r][K]) or Q[i][j] (B [N][r]).
+// One wave computes pair w (whole waves; w >= T * r does nothing).
 template <bool QROW>
-__global__ __launch_bounds__(kThreads) void lora_rowdot_kernel(const uint16_t* __restrict__ P,
-                                                               const uint16_t* __restrict__ Q,
-                                                               int T, int L, int r,
-                                                               float* __restrict__ out) {
-  const int w = (int)blockIdx.x * (kThreads / 64) + wave_id();
+__device__ __forceinline__ void rowdot_wave(const uint16_t* __restrict__ P,
+                                            const uint16_t* __restrict__ Q, int T, int L, int r,
+                                            float* __restrict__ out, int w) {
   if (w >= T * r) return;  // whole waves
   const int t = w / r, j = w - t * r;
   const int lane = threadIdx.x & 63;
@@ -81,6 +80,27 @@ __global__ __launch_bounds__(kThreads) void lora_rowdot_kernel(const uint16_t* _
   for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_xor(acc, off);
   if (lane == 0) out[w] = acc;
 }
+
+template <bool QROW>
+__global__ __launch_bounds__(kThreads) void lora_rowdot_kernel(const uint16_t* __restrict__ P,
+                                                               const uint16_t* __restrict__ Q,
+                                                               int T, int L, int r,
+                                                               float* __restrict__ out) {
+  rowdot_wave<QROW>(P, Q, T, L, r, out, (int)blockIdx.x * (kThreads / 64) + wave_id());
+}
+
+// Rank-r codes computed by extra workgroups of a product launch whose tiles
+// do not read them (a split contraction: only the reduce does), so they need
+// no launch of their own: out[t][j] = sum_i P[t][i] Q(j, i) exactly as
+// lora_rowdot_kernel<QROW> computes it, by `wgs` workgroups (0: none).
+struct RowdotJob {
+  const uint16_t* P;
+  const uint16_t* Q;
+  int L;
+  float* out;
+  int wgs;
+};
+inline int rowdot_wgs(int64_t T, int64_t r) { return (int)((T * r + 3) / 4); }
 
 // Epilogue of a 64 x BN tile: out = bf16(acc + s * sum_j c[row][j] f[j][col]),
 // c = the rows' rank-r codes (fp32 [T][r]), f = the adapter factor's columns
@@ -126,13 +146,21 @@ __device__ __forceinline__ void lora_epilogue(const Gm& gm, unsigned char* lds,
 // y tile (64 tokens x BN outputs): x W^T on the MFMA mainloop, then + s u B^T.
 // With S > 1 splits of K the tile covers K split ks and writes its fp32
 // partial to part[ks][t][n] instead (lora_fwd_reduce_kernel finishes y).
+// Workgroups past the tiles (n_ttiles * n_ntiles * S of them) run the job ju
+// (the rows' codes u, with S > 1 only).
 template <int BN>
 __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, const float* __restrict__ u,
     const uint16_t* __restrict__ B, int T, int K, int N, int r, float scale, int n_ttiles,
-    int n_ntiles, int S, uint16_t* __restrict__ y, float* __restrict__ part) {
+    int n_ntiles, int S, uint16_t* __restrict__ y, float* __restrict__ part, RowdotJob ju) {
   using Gm = LoraFwdGemm<BN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
+  const int n_main = n_ttiles * n_ntiles * S;
+  if ((int)blockIdx.x >= n_main) {
+    rowdot_wave<true>(ju.P, ju.Q, T, ju.L, r, ju.out,
+                      ((int)blockIdx.x - n_main) * (kThreads / 64) + wave_id());
+    return;
+  }
   const int tt = (int)blockIdx.x % n_ttiles, rest = (int)blockIdx.x / n_ttiles;
   const int nt = rest % n_ntiles, ks = rest / n_ntiles;
   const int row0 = tt * kLoraBM, col0 = nt * BN;
@@ -201,11 +229,24 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_reduce_kernel(
 // splits of the contraction over N (fixed by N alone) the tile covers split
 // ns and writes its fp32 partial to part[ns][t][k]; lora_dx_reduce_kernel
 // finishes dx.
+// Workgroups past the tiles run the job jv (the codes v = dy B), then ju
+// (u = x A^T), with S > 1 only.
 __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ W, const float* __restrict__ v,
     const uint16_t* __restrict__ A, int T, int K, int N, int r, float scale, int n_ttiles,
-    int n_ktiles, int S, uint16_t* __restrict__ dx, float* __restrict__ part) {
+    int n_ktiles, int S, uint16_t* __restrict__ dx, float* __restrict__ part, RowdotJob jv,
+    RowdotJob ju) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[LoraDxGemm::LDS_BYTES];
+  const int n_main = n_ttiles * n_ktiles * S;
+  if ((int)blockIdx.x >= n_main) {
+    const int b = (int)blockIdx.x - n_main;
+    if (b < jv.wgs)
+      rowdot_wave<false>(jv.P, jv.Q, T, jv.L, r, jv.out, b * (kThreads / 64) + wave_id());
+    else
+      rowdot_wave<true>(ju.P, ju.Q, T, ju.L, r, ju.out,
+                        (b - jv.wgs) * (kThreads / 64) + wave_id());
+    return;
+  }
   const int tt = (int)blockIdx.x % n_ttiles, rest = (int)blockIdx.x / n_ttiles;
   const int kt = rest % n_ktiles, ns = rest / n_ktiles;
   const int row0 = tt * kLoraBM, c0 = kt * kLoraBN;
@@ -371,28 +412,34 @@ RLK_API rlk_status rlk_lora_linear_fwd(const void* x, const void* weight, const 
   float* u = static_cast<float*>(workspace);
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          (size_t(2) * T * r * 4 + 255) / 256 * 256);
-  hipLaunchKernelGGL(rlk::lora_rowdot_kernel<true>, dim3(rlk::cdiv_i(T * r, 4)), dim3(rlk::kThreads),
-                     0, st, xb, Ab, (int)T, (int)K, (int)r, u);
   const int nt = rlk::cdiv_i(T, rlk::kLoraBM);
   const int S = rlk::lora_ksplit(K);
   uint16_t* yb = static_cast<uint16_t*>(y);
+  // u = x A^T: with S > 1 only the reduce reads it, so extra workgroups of
+  // the product launch compute it; with S = 1 the tiles' epilogue needs it first
+  rlk::RowdotJob ju{xb, Ab, (int)K, u, 0};
+  if (S > 1)
+    ju.wgs = rlk::rowdot_wgs(T, r);
+  else
+    hipLaunchKernelGGL(rlk::lora_rowdot_kernel<true>, dim3(rlk::rowdot_wgs(T, r)),
+                       dim3(rlk::kThreads), 0, st, xb, Ab, (int)T, (int)K, (int)r, u);
   // narrower tiles when the wide ones would leave most compute units idle
   // (the tile width does not change any element's arithmetic)
   if ((int64_t)nt * rlk::cdiv_i(N, rlk::kLoraBN) * S >= 256) {
     const int nn = rlk::cdiv_i(N, rlk::kLoraBN);
-    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBN>, dim3(nt * nn * S), dim3(rlk::kThreads),
-                       0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r, scale, nt, nn, S, yb,
-                       part);
+    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBN>, dim3(nt * nn * S + ju.wgs),
+                       dim3(rlk::kThreads), 0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r,
+                       scale, nt, nn, S, yb, part, ju);
   } else if ((int64_t)nt * rlk::cdiv_i(N, rlk::kLoraBNm) * S >= 256) {
     const int nn = rlk::cdiv_i(N, rlk::kLoraBNm);
-    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBNm>, dim3(nt * nn * S), dim3(rlk::kThreads),
-                       0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r, scale, nt, nn, S, yb,
-                       part);
+    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBNm>, dim3(nt * nn * S + ju.wgs),
+                       dim3(rlk::kThreads), 0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r,
+                       scale, nt, nn, S, yb, part, ju);
   } else {
     const int nn = rlk::cdiv_i(N, rlk::kLoraBNs);
-    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBNs>, dim3(nt * nn * S), dim3(rlk::kThreads),
-                       0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r, scale, nt, nn, S, yb,
-                       part);
+    hipLaunchKernelGGL(rlk::lora_fwd_kernel<rlk::kLoraBNs>, dim3(nt * nn * S + ju.wgs),
+                       dim3(rlk::kThreads), 0, st, xb, Wb, u, Bb, (int)T, (int)K, (int)N, (int)r,
+                       scale, nt, nn, S, yb, part, ju);
   }
   if (S > 1)
     hipLaunchKernelGGL(rlk::lora_fwd_reduce_kernel, dim3(T * rlk::cdiv_i(N, rlk::kThreads)),
@@ -433,22 +480,31 @@ RLK_API rlk_status rlk_lora_linear_bwd(const void* x, const void* weight, const 
   const auto* dyb = static_cast<const uint16_t*>(dy);
   float* u = static_cast<float*>(workspace);
   float* v = u + T * r;
-  const dim3 pairs(rlk::cdiv_i(T * r, 4));
-  if (dx || da)
-    hipLaunchKernelGGL(rlk::lora_rowdot_kernel<false>, pairs, dim3(rlk::kThreads), 0, st, dyb, Bb,
-                       (int)T, (int)N, (int)r, v);
-  if (db)
-    hipLaunchKernelGGL(rlk::lora_rowdot_kernel<true>, pairs, dim3(rlk::kThreads), 0, st, xb, Ab,
-                       (int)T, (int)K, (int)r, u);
+  const dim3 pairs(rlk::rowdot_wgs(T, r));
+  // v = dy B and u = x A^T: with a split contraction of dx (Sx > 1) its tiles
+  // do not read v, so extra workgroups of the dx launch compute both
+  const int Sx = rlk::lora_ksplit(N);
+  const bool fold = dx && Sx > 1;
+  rlk::RowdotJob jv{dyb, Bb, (int)N, v, 0}, ju{xb, Ab, (int)K, u, 0};
+  if (fold) {
+    jv.wgs = rlk::rowdot_wgs(T, r);
+    if (db) ju.wgs = rlk::rowdot_wgs(T, r);
+  } else {
+    if (dx || da)
+      hipLaunchKernelGGL(rlk::lora_rowdot_kernel<false>, pairs, dim3(rlk::kThreads), 0, st, dyb,
+                         Bb, (int)T, (int)N, (int)r, v);
+    if (db)
+      hipLaunchKernelGGL(rlk::lora_rowdot_kernel<true>, pairs, dim3(rlk::kThreads), 0, st, xb,
+                         Ab, (int)T, (int)K, (int)r, u);
+  }
   if (dx) {
     const int nt = rlk::cdiv_i(T, rlk::kLoraBM);
     const int nk = rlk::cdiv_i(K, rlk::kLoraBN);
-    const int Sx = rlk::lora_ksplit(N);
     float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            (size_t(2) * T * r * 4 + 255) / 256 * 256);
-    hipLaunchKernelGGL(rlk::lora_dx_kernel, dim3(nt * nk * Sx), dim3(rlk::kThreads), 0, st, dyb,
-                       Wb, v, Ab, (int)T, (int)K, (int)N, (int)r, scale, nt, nk, Sx,
-                       static_cast<uint16_t*>(dx), part);
+    hipLaunchKernelGGL(rlk::lora_dx_kernel, dim3(nt * nk * Sx + jv.wgs + ju.wgs),
+                       dim3(rlk::kThreads), 0, st, dyb, Wb, v, Ab, (int)T, (int)K, (int)N,
+                       (int)r, scale, nt, nk, Sx, static_cast<uint16_t*>(dx), part, jv, ju);
     if (Sx > 1)
       hipLaunchKernelGGL(rlk::lora_dx_reduce_kernel, dim3(T * rlk::cdiv_i(K, rlk::kThreads)),
                          dim3(rlk::kThreads), 0, st, part, v, Ab, (int)T, (int)K, (int)r, Sx, scale,

@@ -196,3 +196,48 @@ def test_small_batch_split_forward_matches_tiles_bitwise(N, K, T):
     yn = rlk.lora_fwd(xs, W, A, B, 1.25, ws=ws.view(torch.uint8))
     torch.cuda.synchronize()
     assert bits_equal(yn, ys), "a stale workspace changed the result"
+
+
+def test_outputs_into_caller_buffers_and_graph_replay():
+    # out= buffers receive the same bits as fresh outputs, wrong ones are
+    # refused before anything runs, and a graph of captured calls replays to
+    # the eager bits every time (the timing path of the LoRA bench lines).
+    c = wl.lora_page_cases()[2]  # N5120 K5120 T33: split contractions both ways
+    x, W, A, B, dy = (dev(t) for t in (c.x, c.W, c.A, c.B, c.dy))
+    y = rlk.lora_fwd(x, W, A, B, 2.0)
+    dx, da, db = rlk.lora_bwd(x, W, A, B, dy, 2.0)
+    yo = torch.empty_like(y)
+    outs = (torch.empty_like(dx), torch.empty_like(da), torch.empty_like(db))
+    rlk.lora_fwd(x, W, A, B, 2.0, out=yo)
+    rlk.lora_bwd(x, W, A, B, dy, 2.0, out=outs)
+    torch.cuda.synchronize()
+    assert bits_equal(yo, y)
+    for a, b in zip(outs, (dx, da, db)):
+        assert bits_equal(a, b)
+    with pytest.raises(ValueError):
+        rlk.lora_fwd(x, W, A, B, 2.0, out=torch.empty(c.T, c.N + 64, dtype=torch.bfloat16,
+                                                       device="cuda"))
+    with pytest.raises(ValueError):
+        rlk.lora_bwd(x, W, A, B, dy, 2.0, out=(outs[0], outs[1].t(), outs[2]))
+    nws = rlk.load_library().rlk_lora_linear_workspace_bytes(c.T, c.K, c.N, c.r)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(3):
+                rlk.lora_fwd(x, W, A, B, 2.0, out=yo, ws=ws)
+                rlk.lora_bwd(x, W, A, B, dy, 2.0, ws=ws, out=outs)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in (yo, *outs):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bits_equal(yo, y)
+        for a, b in zip(outs, (dx, da, db)):
+            assert bits_equal(a, b)
+        rlk.lora_fwd(x, W, A, B, 0.5)  # eager work between the replays
+    del g
