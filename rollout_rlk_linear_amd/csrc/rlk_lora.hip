@@ -81,18 +81,8 @@ __device__ __forceinline__ void rowdot_wave(const uint16_t* __restrict__ P,
   if (lane == 0) out[w] = acc;
 }
 
-template <bool QROW>
-__global__ __launch_bounds__(kThreads) void lora_rowdot_kernel(const uint16_t* __restrict__ P,
-                                                               const uint16_t* __restrict__ Q,
-                                                               int T, int L, int r,
-                                                               float* __restrict__ out) {
-  rowdot_wave<QROW>(P, Q, T, L, r, out, (int)blockIdx.x * (kThreads / 64) + wave_id());
-}
-
-// Rank-r codes computed by extra workgroups of a product launch whose tiles
-// do not read them (a split contraction: only the reduce does), so they need
-// no launch of their own: out[t][j] = sum_i P[t][i] Q(j, i) exactly as
-// lora_rowdot_kernel<QROW> computes it, by `wgs` workgroups (0: none).
+// A rank-r code job: out[t][j] = sum_i P[t][i] Q(j, i) for the T x r pairs,
+// by `wgs` workgroups of four waves (0: none).
 struct RowdotJob {
   const uint16_t* P;
   const uint16_t* Q;
@@ -101,6 +91,19 @@ struct RowdotJob {
   int wgs;
 };
 inline int rowdot_wgs(int64_t T, int64_t r) { return (int)((T * r + 3) / 4); }
+
+// The codes v = dy B (job jv, Q = B [N][r]) and u = x A^T (job ju, Q = A
+// [r][K]) in one launch: workgroups 0 .. jv.wgs - 1 take jv, the rest ju. A
+// split product launch runs the same jobs in extra workgroups of its own
+// instead (its tiles do not read the codes; only its reduce does).
+__global__ __launch_bounds__(kThreads) void lora_codes_kernel(int T, int r, RowdotJob jv,
+                                                              RowdotJob ju) {
+  const int b = (int)blockIdx.x;
+  if (b < jv.wgs)
+    rowdot_wave<false>(jv.P, jv.Q, T, jv.L, r, jv.out, b * (kThreads / 64) + wave_id());
+  else
+    rowdot_wave<true>(ju.P, ju.Q, T, ju.L, r, ju.out, (b - jv.wgs) * (kThreads / 64) + wave_id());
+}
 
 // Epilogue of a 64 x BN tile: out = bf16(acc + s * sum_j c[row][j] f[j][col]),
 // c = the rows' rank-r codes (fp32 [T][r]), f = the adapter factor's columns
@@ -207,9 +210,24 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_reduce_kernel(
   for (int ks = 1; ks < S; ++ks) acc = acc + part[(int64_t)ks * n_el + i];
   const float* ut = u + (int64_t)t * r;
   const uint16_t* Bn = B + (int64_t)n * r;
-  // the same ascending chain, its operands loaded four at a time ahead of it
+  // the same ascending chain, its operands loaded ahead of it: B's row in
+  // 16-byte pieces when r is a multiple of 8 (the row then starts 16-byte
+  // aligned), else four elements at a time
   float term = 0.f;
   int j = 0;
+  if ((r & 7) == 0) {
+    for (; j < r; j += 8) {
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(Bn + j);
+      float bb[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bb[2 * e] = bf16_to_f32(bv[e] & 0xffffu);
+        bb[2 * e + 1] = bf16_to_f32(bv[e] >> 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) term = fmaf(ut[j + e], bb[e], term);
+    }
+  }
   for (; j + 4 <= r; j += 4) {
     float uu[4], bb[4];
 #pragma unroll
@@ -307,51 +325,51 @@ __global__ __launch_bounds__(kThreads) void lora_dx_reduce_kernel(
   dx[i] = (uint16_t)f32_to_bf16_rne(acc + scale * term);
 }
 
-// dA[j][k] = s * (fused multiply-add chain over t ascending of v[t][j] x[t][k]).
-__global__ __launch_bounds__(kThreads) void lora_da_kernel(const float* __restrict__ v,
-                                                           const uint16_t* __restrict__ x, int T,
-                                                           int K, int r, float scale,
-                                                           float* __restrict__ da) {
-  const int k = (int)blockIdx.x * kThreads + threadIdx.x;
-  const int j = (int)blockIdx.y;
-  if (k >= K) return;
-  // the ascending chain, its operands loaded eight at a time ahead of it
-  float acc = 0.f;
-  int t = 0;
-  for (; t + 8 <= T; t += 8) {
-    float a[8], b[8];
+// dA[j][k] = s * (fused multiply-add chain over t ascending of v[t][j] x[t][k]),
+// and dB[n][j] = s * (the same over dy[t][n] u[t][j]), in one launch: the
+// first da_blocks workgroups take dA (workgroup b: column block b % kb of row
+// j = b / kb, kb = ceil(K / 256)), the rest dB (one output a thread).
+__global__ __launch_bounds__(kThreads) void lora_dadb_kernel(
+    const float* __restrict__ v, const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
+    const float* __restrict__ u, int T, int K, int N, int r, float scale, int da_blocks,
+    float* __restrict__ da, float* __restrict__ db) {
+  const int b = (int)blockIdx.x;
+  if (b < da_blocks) {
+    const int kb = (K + kThreads - 1) / kThreads;
+    const int j = b / kb;
+    const int k = (b - j * kb) * kThreads + (int)threadIdx.x;
+    if (k >= K) return;
+    // the ascending chain, its operands loaded eight at a time ahead of it
+    float acc = 0.f;
+    int t = 0;
+    for (; t + 8 <= T; t += 8) {
+      float a[8], c[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      a[e] = v[(int64_t)(t + e) * r + j];
-      b[e] = bf16_to_f32(x[(int64_t)(t + e) * K + k]);
+      for (int e = 0; e < 8; ++e) {
+        a[e] = v[(int64_t)(t + e) * r + j];
+        c[e] = bf16_to_f32(x[(int64_t)(t + e) * K + k]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(a[e], c[e], acc);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
+    for (; t < T; ++t) acc = fmaf(v[(int64_t)t * r + j], bf16_to_f32(x[(int64_t)t * K + k]), acc);
+    da[(int64_t)j * K + k] = scale * acc;
+    return;
   }
-  for (; t < T; ++t) acc = fmaf(v[(int64_t)t * r + j], bf16_to_f32(x[(int64_t)t * K + k]), acc);
-  da[(int64_t)j * K + k] = scale * acc;
-}
-
-// dB[n][j] = s * (fused multiply-add chain over t ascending of dy[t][n] u[t][j]).
-__global__ __launch_bounds__(kThreads) void lora_db_kernel(const uint16_t* __restrict__ dy,
-                                                           const float* __restrict__ u, int T,
-                                                           int N, int r, float scale,
-                                                           float* __restrict__ db) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t i = (int64_t)(b - da_blocks) * kThreads + threadIdx.x;
   if (i >= (int64_t)N * r) return;
   const int n = (int)(i / r), j = (int)(i - (int64_t)n * r);
-  // the ascending chain, its operands loaded eight at a time ahead of it
   float acc = 0.f;
   int t = 0;
   for (; t + 8 <= T; t += 8) {
-    float a[8], b[8];
+    float a[8], c[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       a[e] = bf16_to_f32(dy[(int64_t)(t + e) * N + n]);
-      b[e] = u[(int64_t)(t + e) * r + j];
+      c[e] = u[(int64_t)(t + e) * r + j];
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(a[e], b[e], acc);
+    for (int e = 0; e < 8; ++e) acc = fmaf(a[e], c[e], acc);
   }
   for (; t < T; ++t) acc = fmaf(bf16_to_f32(dy[(int64_t)t * N + n]), u[(int64_t)t * r + j], acc);
   db[i] = scale * acc;
@@ -417,12 +435,13 @@ RLK_API rlk_status rlk_lora_linear_fwd(const void* x, const void* weight, const 
   uint16_t* yb = static_cast<uint16_t*>(y);
   // u = x A^T: with S > 1 only the reduce reads it, so extra workgroups of
   // the product launch compute it; with S = 1 the tiles' epilogue needs it first
-  rlk::RowdotJob ju{xb, Ab, (int)K, u, 0};
-  if (S > 1)
-    ju.wgs = rlk::rowdot_wgs(T, r);
-  else
-    hipLaunchKernelGGL(rlk::lora_rowdot_kernel<true>, dim3(rlk::rowdot_wgs(T, r)),
-                       dim3(rlk::kThreads), 0, st, xb, Ab, (int)T, (int)K, (int)r, u);
+  rlk::RowdotJob ju{xb, Ab, (int)K, u, rlk::rowdot_wgs(T, r)};
+  if (S == 1) {
+    const rlk::RowdotJob none{nullptr, nullptr, 0, nullptr, 0};
+    hipLaunchKernelGGL(rlk::lora_codes_kernel, dim3(ju.wgs), dim3(rlk::kThreads), 0, st, (int)T,
+                       (int)r, none, ju);
+    ju.wgs = 0;
+  }
   // narrower tiles when the wide ones would leave most compute units idle
   // (the tile width does not change any element's arithmetic)
   if ((int64_t)nt * rlk::cdiv_i(N, rlk::kLoraBN) * S >= 256) {
@@ -480,22 +499,18 @@ RLK_API rlk_status rlk_lora_linear_bwd(const void* x, const void* weight, const 
   const auto* dyb = static_cast<const uint16_t*>(dy);
   float* u = static_cast<float*>(workspace);
   float* v = u + T * r;
-  const dim3 pairs(rlk::rowdot_wgs(T, r));
-  // v = dy B and u = x A^T: with a split contraction of dx (Sx > 1) its tiles
-  // do not read v, so extra workgroups of the dx launch compute both
+  // v = dy B (for dx and dA) and u = x A^T (for dB): with a split
+  // contraction of dx (Sx > 1) its tiles do not read v, so extra workgroups
+  // of the dx launch compute both; otherwise one launch of their own
   const int Sx = rlk::lora_ksplit(N);
   const bool fold = dx && Sx > 1;
-  rlk::RowdotJob jv{dyb, Bb, (int)N, v, 0}, ju{xb, Ab, (int)K, u, 0};
-  if (fold) {
-    jv.wgs = rlk::rowdot_wgs(T, r);
-    if (db) ju.wgs = rlk::rowdot_wgs(T, r);
-  } else {
-    if (dx || da)
-      hipLaunchKernelGGL(rlk::lora_rowdot_kernel<false>, pairs, dim3(rlk::kThreads), 0, st, dyb,
-                         Bb, (int)T, (int)N, (int)r, v);
-    if (db)
-      hipLaunchKernelGGL(rlk::lora_rowdot_kernel<true>, pairs, dim3(rlk::kThreads), 0, st, xb,
-                         Ab, (int)T, (int)K, (int)r, u);
+  rlk::RowdotJob jv{dyb, Bb, (int)N, v, (dx || da) ? rlk::rowdot_wgs(T, r) : 0};
+  rlk::RowdotJob ju{xb, Ab, (int)K, u, db ? rlk::rowdot_wgs(T, r) : 0};
+  if (!fold) {
+    if (jv.wgs + ju.wgs > 0)
+      hipLaunchKernelGGL(rlk::lora_codes_kernel, dim3(jv.wgs + ju.wgs), dim3(rlk::kThreads), 0,
+                         st, (int)T, (int)r, jv, ju);
+    jv.wgs = ju.wgs = 0;
   }
   if (dx) {
     const int nt = rlk::cdiv_i(T, rlk::kLoraBM);
@@ -510,12 +525,12 @@ RLK_API rlk_status rlk_lora_linear_bwd(const void* x, const void* weight, const 
                          dim3(rlk::kThreads), 0, st, part, v, Ab, (int)T, (int)K, (int)r, Sx, scale,
                          static_cast<uint16_t*>(dx));
   }
-  if (da)
-    hipLaunchKernelGGL(rlk::lora_da_kernel, dim3(rlk::cdiv_i(K, rlk::kThreads), (unsigned)r),
-                       dim3(rlk::kThreads), 0, st, v, xb, (int)T, (int)K, (int)r, scale, da);
-  if (db)
-    hipLaunchKernelGGL(rlk::lora_db_kernel, dim3(rlk::cdiv_i(N * r, rlk::kThreads)),
-                       dim3(rlk::kThreads), 0, st, dyb, u, (int)T, (int)N, (int)r, scale, db);
+  const int da_blocks = da ? rlk::cdiv_i(K, rlk::kThreads) * (int)r : 0;
+  const int db_blocks = db ? rlk::cdiv_i(N * r, rlk::kThreads) : 0;
+  if (da_blocks + db_blocks > 0)
+    hipLaunchKernelGGL(rlk::lora_dadb_kernel, dim3(da_blocks + db_blocks), dim3(rlk::kThreads), 0,
+                       st, v, xb, dyb, u, (int)T, (int)K, (int)N, (int)r, scale, da_blocks, da,
+                       db);
   return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 
