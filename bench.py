@@ -82,7 +82,6 @@ def algorithmic_work(T, H, V, nsplits):
         "bwd_dw": (f, Gt + h + 4.0 * V * H),
         "bwd_dh": (f, Gt + W + 4.0 * nsplits * T * H),
         "fwd_combine": (0.0, T * G * 16.0 + T * 4 * 6.0),
-        "bwd_rowprep": (0.0, T * (16 + 12 + 32.0)),
         "bwd_dh_reduce": (0.0, nsplits * T * H * 4.0 + T * H * 2.0),
     }
 

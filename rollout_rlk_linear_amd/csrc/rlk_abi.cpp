@@ -127,8 +127,8 @@ namespace rlk {
 int check_device_status() { return (int)check_device(); }
 
 const char* const kKernelNames[K_COUNT] = {
-    "fwd_tile",  "fwd_combine", "bwd_rowprep", "bwd_recompute", "bwd_dw",     "bwd_dh",
-    "bwd_dh_reduce", "fill_zero", "combine",   "fwd_stream",    "pack_weight", "dh_merge"};
+    "fwd_tile",      "fwd_combine", "bwd_recompute", "bwd_dw",      "bwd_dh",
+    "bwd_dh_reduce", "fill_zero",   "combine",       "fwd_stream",  "pack_weight", "dh_merge"};
 
 void prof_before(int id, hipStream_t st) {
   if (!g_prof.on.load(std::memory_order_relaxed)) return;
@@ -208,8 +208,7 @@ BwdPlan bwd_plan(int64_t T, int64_t H, const FwdSlicing& sl, bool want_dh) {
   p.splits_per_chunk = (int)spc;
   p.nchunks = (int)ceil_div(p.nsplits, spc);
   p.ldg = spc * p.split_w;
-  p.off_rowc = 0;
-  p.off_gtv = align256(size_t(p.Tp) * 32);
+  p.off_gtv = 0;
   p.off_part = align256(p.off_gtv + size_t(p.Tp) * size_t(p.ldg) * 2);
   p.total = align256(p.off_part + (want_dh ? size_t(p.nsplits) * size_t(T) * size_t(H) * 4 : 0));
   return p;
@@ -421,7 +420,6 @@ RLK_API rlk_status rlk_linear_logp_bwd(const void* hidden, const void* weight,
   a.dhidden = dhidden;
   a.dh_f32 = (flags & RLK_DH_F32) ? 1 : 0;
   a.dweight = dweight;
-  a.rowc = reinterpret_cast<float4*>(ws + plan.off_rowc);
   a.gtv = reinterpret_cast<uint16_t*>(ws + plan.off_gtv);
   a.part = reinterpret_cast<float*>(ws + plan.off_part);
   if (rlk::launch_bwd(a, plan, static_cast<hipStream_t>(stream)) != hipSuccess) return RLK_ERR_HIP;

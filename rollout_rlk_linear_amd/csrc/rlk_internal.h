@@ -85,7 +85,7 @@ struct BwdPlan {
   int nchunks;
   int64_t ldg;          // row stride of the G chunk buffer (columns)
   int64_t Tp;           // T rounded up to the dW k-step (32)
-  size_t off_rowc, off_gtv, off_part, total;
+  size_t off_gtv, off_part, total;
   // padded column where split s begins / ends, and its valid columns
   int u_begin(int s) const { return (s / n_sub) * Vs_pad + (s % n_sub) * split_w; }
   int u_end(int s) const {
@@ -110,7 +110,6 @@ struct BwdArgs {
   void* dhidden;
   int dh_f32;
   float* dweight;
-  float4* rowc;
   uint16_t* gtv;  // [Tp][ldg] logit gradient of one chunk, rows t (dH and dW operand)
   float* part;
   int n_cu;  // compute units of the device (persistent recompute grid)
@@ -120,7 +119,6 @@ struct BwdArgs {
 enum KernelId {
   K_FWD_TILE = 0,
   K_FWD_COMBINE,
-  K_BWD_ROWPREP,
   K_BWD_RECOMPUTE,
   K_BWD_DW,
   K_BWD_DH,

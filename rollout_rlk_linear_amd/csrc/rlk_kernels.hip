@@ -12,10 +12,10 @@
 //                entropy and the row's statistics record.
 // Backward (per vocabulary chunk, chunks made of whole dH splits; columns in
 // the padded per-slice layout of BwdPlan, each virtual slice padded to 256):
-//   bwd_rowprep    per row: log1p(R), -B/(1+R), upstream gradients, local target.
 //   bwd_recompute  logits of the chunk again (same MFMA chain as the forward,
-//                  so the same bits), the logit gradient G in fp32, RNE to
-//                  bf16, staged through LDS and stored [T][chunk] coalesced.
+//                  so the same bits), the logit gradient G in fp32 from the
+//                  row's record and upstream gradients, RNE to bf16, staged
+//                  through LDS and stored [T][chunk] coalesced.
 //   bwd_dw         dW[v, :] = sum_t G[t, v] h[t, :]  (both operands read
 //                  K-major through transposing LDS reads), fp32, one owner
 //                  per element.
@@ -588,23 +588,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restr
 
 // ======================================================== backward =======
 
-// rowc[2t]   = {m, log1p(R), -B/(1+R), dlogp}
-// rowc[2t+1] = {dentropy, bits of (y - vocab_start), R/(1+R), 0}
-__global__ __launch_bounds__(kThreads) void bwd_rowprep_kernel(
-    const float4* __restrict__ stats, const float* __restrict__ dlogp,
-    const float* __restrict__ dent, const int32_t* __restrict__ targets, int T,
-    int64_t vocab_start, float4* __restrict__ rowc) {
-  const int t = blockIdx.x * kThreads + threadIdx.x;
-  if (t >= T) return;
-  const float4 s = stats[t];
+// A row's constants for the logit gradient, from its whole-vocabulary
+// record s = (m, R, B, z_y) and upstream gradients dl, de:
+// c0 = {m, log1p(R), -B/(1+R), dl}, c1 = {de, bits of (y - vocab_start) or -1, R/(1+R), 0}.
+__device__ __forceinline__ void row_constants(float4 s, float dl, float de, int32_t y,
+                                              int64_t vocab_start, float4& c0, float4& c1) {
   const float L = log1pf(s.y);
   const float Hb = -(s.z / (1.f + s.y));
-  const float dl = dlogp ? dlogp[t] : 0.f;
-  const float de = dent ? dent[t] : 0.f;
-  const int64_t yl = (int64_t)targets[t] - vocab_start;
+  const int64_t yl = (int64_t)y - vocab_start;
   const int yli = (yl < INT32_MIN || yl > INT32_MAX) ? -1 : (int)yl;
-  rowc[2 * t] = make_float4(s.x, L, Hb, dl);
-  rowc[2 * t + 1] = make_float4(de, __int_as_float(yli), s.y / (1.f + s.y), 0.f);
+  c0 = make_float4(s.x, L, Hb, dl);
+  c1 = make_float4(de, __int_as_float(yli), s.y / (1.f + s.y), 0.f);
 }
 
 // Padded column u of the backward layout: virtual slice q = u / Vs_pad,
@@ -632,14 +626,16 @@ __device__ __forceinline__ void padded_col(int u, int Vs, int Vs_pad, int& row, 
 // epilogue works only in A's and B's pair-1 slots, 32 rows a round (row
 // block i of both wave rows) staged as [t][v] so that the stores are whole
 // 16-byte row pieces, the rounds alternating between the two slots, and the
-// rows' constants (loaded from rowc during the mainloop) beside the first
-// round's buffer. When every wave issued all of a tile's stores, the next
+// rows' constants (from their records and upstream gradients, loaded during
+// the mainloop) beside the first round's buffer. When every wave issued all of a tile's stores, the next
 // mainloop's first wait leaves them in flight.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
     int u0, int Vs, int Vs_pad, int n_tiles, int n_ttiles, int n_items,
-    const float4* __restrict__ rowc, uint16_t* __restrict__ gtv, int64_t ldg) {
+    const float4* __restrict__ stats, const float* __restrict__ dlogp,
+    const float* __restrict__ dent, const int32_t* __restrict__ targets, int64_t vocab_start,
+    uint16_t* __restrict__ gtv, int64_t ldg) {
   using Gm = AsyncGemmP<BM, BN, WM, WN>;
   static_assert(WM == 2, "a round is row block i of both wave rows: 32 rows");
   constexpr int LDG_S = BN + 8;           // staged row (bf16), 16 B longer than the tile's
@@ -696,13 +692,18 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
   bool young = false;  // every wave has issued all of the previous tile's stores
 #pragma unroll 1
   for (;;) {
-    // row constants of this tile (thread tid: row row0 + tid; rows past T
-    // take row T - 1 and are zeroed below), in flight during the mainloop
-    float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
+    // this tile's rows' records and upstream gradients (thread tid: row
+    // row0 + tid; rows past T take row T - 1 and are zeroed below), in
+    // flight during the mainloop
+    float4 rs = make_float4(0.f, 0.f, 0.f, 0.f);
+    float rdl = 0.f, rde = 0.f;
+    int32_t ry = 0;
     if (tid < BM) {
       const int t = cur.row0 + tid < T ? cur.row0 + tid : T - 1;
-      c0 = rowc[2 * t];
-      c1 = rowc[2 * t + 1];
+      rs = stats[t];
+      if (dlogp) rdl = dlogp[t];
+      if (dent) rde = dent[t];
+      ry = targets[t];
     }
     gm.zero();
     gm.template run<STORES>(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0,
@@ -710,8 +711,10 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
                             /*prefetched=*/true, young);
     // run() ends with every load drained: the constants are settled here, so
     // the compiler's wait for them never meets the next prologue's DMA
-    asm volatile("" : "+v"(c0.x), "+v"(c0.y), "+v"(c0.z), "+v"(c0.w), "+v"(c1.x), "+v"(c1.y),
-                 "+v"(c1.z), "+v"(c1.w));
+    asm volatile("" : "+v"(rs.x), "+v"(rs.y), "+v"(rs.z), "+v"(rs.w), "+v"(rdl), "+v"(rde),
+                 "+v"(ry));
+    float4 c0, c1;
+    row_constants(rs, rdl, rde, ry, vocab_start, c0, c1);
     const int nit = next_item(it + stride);
     const bool more = nit < n_items;
     const Item nxt = more ? item_of(nit) : cur;
@@ -1056,7 +1059,8 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 #define RLK_RECOMPUTE(BM, BN, WM, WN)                                                          \
   template __global__ void bwd_recompute_kernel<BM, BN, WM, WN>(                               \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
-      int, int, const float4* __restrict__, uint16_t* __restrict__, int64_t);
+      int, int, const float4* __restrict__, const float* __restrict__, const float* __restrict__, \
+      const int32_t* __restrict__, int64_t, uint16_t* __restrict__, int64_t);
 #define RLK_DH(BM, BN, WM, WN)                                                                \
   template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                       \
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, SplitMap, \
@@ -1150,8 +1154,6 @@ hipError_t launch_combine(const float4* partials, int S, int T, float* logp, flo
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
   const int T = a.T, H = a.H;
   const int Tp = (int)p.Tp;
-  RLK_LAUNCH(K_BWD_ROWPREP, bwd_rowprep_kernel, cdiv(T, kThreads), st, a.stats, a.dlogp,
-             a.dentropy, a.targets, T, a.vocab_start, a.rowc);
   const bool small = T <= kSmallT;
   const int bm = small ? 32 : 256;
   // persistent recompute: a multiple of 8 workgroups, one per CU for 256-row tiles
@@ -1173,14 +1175,14 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
       // one item per workgroup (up to four resident per CU with 40 KB of LDS
       // each): for these short tiles that beats a persistent walk
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, BN, 2, 2>), n_items,
-                 st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.rowc,
-                 a.gtv, p.ldg);
+                 st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.stats,
+                 a.dlogp, a.dentropy, a.targets, a.vocab_start, a.gtv, p.ldg);
     } else {
       const int ntl = width / 256;
       const int n_items = cdiv(ntl, 8) * 8 * nt;
       RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2>), min(grid_cap, n_items),
-                 st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.rowc,
-                 a.gtv, p.ldg);
+                 st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.stats,
+                 a.dlogp, a.dentropy, a.targets, a.vocab_start, a.gtv, p.ldg);
     }
     const int nvt = width / 256;
     const int nhw = cdiv(H, kDwBN);
