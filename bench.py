@@ -19,7 +19,7 @@ one 37984-row vocabulary slice); the same GEMM shapes through torch.matmul
 (hipBLASLt) as a yardstick; and the float64 CPU oracle timed on the same
 batch.
 
-    python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-cpu-baseline] [--quick]
+    python bench.py [--steps 20] [--warmup 10] [--gpus 1] [--no-cpu-baseline] [--quick]
 """
 
 from __future__ import annotations
@@ -497,7 +497,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--quick", action="store_true",
@@ -596,23 +596,33 @@ def main():
         o = rlk.fwd(hidden, weight, targets, out=fo)
         rlk.bwd(hidden, weight, targets, o["stats"], dlogp, None, out=bo)
 
+    # warm-up: the clock takes about ten steps to settle after the idle set-up
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # headline pass: only the step events, no per-launch timer
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # headline pass: the K steps between two events, nothing recorded between
+    # them (an event between steps adds a few microseconds to each boundary)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    # second pass: an event after every step, for the distribution of step times
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev[0].record()
     for i in range(args.steps):
         step()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    ms_total = ev[0].elapsed_time(ev[args.steps])
-    ms_step = ms_total / args.steps
-    # second pass, for the per-kernel table: the library's per-launch events
+    # third pass, for the per-kernel table: the library's per-launch events
     rlk.profile_begin()
     for _ in range(args.steps):
         step()
