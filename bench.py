@@ -44,7 +44,7 @@ CSRC = os.path.join(ROOT, "rollout_rlk_linear_amd", "csrc")
 
 
 # the sources that decide the linear-logp kernels' code and launches
-HASHED_SOURCES = ("rlk_abi.cpp", "rlk_device.cuh", "rlk_internal.h", "rlk_kernels.hip")
+HASHED_SOURCES = ("rlk_abi.cpp", "rlk_device.h", "rlk_internal.h", "rlk_kernels.hip")
 
 
 def kernel_source_hash() -> str:

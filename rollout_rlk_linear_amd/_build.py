@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "librlk_linear.so")
 ARCH = "gfx950"
 
 SOURCES = ["rlk_kernels.hip", "rlk_microbench.hip", "rlk_lora.hip", "rlk_abi.cpp"]
-HEADERS = ["rlk_device.cuh", "rlk_internal.h"]
+HEADERS = ["rlk_device.h", "rlk_internal.h"]
 
 
 def hipcc() -> str:

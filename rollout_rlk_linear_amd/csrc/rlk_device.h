@@ -1,4 +1,4 @@
-// rlk_device.cuh — device building blocks for the gfx950 linear log-prob kernels.
+// rlk_device.h — device building blocks for the gfx950 linear log-prob kernels.
 //
 // * LDS-DMA fed bf16 MFMA mainloops (v_mfma_f32_16x16x32_bf16, and
 //   v_mfma_f32_32x32x16_bf16 for dH) computing a BM x BN fp32 tile with K

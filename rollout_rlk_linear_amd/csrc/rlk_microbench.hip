@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "rlk_device.cuh"
+#include "rlk_device.h"
 #include "rlk_internal.h"
 #include "../../include/rlk_microbench.h"
 

@@ -1,6 +1,6 @@
 """Address model of the LDS-DMA operand staging (CPU only, no GPU).
 
-The mainloops in ``rlk_device.cuh`` and the small-batch stream in
+The mainloops in ``rlk_device.h`` and the small-batch stream in
 ``rlk_kernels.hip`` fetch operands with gfx950 raw buffer loads
 (``buffer_load_dwordx4 ... offen lds``): lane i fetches the 16 bytes at
 base + soffset + voffset, and the hardware range check compares the vector
