@@ -211,11 +211,23 @@ __device__ __forceinline__ int row_piece(int s, int r) { return (s - (r >> 1)) &
 // states in all) is for the call sites where it does that; the test suite
 // scans the built code for the pattern, so a site that needs it and lacks it
 // does not go unnoticed.
-template <bool SETTLE = false>
+// NT = true marks the load non-temporal (the nt cache bit: lines it brings in
+// are not retained), for a stream that would otherwise push out data a
+// later kernel reads; it always settles.
+template <bool SETTLE = false, bool NT = false>
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t addr, int voff, int soff) {
   const i32x4 rs = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
                     __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
-  if constexpr (SETTLE)
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen nt lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane((int)addr)), "v"(voff), "s"(rs),
+          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory", "m0");
+  else if constexpr (SETTLE)
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 4\n\t"
@@ -274,7 +286,8 @@ __device__ __forceinline__ void barrier_only() {
 // k-step all B fragments and two A fragments are read first, then A fragment
 // i+2 is read while the MFMAs of row block i run (scheduling group barriers
 // pin the order).
-template <int BM, int BN, int WM, int WN, int NSB = 2>
+// BNT: B's loads are non-temporal (dma16's NT).
+template <int BM, int BN, int WM, int WN, int NSB = 2, bool BNT = false>
 struct AsyncGemmP {
   static constexpr int NW = WM * WN;
   static_assert(NW == 4, "4 waves per tile");
@@ -329,7 +342,7 @@ struct AsyncGemmP {
     const int kb0 = k_begin * 2;
 #pragma unroll
     for (int ii = 0; ii < NB_B; ++ii)
-      dma16(rsB, lds0 + (uint32_t)(2 * SLOT_A) + 1024u * wave + 1024u * NW * ii,
+      dma16<false, BNT>(rsB, lds0 + (uint32_t)(2 * SLOT_A) + 1024u * wave + 1024u * NW * ii,
             voffB + (int)(ii * 64 * ldb), kb0);
 #pragma unroll
     for (int ii = 0; ii < NB_A; ++ii)
@@ -338,7 +351,7 @@ struct AsyncGemmP {
       const i32x4 rb1 = npairs > 1 ? rsB : rsNull;
 #pragma unroll
       for (int ii = 0; ii < NB_B; ++ii)
-        dma16(rb1, lds0 + (uint32_t)(2 * SLOT_A + SLOT_B) + 1024u * wave + 1024u * NW * ii,
+        dma16<false, BNT>(rb1, lds0 + (uint32_t)(2 * SLOT_A + SLOT_B) + 1024u * wave + 1024u * NW * ii,
               voffB + (int)(ii * 64 * ldb), kb0 + 128);
     }
   }
@@ -391,7 +404,7 @@ struct AsyncGemmP {
       if (ii < NB_A)
         dma16(ra, a + 1024u * NW * ii, voffA + (int)(ii * 64 * lda), ka);
       else
-        dma16(rb, b + 1024u * NW * (ii - NB_A), voffB + (int)((ii - NB_A) * 64 * ldb), kb);
+        dma16<false, BNT>(rb, b + 1024u * NW * (ii - NB_A), voffB + (int)((ii - NB_A) * 64 * ldb), kb);
     };
     // fragment offsets of this lane in a slot for half h (k-step 2 p + h):
     // row l % 16 of the block, logical piece 4 h + l / 16

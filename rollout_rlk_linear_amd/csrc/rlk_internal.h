@@ -22,6 +22,10 @@ constexpr int kMaxSplits = 8;
 constexpr int kSplitCols = 16384;
 // Soft bound on the elements of one bf16 logit-gradient chunk (T x columns).
 constexpr int64_t kChunkElems = int64_t(1) << 28;
+// A chunk of G at most this large stays in the 256 MB Infinity Cache between
+// the recompute that writes it and dW and dH that read it, if the recompute's
+// stream of W does not push it out: the recompute then loads W non-temporal.
+constexpr size_t kGResidentBytes = size_t(192) << 20;
 // Columns h of one dW tile (the tile is 256 v x kDwBN h).
 constexpr int kDwBN = 128;
 

@@ -629,14 +629,14 @@ __device__ __forceinline__ void padded_col(int u, int Vs, int Vs_pad, int& row, 
 // rows' constants (from their records and upstream gradients, loaded during
 // the mainloop) beside the first round's buffer. When every wave issued all of a tile's stores, the next
 // mainloop's first wait leaves them in flight.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool WNT>
 __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight, int T, int H,
     int u0, int Vs, int Vs_pad, int n_tiles, int n_ttiles, int n_items,
     const float4* __restrict__ stats, const float* __restrict__ dlogp,
     const float* __restrict__ dent, const int32_t* __restrict__ targets, int64_t vocab_start,
     uint16_t* __restrict__ gtv, int64_t ldg) {
-  using Gm = AsyncGemmP<BM, BN, WM, WN>;
+  using Gm = AsyncGemmP<BM, BN, WM, WN, 2, WNT>;  // WNT: W's loads non-temporal
   static_assert(WM == 2, "a round is row block i of both wave rows: 32 rows");
   constexpr int LDG_S = BN + 8;           // staged row (bf16), 16 B longer than the tile's
   constexpr int RBYTES = 32 * LDG_S * 2;  // one round
@@ -1056,8 +1056,8 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   template __global__ void fwd_tile_kernel<BM, WM, WN>(                                       \
       const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__, \
       int, int, int, int, int64_t, int, int, int, float4* __restrict__);
-#define RLK_RECOMPUTE(BM, BN, WM, WN)                                                          \
-  template __global__ void bwd_recompute_kernel<BM, BN, WM, WN>(                               \
+#define RLK_RECOMPUTE(BM, BN, WM, WN, WNT)                                                     \
+  template __global__ void bwd_recompute_kernel<BM, BN, WM, WN, WNT>(                          \
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
       int, int, const float4* __restrict__, const float* __restrict__, const float* __restrict__, \
       const int32_t* __restrict__, int64_t, uint16_t* __restrict__, int64_t);
@@ -1066,8 +1066,9 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, SplitMap, \
       int, int, int, int, int, float* __restrict__);
 RLK_FWD_TILE(256, 2, 2)
-RLK_RECOMPUTE(32, 128, 2, 2)
-RLK_RECOMPUTE(256, 256, 2, 2)
+RLK_RECOMPUTE(32, 128, 2, 2, false)
+RLK_RECOMPUTE(256, 256, 2, 2, false)
+RLK_RECOMPUTE(256, 256, 2, 2, true)
 RLK_DH(32, 128, 1, 4)
 RLK_DH(256, 256, 2, 2)
 
@@ -1174,15 +1175,25 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
       const int n_items = cdiv(ntl, 8) * 8 * nt;
       // one item per workgroup (up to four resident per CU with 40 KB of LDS
       // each): for these short tiles that beats a persistent walk
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, BN, 2, 2>), n_items,
+      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<32, BN, 2, 2, false>), n_items,
                  st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.stats,
                  a.dlogp, a.dentropy, a.targets, a.vocab_start, a.gtv, p.ldg);
     } else {
       const int ntl = width / 256;
       const int n_items = cdiv(ntl, 8) * 8 * nt;
-      RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2>), min(grid_cap, n_items),
-                 st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl, nt, n_items, a.stats,
-                 a.dlogp, a.dentropy, a.targets, a.vocab_start, a.gtv, p.ldg);
+      // the chunk's G stays in the Infinity Cache for dW and dH when it fits
+      // with room to spare and the recompute's W stream does not evict it
+      const bool wnt = size_t(p.Tp) * size_t(width) * 2 <= kGResidentBytes;
+      if (wnt)
+        RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2, true>),
+                   min(grid_cap, n_items), st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl,
+                   nt, n_items, a.stats, a.dlogp, a.dentropy, a.targets, a.vocab_start, a.gtv,
+                   p.ldg);
+      else
+        RLK_LAUNCH(K_BWD_RECOMPUTE, (bwd_recompute_kernel<256, 256, 2, 2, false>),
+                   min(grid_cap, n_items), st, a.hidden, a.weight, T, H, u0, p.Vs, p.Vs_pad, ntl,
+                   nt, n_items, a.stats, a.dlogp, a.dentropy, a.targets, a.vocab_start, a.gtv,
+                   p.ldg);
     }
     const int nvt = width / 256;
     const int nhw = cdiv(H, kDwBN);
