@@ -96,12 +96,15 @@ __device__ __forceinline__ FwdItem fwd_item(int it, int n_ttiles, int BM, int Gs
   return FwdItem{g, tt * BM, (g / Gs) * Vs + lg * GROUP, min(GROUP, Vs - lg * GROUP)};
 }
 
-template <int BM, int WM, int WN>
+// WNT: W's loads are non-temporal, for launches with one T-tile (each W line
+// is then read once, and not keeping it leaves L2 to hidden, which every item
+// reads); with two or more T-tiles the second read of a line needs it kept.
+template <int BM, int WM, int WN, bool WNT>
 __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ weight,
     const int32_t* __restrict__ targets, int T, int H, int Vs, int Gs, int64_t vocab_start, int G,
     int n_ttiles, int n_items, float4* __restrict__ part) {
-  using Gm = AsyncGemmP<BM, GROUP, WM, WN, 2>;
+  using Gm = AsyncGemmP<BM, GROUP, WM, WN, 2, WNT>;
   static_assert(WN == 2 && Gm::WTN == 128 && Gm::NJ == 8, "one 128-column chunk per wave");
   static_assert(BM * 2 * 16 + BM * 4 <= Gm::SLOT_B, "chunk records and targets fit B's pair-1 slot");
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
@@ -1052,8 +1055,8 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
 
 // Explicit instantiations: every launched template kernel gets its host stub
 // even where the host pass would not instantiate it implicitly.
-#define RLK_FWD_TILE(BM, WM, WN)                                                              \
-  template __global__ void fwd_tile_kernel<BM, WM, WN>(                                       \
+#define RLK_FWD_TILE(BM, WM, WN, WNT)                                                         \
+  template __global__ void fwd_tile_kernel<BM, WM, WN, WNT>(                                  \
       const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__, \
       int, int, int, int, int64_t, int, int, int, float4* __restrict__);
 #define RLK_RECOMPUTE(BM, BN, WM, WN, WNT)                                                     \
@@ -1065,7 +1068,8 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                       \
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, SplitMap, \
       int, int, int, int, int, float* __restrict__);
-RLK_FWD_TILE(256, 2, 2)
+RLK_FWD_TILE(256, 2, 2, false)
+RLK_FWD_TILE(256, 2, 2, true)
 RLK_RECOMPUTE(32, 128, 2, 2, false)
 RLK_RECOMPUTE(256, 256, 2, 2, false)
 RLK_RECOMPUTE(256, 256, 2, 2, true)
@@ -1127,8 +1131,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
     const int n_items = cdiv(G, 8) * 8 * nt;
     const int n_cu = a.n_cu > 0 ? a.n_cu : 256;
     const int grid = min(cdiv(n_cu, 8) * 8, n_items);  // a multiple of 8
-    RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2>), grid, st, a.hidden, a.weight,
-               a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, n_items, a.part);
+    if (nt == 1)
+      RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2, true>), grid, st, a.hidden, a.weight,
+                 a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, n_items, a.part);
+    else
+      RLK_LAUNCH(K_FWD_TILE, (fwd_tile_kernel<256, 2, 2, false>), grid, st, a.hidden, a.weight,
+                 a.targets, a.T, a.H, sl.Vs, sl.Gs, a.vocab_start, G, nt, n_items, a.part);
   }
   RLK_LAUNCH(K_FWD_COMBINE, fwd_combine_kernel, a.T, st, a.part, a.targets,
              a.T, G, sl.P, sl.Gs, sl.Vs, units, a.vocab_total, a.full, a.logp, a.entropy, a.stats);
