@@ -136,6 +136,34 @@ def test_dhidden_rows_bitwise(setup):
     assert bits_equal(got[pos], ref)
 
 
+def test_rows_bitwise_across_cache_policies(setup):
+    """The load policy of W changes with the batch: one T-tile of the forward
+    reads W non-temporally, several do not; the recompute of G reads W
+    non-temporally while the bf16 G of the batch fits in 192 MiB (T up to
+    662 rows at V = 151936) and with the default policy above that. A cache
+    hint must not change a bit: the pool's rows inside a 768-row batch (three
+    T-tiles, G of 223 MiB) give the records and dhidden rows of the 64-row
+    batch (one T-tile, G resident)."""
+    W, h, y, dl = setup["W"], setup["h"], setup["y"], setup["dlogp"]
+    ref, ref_st = score(W, h, y)
+    ref_dh, _ = rlk.bwd(h, W, y, ref_st, dl, None, want_dweight=False)
+    T = 768
+    assert T * W.shape[0] * 2 > (192 << 20)
+    big_h, big_y, _ = wl.qwen_rows(T, 11)
+    pos = torch.randperm(T, generator=torch.Generator().manual_seed(12))[:64]
+    big_h[pos] = setup["pool"]["hidden"]
+    big_y[pos] = setup["pool"]["targets"]
+    big_h, big_y, pos = dev(big_h), dev(big_y), pos.cuda()
+    got, st = score(W, big_h, big_y)
+    dlb = torch.zeros(T, device="cuda")
+    dlb[pos] = dl
+    dh, _ = rlk.bwd(big_h, W, big_y, st, dlb, None, want_dweight=False)
+    torch.cuda.synchronize()
+    assert mismatch(got[pos], ref) == 0
+    assert mismatch(st[pos], ref_st) == 0
+    assert bits_equal(dh[pos], ref_dh)
+
+
 def test_dweight_repeat_deterministic(setup):
     W, h, y, dl = setup["W"], setup["h"], setup["y"], setup["dlogp"]
     _, st = score(W, h, y)
