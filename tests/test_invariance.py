@@ -164,6 +164,36 @@ def test_rows_bitwise_across_cache_policies(setup):
     assert bits_equal(dh[pos], ref_dh)
 
 
+def test_concurrent_streams_bitwise(setup):
+    """Two forward + backward calls issued on two streams at once, each with
+    its own workspace, give the bits the same calls give one after the
+    other: the library keeps no state between calls that the kernels of
+    one call could see from another."""
+    W, h, y, dl = setup["W"], setup["h"], setup["y"], setup["dlogp"]
+    emb = setup["pool"]["embed"]
+    he, ye = dev(emb["hidden"]), dev(emb["targets"])
+    dle = torch.randn(he.shape[0], generator=torch.Generator().manual_seed(13)).cuda()
+
+    def run(hh, yy, dd):
+        o = rlk.fwd(hh, W, yy)
+        dh, dw = rlk.bwd(hh, W, yy, o["stats"], dd, None)
+        return o["stats"], dh, dw
+
+    serial = [run(h, y, dl), run(he, ye, dle)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(streams[0]):
+        a = run(h, y, dl)
+    with torch.cuda.stream(streams[1]):
+        b = run(he, ye, dle)
+    torch.cuda.synchronize()
+    for got, ref in zip((a, b), serial):
+        for g, r in zip(got, ref):
+            assert bits_equal(g, r)
+
+
 def test_dweight_repeat_deterministic(setup):
     W, h, y, dl = setup["W"], setup["h"], setup["y"], setup["dlogp"]
     _, st = score(W, h, y)
