@@ -523,7 +523,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}); the multi-GPU path is not part of this build", file=sys.stderr)
+              f"{world}); the library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
