@@ -9,7 +9,9 @@ Qwen3-8B-shaped rows (H = 4096, V = 151936) is scored in batches of 1, 2, 3,
 4, 24 and 64, under 3 row permutations, embedded in a batch of 512 other rows,
 and repeated, and scored through the packed-weight rollout path in batches
 of 1 to 4, 24 and 64; every row's logp, entropy and statistics record must be
-bit-identical across all of them. The same holds for each row of dhidden.
+bit-identical across all of them. The same holds for each row of dhidden,
+also inside 200- and 768-row batches (the two load policies of W), and for
+calls issued on two streams at once.
 """
 
 import pytest
@@ -136,19 +138,22 @@ def test_dhidden_rows_bitwise(setup):
     assert bits_equal(got[pos], ref)
 
 
-def test_rows_bitwise_across_cache_policies(setup):
-    """The load policy of W changes with the batch: one T-tile of the forward
-    reads W non-temporally, several do not; the recompute of G reads W
-    non-temporally while the bf16 G of the batch fits in 192 MiB (T up to
-    662 rows at V = 151936) and with the default policy above that. A cache
-    hint must not change a bit: the pool's rows inside a 768-row batch (three
-    T-tiles, G of 223 MiB) give the records and dhidden rows of the 64-row
-    batch (one T-tile, G resident)."""
+@pytest.mark.parametrize("T", [200, 768])
+def test_rows_bitwise_across_cache_policies(setup, T):
+    """The load policy of W changes with the batch. The forward's tile kernel
+    reads W non-temporally when the batch is one T-tile (65 to 256 rows) and
+    with the default policy for more; the recompute of G reads it
+    non-temporally while the batch's bf16 G fits in 192 MiB (up to 640 rows
+    at V = 151936) and with the default policy above that. A cache hint must
+    not change a bit: the pool's rows inside a 200-row batch (both hints on)
+    and inside a 768-row batch (both off, G of 223 MiB) give the records and
+    dhidden rows that the 64-row batch gives on the small-batch kernels."""
     W, h, y, dl = setup["W"], setup["h"], setup["y"], setup["dlogp"]
     ref, ref_st = score(W, h, y)
     ref_dh, _ = rlk.bwd(h, W, y, ref_st, dl, None, want_dweight=False)
-    T = 768
-    assert T * W.shape[0] * 2 > (192 << 20)
+    g_fits = (T + 31) // 32 * 32 * W.shape[0] * 2 <= (192 << 20)
+    one_tile = 64 < T <= 256
+    assert (g_fits, one_tile) == ((True, True) if T == 200 else (False, False))
     big_h, big_y, _ = wl.qwen_rows(T, 11)
     pos = torch.randperm(T, generator=torch.Generator().manual_seed(12))[:64]
     big_h[pos] = setup["pool"]["hidden"]
