@@ -250,12 +250,16 @@ def model_stream(MI, KS, packed, T, H, vrows):
     return fa, fb
 
 
-@pytest.mark.parametrize("MI,KS", [(1, 1), (2, 1), (4, 1), (1, 2), (2, 2), (4, 2)])
-@pytest.mark.parametrize("T,vrows", [(1, 128), (3, 5), (16, 127), (20, 128), (33, 1), (64, 64)])
+# (MI, KS, T, vrows): the launcher runs MI 16-row blocks for T <= 16 MI rows
+STREAM_CASES = [(mi, ks, t, vr)
+                for mi, ks in [(1, 1), (2, 1), (4, 1), (1, 2), (2, 2), (4, 2)]
+                for t, vr in [(1, 128), (3, 5), (16, 127), (20, 128), (33, 1), (64, 64)]
+                if t <= 16 * mi]
+
+
+@pytest.mark.parametrize("MI,KS,T,vrows", STREAM_CASES)
 @pytest.mark.parametrize("packed", [False, True])
 def test_stream_reads_inside_operands(MI, KS, T, vrows, packed):
-    if T > 16 * MI:
-        pytest.skip("rows beyond this configuration")
     H = 256
     fa, fb = model_stream(MI, KS, packed, T, H, vrows)
     check_k_contiguous(fa, T, H, 0, H, f"stream hidden MI={MI} KS={KS}")
