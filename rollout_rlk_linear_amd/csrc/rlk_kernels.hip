@@ -766,7 +766,12 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
             const float omp = (zd == 0.f) ? Rn : 1.f - p;
             const float onehot_term = (cl == yloc) ? omp : -p;
             const float g = dl * onehot_term - de * (p * (zd + Hb));
-            gv[u] = (rv && cvalid[j + u]) ? g : 0.f;
+            // zero outside the rows and columns (+0, as a select would give),
+            // by a mask: written as a select, the compiler moves g's arithmetic
+            // under exec-masked branches, one per element pair, and the row's
+            // 8 elements no longer interleave
+            const uint32_t keep = (rv && cvalid[j + u]) ? 0xFFFFFFFFu : 0u;
+            gv[u] = __uint_as_float(__float_as_uint(g) & keep);
           }
           const uint32_t pk = pack_bf16x2(gv[0], gv[1]);
           const int cl0 = wn * Gm::WTN + 16 * j + (lane & 15);
