@@ -116,25 +116,26 @@ __device__ __forceinline__ Part part_empty() { return Part{neg_inf(), 0.f, 0.f, 
 // Merge of two partials over disjoint column sets. The side with the larger
 // max is the base (the left one on a tie); with d = m_other - m_base <= 0,
 //   R = R_base + e^d (1 + R_other),  B = B_base + e^d (B_other + (1 + R_other) d).
-// An empty side (m = -inf) contributes nothing. Accurate expf; contraction is
-// disabled for the whole library, so the arithmetic is exactly as written.
+// An empty side (m = -inf) contributes nothing: its terms are masked to +0,
+// and R_base, B_base come out unchanged (they are never -0: every record's
+// sums include the +0 of its max column). Straight-line on
+// purpose: with an early return for the empty side the compiler branches
+// around the exponential, and the merge chains of the combine serialise.
+// Accurate expf; contraction is disabled for the whole library, so the
+// arithmetic is exactly as written.
 __device__ __forceinline__ Part part_merge(const Part& l, const Part& r) {
   const bool left_base = !(r.m > l.m);
-  const Part& b = left_base ? l : r;
-  const Part& o = left_base ? r : l;
+  const float bm = left_base ? l.m : r.m, bR = left_base ? l.R : r.R, bB = left_base ? l.B : r.B;
+  const float om = left_base ? r.m : l.m, oR = left_base ? r.R : l.R, oB = left_base ? r.B : l.B;
   Part out;
-  out.m = b.m;
+  out.m = bm;
   out.zy = fmaxf(l.zy, r.zy);
-  if (o.m == neg_inf()) {
-    out.R = b.R;
-    out.B = b.B;
-    return out;
-  }
-  const float d = o.m - b.m;
+  const float d = om - bm;
   const float e = expf(d);
-  const float one_r = 1.f + o.R;
-  out.R = b.R + e * one_r;
-  out.B = b.B + e * (o.B + one_r * d);
+  const float one_r = 1.f + oR;
+  const uint32_t keep = om == neg_inf() ? 0u : 0xFFFFFFFFu;
+  out.R = bR + __uint_as_float(__float_as_uint(e * one_r) & keep);
+  out.B = bB + __uint_as_float(__float_as_uint(e * (oB + one_r * d)) & keep);
   return out;
 }
 

@@ -536,7 +536,8 @@ __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) {
       const Part o = shfl_xor_part(acc, s);
-      acc = (lane & s) ? part_merge(o, acc) : part_merge(acc, o);
+      const bool hi = (lane & s) != 0;  // the lower lane is the left operand
+      acc = part_merge(hi ? o : acc, hi ? acc : o);
     }
     if (lane == 0) srec[p] = make_float4(acc.m, acc.R, acc.B, acc.zy);
   }
