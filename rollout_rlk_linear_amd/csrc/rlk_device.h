@@ -362,7 +362,13 @@ struct AsyncGemmP {
   // the previous tile's stores), which need not have completed for pair 0:
   // with in-order completion, YOUNG pending operations at most mean that
   // everything older, the prologue included, has landed.
-  template <int YOUNG = 0>
+  // UNROLL: the pair's two k-steps as straight-line code (the refill test
+  // becomes a constant instead of a branch after every row block). The
+  // register allocator keeps each accumulator chain in place only when the
+  // first pair has code of its own, which a young first wait (YOUNG > 0
+  // with young_pending) gives it; without that it splits the chains through
+  // VGPRs, so the callers that unroll also pass a young first wait.
+  template <int YOUNG = 0, bool UNROLL = false>
   __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
                                       int a_rows, const uint16_t* B, int64_t ldb, int b_rows,
                                       int k_begin, int k_end, bool prefetched = false,
@@ -436,7 +442,8 @@ struct AsyncGemmP {
       const i32x4 rb = pb < npairs ? rsB : rsNull;
       const unsigned char* sa = lds + (p & 1) * SLOT_A;
       const unsigned char* sb = lds + 2 * SLOT_A + (p % NSB) * SLOT_B;
-#pragma unroll 1
+      constexpr int HSTEPS = UNROLL ? 2 : 1;
+#pragma unroll HSTEPS
       for (int h = 0; h < 2; ++h) {
         constexpr int A0 = MI < 2 ? MI : 2;
         const uint32_t fo = h ? foff1 : foff0;

@@ -117,11 +117,13 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     return it;
   };
   // target of row row0 + tid (loaded early), then its column in the
-  // item's group or -1
+  // item's group or -1. The load's row is clamped into the batch rather than
+  // predicated, so every wave issues exactly one load after the item's
+  // prologue; run() may then leave it in flight at its first wait
+  // (target_col ignores rows past T).
   const int tid = threadIdx.x;
   auto target_of = [&](const FwdItem& f) {
-    const int t = f.row0 + tid;
-    return (tid < BM && t < T) ? targets[t] : -1;
+    return targets[min(f.row0 + (tid < BM ? tid : 0), T - 1)];
   };
   auto target_col = [&](const FwdItem& f, int32_t y32) {
     int yc = -1;
@@ -149,8 +151,12 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     const FwdItem nxt = nit < n_items ? fwd_item(nit, n_ttiles, BM, Gs, Vs) : cur;
     int32_t ny = target_of(nxt);  // in flight during the mainloop
     gm.zero();
-    gm.run(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0, weight + (int64_t)cur.col0 * H, H,
-           cur.vlim, 0, H, /*prefetched=*/true);
+    // the first pair in code of its own (the young wait), then the rest
+    // unrolled by k-step: with the first pair peeled, the register
+    // allocator keeps every accumulator chain in its AGPRs
+    gm.template run<1, true>(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0,
+                             weight + (int64_t)cur.col0 * H, H, cur.vlim, 0, H,
+                             /*prefetched=*/true, /*young_pending=*/true);
     // run() ends with every load drained: the next target is settled here, so
     // the compiler's wait for it never meets the next prologue's DMA
     asm volatile("" : "+v"(ny));
@@ -710,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void bwd_recompute_kernel(
       ry = targets[t];
     }
     gm.zero();
-    gm.template run<STORES>(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0,
+    gm.template run<STORES, true>(lds, hidden + (int64_t)cur.row0 * H, H, T - cur.row0,
                             weight + (int64_t)cur.col0 * H, H, cur.vlim, 0, H,
                             /*prefetched=*/true, young);
     // run() ends with every load drained: the constants are settled here, so
