@@ -591,7 +591,7 @@ struct AsyncGemmKN {
     const int nsteps = (k_end - k_begin) / 32;
     if (nsteps <= 0) return;
     const int ar = a_rows < 0 ? 0 : (a_rows > BM ? BM : a_rows);
-    const i32x4 rsA = make_rsrc(A, (uint32_t)(ar * lda * 2));
+    const i32x4 rsA_all = make_rsrc(A, (uint32_t)(ar * lda * 2));
     const uint32_t lds0 = lds_addr(lds);
 
     const int drow = lane >> 2;
@@ -617,6 +617,10 @@ struct AsyncGemmKN {
       // the resource ends at column nb_valid of the stage's last valid row
       const uint32_t bbytes = brows > 0 ? (uint32_t)(((brows - 1) * ldb + nb_valid) * 2) : 0u;
       const i32x4 rsB = make_rsrc(B + (int64_t)k0 * ldb, bbytes);
+      // a stage past the last (padded issue below) reads through empty
+      // resources: A's k offset travels in the scalar offset, which the
+      // range check does not cover, so A's resource is emptied too
+      const i32x4 rsA = s < nsteps ? rsA_all : make_rsrc(A, 0u);
       if constexpr (NI_A % NW == 0 && NI % NW == 0) {
         // block wave + NW ii is an A block iff ii < NI_A / NW (known at compile time)
 #pragma unroll
@@ -685,7 +689,7 @@ struct AsyncGemmKN {
     constexpr bool SPLIT = NI_A % NW == 0 && NI % NW == 0 && NI / NW <= MI * KSUB;
     // the first block of each operand in a stage settles the descriptor's
     // SGPRs (the compiler reads them back from VGPRs once per stage)
-    auto issue_block = [&](int ii, uint32_t dst, int k0, const i32x4& rsB) {
+    auto issue_block = [&](int ii, uint32_t dst, int k0, const i32x4& rsA, const i32x4& rsB) {
       if (ii == 0)
         dma16<true>(rsA, dst, voff[0], k0 * 2);
       else if (ii < NI_A / NW)
@@ -703,9 +707,17 @@ struct AsyncGemmKN {
     };
 
     // a ring of NST single-k-step slots; A fragments read two row blocks ahead
-    for (int s = 0; s < NST - 1 && s < nsteps; ++s) issue(s);
+    // With split issue every step issues one stage, past the last through
+    // empty resources (no memory touched, zeros into a slot no later step
+    // reads): no branch sits between the MFMAs, and the wait is the constant
+    // NST - 2 stages behind (the clamped count of wait_stage takes a branch
+    // per step).
+    for (int s = 0; s < NST - 1 && (SPLIT || s < nsteps); ++s) issue(s);
     for (int s = 0; s < nsteps; ++s) {
-      wait_stage(s, last_of(s + NST - 2));
+      if constexpr (SPLIT)
+        wait_vmcnt<(NST - 2) * (NI / NW)>();
+      else
+        wait_stage(s, last_of(s + NST - 2));
       barrier_only();
       const bool refill = s + NST - 1 < nsteps;
       if (!SPLIT && refill) issue(s + NST - 1);
@@ -713,6 +725,7 @@ struct AsyncGemmKN {
       const uint32_t dst =
           lds0 + (uint32_t)(((s + NST - 1) % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave;
       const i32x4 rsB3 = stage_rsrc_b(k3);
+      const i32x4 rsA3 = refill ? rsA_all : make_rsrc(A, 0u);
       unsigned char* st = lds + (s % NST) * STAGE_BYTES;
       constexpr int A0 = MI < 2 ? MI : 2;
 #pragma unroll
@@ -747,7 +760,7 @@ struct AsyncGemmKN {
             __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
           }
           if constexpr (SPLIT) {
-            if (q * MI + i < NI / NW && refill) issue_block(q * MI + i, dst, k3, rsB3);
+            if (q * MI + i < NI / NW) issue_block(q * MI + i, dst, k3, rsA3, rsB3);
           }
         }
       }
@@ -814,8 +827,13 @@ struct AsyncGemmKK {
     return make_rsrc(base + (int64_t)k0 * ld, bytes);
   }
 
-  __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,
-                                      int ka_valid, int na_valid, const uint16_t* B, int64_t ldb,
+    // PAD: every step issues one stage, past the last one through empty
+  // resources (no memory touched, zeros into a slot no later step reads),
+  // so no branch sits between the MFMAs and each wait is the constant
+  // NST - 2 stages behind. The empty stages cost their latency once at the
+  // end; with only 1-2 steps that outweighs the branches saved.
+  template <bool PAD = false>
+  __device__ __forceinline__ void run(unsigned char* lds, const uint16_t* A, int64_t lda,                                     int ka_valid, int na_valid, const uint16_t* B, int64_t ldb,
                                       int kb_valid, int nb_valid, int k_begin, int k_end) {
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -888,12 +906,16 @@ struct AsyncGemmKK {
         wait_vmcnt<0>();
     };
 
-    for (int s = 0; s < NST - 1 && s < nsteps; ++s) issue(s);
+    for (int s = 0; s < NST - 1 && (PAD || s < nsteps); ++s) issue(s);
     for (int s = 0; s < nsteps; ++s) {
-      wait_stage(s, s + NST - 2);
+      if constexpr (PAD)
+        wait_vmcnt<(NST - 2) * NB>();
+      else
+        wait_stage(s, s + NST - 2);
       barrier_only();
       // refill the slot of stage s-1 (every wave is past its reads) with
-      // stage s+NST-1, one DMA block per MFMA row block
+      // stage s+NST-1, one DMA block per MFMA row block (past the end the
+      // stage's resources are empty: stage_rsrc clamps the rows to none)
       const bool refill = s + NST - 1 < nsteps;
       const int kr = k_begin + 32 * (s + NST - 1);
       const i32x4 ra = stage_rsrc(A, lda, kr, ka_valid, na_valid);
@@ -920,7 +942,7 @@ struct AsyncGemmKK {
         } else {
           __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);
         }
-        if (i < NB && refill) issue_block(i, dst, ra, rb);
+        if (i < NB && (PAD || refill)) issue_block(i, dst, ra, rb);
       }
     }
     wait_vmcnt<0>();

@@ -835,6 +835,7 @@ DwMap dw_map(int n_vtiles, int n_htiles) {
 // of the buffer (padded columns u0 + vt 256 ..), dW rows from the call-local
 // vocabulary row of its first column; lds holds DwGemm::LDS_BYTES.
 using DwGemm = AsyncGemmKK<256, kDwBN, 2, 2, 3>;
+template <bool PAD>
 __device__ __forceinline__ void dw_tile(unsigned char* lds, const uint16_t* __restrict__ gtv,
                                         int64_t ldg, const uint16_t* __restrict__ hidden, int T,
                                         int Tp, int H, int u0, int Vs, int Vs_pad, int vt, int ht,
@@ -843,7 +844,7 @@ __device__ __forceinline__ void dw_tile(unsigned char* lds, const uint16_t* __re
   const int v0 = vt * 256, h0 = ht * kDwBN;
   Gm gm;
   gm.zero();
-  gm.run(lds, gtv + v0, ldg, T, 256, hidden + h0, H, T, min(kDwBN, H - h0), 0, Tp);
+  gm.template run<PAD>(lds, gtv + v0, ldg, T, 256, hidden + h0, H, T, min(kDwBN, H - h0), 0, Tp);
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave % 2, wn = wave / 2;
@@ -896,6 +897,8 @@ __device__ __forceinline__ void dw_tile_of(const DwMap& map, int xcd, int seq, i
   vt = (xcd / map.groups) * map.v_per_xcd + seq / map.h_per_group;
 }
 
+// PAD: the mainloop's padded refills, for K of 3 steps or more
+template <bool PAD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ hidden,
               int T, int Tp, int H, int u0, int Vs, int Vs_pad, int n_vtiles, int n_htiles,
@@ -906,7 +909,7 @@ bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __r
   int vt, ht;
   dw_tile_of(map, blockIdx.x & 7, seq, vt, ht);
   if (ht >= n_htiles || vt >= n_vtiles) return;
-  dw_tile(lds, gtv, ldg, hidden, T, Tp, H, u0, Vs, Vs_pad, vt, ht, dweight);
+  dw_tile<PAD>(lds, gtv, ldg, hidden, T, Tp, H, u0, Vs, Vs_pad, vt, ht, dweight);
 }
 
 // The splits of the backward, as the kernels see them: P virtual slices of Vs
@@ -1080,6 +1083,12 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
   template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                       \
       const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, SplitMap, \
       int, int, int, int, int, float* __restrict__);
+#define RLK_DW(PAD)                                                                            \
+  template __global__ void bwd_dw_kernel<PAD>(const uint16_t* __restrict__, int64_t,           \
+                                              const uint16_t* __restrict__, int, int, int, int, \
+                                              int, int, int, int, DwMap, float* __restrict__);
+RLK_DW(false)
+RLK_DW(true)
 RLK_FWD_TILE(256, 2, 2, false)
 RLK_FWD_TILE(256, 2, 2, true)
 RLK_RECOMPUTE(32, 128, 2, 2, false)
@@ -1220,8 +1229,12 @@ hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t st) {
     const int nsp = s1 - s0;
     if (a.dweight) {
       const DwMap map = dw_map(nvt, nhw);
-      RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel, 8 * map.per_xcd, st, a.gtv, p.ldg, a.hidden, T, Tp, H,
-                 u0, p.Vs, p.Vs_pad, nvt, nhw, map, a.dweight);
+      if (Tp > 64)
+        RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel<true>, 8 * map.per_xcd, st, a.gtv, p.ldg, a.hidden, T,
+                   Tp, H, u0, p.Vs, p.Vs_pad, nvt, nhw, map, a.dweight);
+      else
+        RLK_LAUNCH(K_BWD_DW, bwd_dw_kernel<false>, 8 * map.per_xcd, st, a.gtv, p.ldg, a.hidden, T,
+                   Tp, H, u0, p.Vs, p.Vs_pad, nvt, nhw, map, a.dweight);
     }
     if (a.dhidden) {
       if (small) {

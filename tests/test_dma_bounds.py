@@ -129,10 +129,14 @@ def bswz(k):
     return 2 * (k & 3) + 8 * ((k >> 3) & 1)
 
 
-def model_gemm_kn(BM, BN, lda, a_rows, ldb, kb_valid, nb_valid, k_begin, k_end, NST=4):
+def model_gemm_kn(BM, BN, lda, a_rows, ldb, kb_valid, nb_valid, k_begin, k_end, NST=4, MI=None):
     NW = 4
     NI_A, NI_B = BM * 64 // 1024, 32 * BN * 2 // 1024
     NI = NI_A + NI_B
+    # split issue (one block per MFMA row block) pads the ring: NST - 1 stages
+    # past the last one go out through empty resources (A's with no records,
+    # since its k offset is in the scalar offset; B's rows clamp to none)
+    split = NI_A % NW == 0 and NI % NW == 0 and (MI is None or NI // NW <= MI)
     PPR = BN // 8
     RPB = 64 // PPR
     ar = min(max(a_rows, 0), BM)
@@ -142,7 +146,7 @@ def model_gemm_kn(BM, BN, lda, a_rows, ldb, kb_valid, nb_valid, k_begin, k_end, 
     brow, bslot = LANES // PPR, LANES % PPR
     nsteps = (k_end - k_begin) // 32
     for wave in range(NW):
-        for s in range(nsteps):
+        for s in range(nsteps + (NST - 1 if split else 0)):
             k0 = k_begin + 32 * s
             brows = min(max(kb_valid - k0, 0), 32)
             bbytes = ((brows - 1) * ldb + nb_valid) * 2 if brows > 0 else 0
@@ -151,7 +155,8 @@ def model_gemm_kn(BM, BN, lda, a_rows, ldb, kb_valid, nb_valid, k_begin, k_end, 
                 if j >= NI:
                     continue
                 if j < NI_A:
-                    fa.issue((16 * j + drow) * lda * 2 + 16 * dpiece, k0 * 2, ar * lda * 2)
+                    fa.issue((16 * j + drow) * lda * 2 + 16 * dpiece, k0 * 2,
+                             ar * lda * 2 if s < nsteps else 0)
                 else:
                     k = RPB * (j - NI_A) + brow
                     fb.issue(k * ldb * 2 + 16 * (bslot ^ bswz(k)), 0, bbytes, base=k0 * ldb * 2)
@@ -169,14 +174,18 @@ def test_gemm_kn_reads_inside_operands(BM, BN, a_rows, kb_valid, H, h0):
     ldg = ((kb_valid + 31) // 32) * 32 + 64   # G rows: the split columns and some more
     k_end = (kb_valid + 31) // 32 * 32
     nb_valid = min(BN, H - h0)
-    fa, fb = model_gemm_kn(BM, BN, ldg, a_rows, H, kb_valid, nb_valid, 0, k_end)
+    # row blocks a wave's MFMA loop has per stage (16x16x32 blocks of WTM rows;
+    # dH runs 32x32x16 at 256 rows: 4 blocks x 2 steps)
+    mi = {(256, 256): 8, (32, 128): 1, (64, 128): 2}[(BM, BN)]
+    fa, fb = model_gemm_kn(BM, BN, ldg, a_rows, H, kb_valid, nb_valid, 0, k_end, MI=mi)
     check_k_contiguous(fa, min(a_rows, BM), ldg, 0, k_end, f"KN A {BM}x{BN}")
     check_k_major(fb, kb_valid, nb_valid, H, f"KN B {BM}x{BN}")
 
 
 # ---------------------------------------------------------- AsyncGemmKK --
 
-def model_gemm_kk(BM, BN, lda, ka_valid, na_valid, ldb, kb_valid, nb_valid, k_begin, k_end):
+def model_gemm_kk(BM, BN, lda, ka_valid, na_valid, ldb, kb_valid, nb_valid, k_begin, k_end,
+                  pad=False, NST=3):
     NW = 4
     PPR_A, PPR_B = BM // 8, BN // 8
     RPB_A, RPB_B = 64 // PPR_A, 64 // PPR_B
@@ -188,8 +197,10 @@ def model_gemm_kk(BM, BN, lda, ka_valid, na_valid, ldb, kb_valid, nb_valid, k_be
         rows = min(max(kv - k0, 0), 32)
         return ((rows - 1) * ld + nv) * 2 if rows > 0 else 0
 
+    nsteps = (k_end - k_begin) // 32
     for wave in range(NW):
-        for s in range((k_end - k_begin) // 32):
+        # padded: NST - 1 stages past the last, whose rows clamp to none
+        for s in range(nsteps + (NST - 1 if pad else 0)):
             k0 = k_begin + 32 * s
             for ii in range(NB):
                 j = wave + NW * ii
@@ -209,7 +220,7 @@ def test_gemm_kk_reads_inside_operands(T, H, h0):
     # dW: A = G [t][v] (256 columns of a ldg-wide row), B = hidden [t][h]
     ldg = 1024
     Tp = (T + 31) // 32 * 32
-    fa, fb = model_gemm_kk(256, 128, ldg, T, 256, H, T, min(128, H - h0), 0, Tp)
+    fa, fb = model_gemm_kk(256, 128, ldg, T, 256, H, T, min(128, H - h0), 0, Tp, pad=Tp > 64)
     check_k_major(fa, T, 256, ldg, "KK A (G)")
     check_k_major(fb, T, min(128, H - h0), H, "KK B (hidden)")
 
