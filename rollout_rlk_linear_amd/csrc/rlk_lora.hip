@@ -170,8 +170,9 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
   const int Ks = K / S;
   Gm gm;
   gm.zero();
-  gm.run(lds, x + (int64_t)row0 * K, K, T - row0, W + (int64_t)col0 * K, K, N - col0, ks * Ks,
-         (ks + 1) * Ks);
+  // the pair's k-steps unrolled (no branch per row block; same MFMA chain)
+  gm.template run<0, true>(lds, x + (int64_t)row0 * K, K, T - row0, W + (int64_t)col0 * K, K,
+                           N - col0, ks * Ks, (ks + 1) * Ks);
   if (S == 1) {
     // run() ends on a barrier: the ring is free. B's column n holds B[n][0..r-1].
     lora_epilogue<BN>(gm, lds, u, B, r, 1, T, N, r, scale, row0, col0, y, N);
