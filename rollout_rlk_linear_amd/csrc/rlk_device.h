@@ -671,18 +671,6 @@ struct AsyncGemmKN {
               (uint32_t)(STAGE_A + k * ROWB_B + 16 * ((col >> 3) ^ bswz(k)) + 2 * (col & 7));
         }
 
-    auto wait_stage = [&](int want, int last) {
-      const int after = last - want;
-      if (after >= 3)
-        wait_vmcnt<3 * NI_W_MIN>();
-      else if (after == 2)
-        wait_vmcnt<2 * NI_W_MIN>();
-      else if (after == 1)
-        wait_vmcnt<NI_W_MIN>();
-      else
-        wait_vmcnt<0>();
-    };
-    auto last_of = [&](int s) { return s < nsteps - 1 ? s : nsteps - 1; };
 
     // The DMA blocks of the stage being refilled go out one per MFMA row
     // block when they divide evenly (which operand each is: compile time).
@@ -707,20 +695,18 @@ struct AsyncGemmKN {
     };
 
     // a ring of NST single-k-step slots; A fragments read two row blocks ahead
-    // With split issue every step issues one stage, past the last through
-    // empty resources (no memory touched, zeros into a slot no later step
-    // reads): no branch sits between the MFMAs, and the wait is the constant
-    // NST - 2 stages behind (the clamped count of wait_stage takes a branch
-    // per step).
-    for (int s = 0; s < NST - 1 && (SPLIT || s < nsteps); ++s) issue(s);
+    // Every step issues one stage, past the last through empty resources
+    // (no memory touched, zeros into a slot no later step reads): no branch
+    // sits between the MFMAs, and the wait is the constant NST - 2 stages
+    // behind (a count clamped at the end takes a branch per step). Where
+    // waves issue unequal block counts the wait counts the smaller, which
+    // waits a little longer in the others.
+    for (int s = 0; s < NST - 1; ++s) issue(s);
     for (int s = 0; s < nsteps; ++s) {
-      if constexpr (SPLIT)
-        wait_vmcnt<(NST - 2) * (NI / NW)>();
-      else
-        wait_stage(s, last_of(s + NST - 2));
+      wait_vmcnt<(NST - 2) * NI_W_MIN>();
       barrier_only();
       const bool refill = s + NST - 1 < nsteps;
-      if (!SPLIT && refill) issue(s + NST - 1);
+      if (!SPLIT) issue(s + NST - 1);
       const int k3 = k_begin + 32 * (s + NST - 1);
       const uint32_t dst =
           lds0 + (uint32_t)(((s + NST - 1) % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave;

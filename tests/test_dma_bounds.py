@@ -129,14 +129,13 @@ def bswz(k):
     return 2 * (k & 3) + 8 * ((k >> 3) & 1)
 
 
-def model_gemm_kn(BM, BN, lda, a_rows, ldb, kb_valid, nb_valid, k_begin, k_end, NST=4, MI=None):
+def model_gemm_kn(BM, BN, lda, a_rows, ldb, kb_valid, nb_valid, k_begin, k_end, NST=4):
     NW = 4
     NI_A, NI_B = BM * 64 // 1024, 32 * BN * 2 // 1024
     NI = NI_A + NI_B
-    # split issue (one block per MFMA row block) pads the ring: NST - 1 stages
-    # past the last one go out through empty resources (A's with no records,
-    # since its k offset is in the scalar offset; B's rows clamp to none)
-    split = NI_A % NW == 0 and NI % NW == 0 and (MI is None or NI // NW <= MI)
+    # the ring is padded: NST - 1 stages past the last one go out through
+    # empty resources (A's with no records, since its k offset is in the
+    # scalar offset; B's rows clamp to none)
     PPR = BN // 8
     RPB = 64 // PPR
     ar = min(max(a_rows, 0), BM)
@@ -146,7 +145,7 @@ def model_gemm_kn(BM, BN, lda, a_rows, ldb, kb_valid, nb_valid, k_begin, k_end, 
     brow, bslot = LANES // PPR, LANES % PPR
     nsteps = (k_end - k_begin) // 32
     for wave in range(NW):
-        for s in range(nsteps + (NST - 1 if split else 0)):
+        for s in range(nsteps + NST - 1):
             k0 = k_begin + 32 * s
             brows = min(max(kb_valid - k0, 0), 32)
             bbytes = ((brows - 1) * ldb + nb_valid) * 2 if brows > 0 else 0
@@ -174,10 +173,7 @@ def test_gemm_kn_reads_inside_operands(BM, BN, a_rows, kb_valid, H, h0):
     ldg = ((kb_valid + 31) // 32) * 32 + 64   # G rows: the split columns and some more
     k_end = (kb_valid + 31) // 32 * 32
     nb_valid = min(BN, H - h0)
-    # row blocks a wave's MFMA loop has per stage (16x16x32 blocks of WTM rows;
-    # dH runs 32x32x16 at 256 rows: 4 blocks x 2 steps)
-    mi = {(256, 256): 8, (32, 128): 1, (64, 128): 2}[(BM, BN)]
-    fa, fb = model_gemm_kn(BM, BN, ldg, a_rows, H, kb_valid, nb_valid, 0, k_end, MI=mi)
+    fa, fb = model_gemm_kn(BM, BN, ldg, a_rows, H, kb_valid, nb_valid, 0, k_end)
     check_k_contiguous(fa, min(a_rows, BM), ldg, 0, k_end, f"KN A {BM}x{BN}")
     check_k_major(fb, kb_valid, nb_valid, H, f"KN B {BM}x{BN}")
 
