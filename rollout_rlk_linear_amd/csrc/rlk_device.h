@@ -906,8 +906,13 @@ struct AsyncGemmKK {
       const int kr = k_begin + 32 * (s + NST - 1);
       const i32x4 ra = stage_rsrc(A, lda, kr, ka_valid, na_valid);
       const i32x4 rb = stage_rsrc(B, ldb, kr, kb_valid, nb_valid);
-      const uint32_t dst = stage_dst(s + NST - 1);
-      const unsigned char* st = lds + (s % NST) * STAGE_BYTES;
+      // the slot once per step (the fragment addresses and the refill's
+      // destination derive from it; computed apart, the compiler spent two
+      // VALU operations on each of the step's 24 fragment addresses)
+      const int slot = s % NST;
+      const uint32_t dst =
+          lds0 + (uint32_t)(((slot + NST - 1) % NST) * STAGE_BYTES) + 1024u * (uint32_t)wave;
+      const unsigned char* st = lds + slot * STAGE_BYTES;
       constexpr int A0 = MI < 2 ? MI : 2;
       bf16x8 af[MI], bfr[NJ];
 #pragma unroll
