@@ -106,10 +106,13 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
     int n_ttiles, int n_items, float4* __restrict__ part) {
   using Gm = AsyncGemmP<BM, GROUP, WM, WN, 2, WNT>;
   static_assert(WN == 2 && Gm::WTN == 128 && Gm::NJ == 8, "one 128-column chunk per wave");
-  static_assert(BM * 2 * 16 + BM * 4 <= Gm::SLOT_B, "chunk records and targets fit B's pair-1 slot");
+  static_assert(BM * 2 * 16 + BM * 4 + kThreads * 16 <= Gm::SLOT_B,
+                "chunk records, targets and the record sink fit B's pair-1 slot");
   __shared__ __attribute__((aligned(16))) unsigned char lds[Gm::LDS_BYTES];
   float4* rec = reinterpret_cast<float4*>(lds + 2 * Gm::SLOT_A + Gm::SLOT_B);  // [BM][2 chunks]
   int* ycol = reinterpret_cast<int*>(lds + 2 * Gm::SLOT_A + Gm::SLOT_B + BM * 2 * 16);  // [BM]
+  float4* sink = reinterpret_cast<float4*>(lds + 2 * Gm::SLOT_A + Gm::SLOT_B + BM * 2 * 16 +
+                                           BM * 4);  // [threads], written, never read
 
   const int stride = gridDim.x;  // a multiple of 8: items keep their XCD
   auto next_item = [&](int it) {
@@ -196,10 +199,13 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(
           float zl = neg_inf();
 #pragma unroll
           for (int j = 0; j < 8; ++j) zl = (j == jt) ? z[j] : zl;
-          zl = (yin && (yc[r] & 15) == (lane & 15)) ? zl : neg_inf();
-          const float zy = row16_max(zl);
-          // all 16 lanes hold the same record and store it to the same slot
-          rec[rl * 2 + wn] = make_float4(c.m, c.R, c.B, zy);
+          // m, R, B are the same in all 16 lanes; the lane that holds the
+          // target logit (lane 0 of the 16 when the target lies elsewhere)
+          // writes the record, the others a slot of their own nobody reads
+          // (the streaming path spreads z_y by a max tree: the same value)
+          const bool owner = (yin ? (yc[r] & 15) : 0) == (lane & 15);
+          float4* dst = owner ? &rec[rl * 2 + wn] : &sink[tid];
+          *dst = make_float4(c.m, c.R, c.B, yin ? zl : neg_inf());
         }
       }
     }
