@@ -20,7 +20,11 @@
  *
  * Numerics (fixed, whatever T and the row's position in the batch):
  *   - x W^T and dy W: bf16 MFMA chains over K (resp. N) ascending in steps of
- *     32 from zero, fp32 accumulation;
+ *     32 from zero, fp32 accumulation. A long contraction is cut into S
+ *     equal splits, S fixed by its length L alone (the largest of 4, 2 with
+ *     L >= 1280 S and L a multiple of 64 S, else 1): each split is such a
+ *     chain over its own range, and the split sums are added in ascending
+ *     split order (((p0 + p1) + p2) + p3) before the adapter term;
  *   - u[t][j] = sum_k x[t][k] A[j][k] and v[t][j] = sum_n dy[t][n] B[n][j] in
  *     fp32: lane l of a wave sums, with fused multiply-adds, the elements
  *     8 l + 512 m + e (m ascending, e = 0..7 ascending), then a 64-lane xor
