@@ -298,6 +298,27 @@ def test_lora_workspace_and_empty_forward(lib):
     assert lora_fwd(lib, T=0, x=NULL, y=NULL, ws=NULL, nws=0) == OK
 
 
+@pytest.mark.parametrize("L", [64, 1216, 1280, 2496, 2560, 2624, 2688, 5056, 5120, 5184, 5248,
+                               5376, 65536])
+def test_lora_split_count_follows_the_length(lib, L):
+    """The number of splits S of a contraction of length L is the largest of
+    4 and 2 with L >= 1280 S and L a multiple of 64 S, else 1, and nothing
+    else (not T, not the other dimension). S is read back from the size of
+    the partials in the workspace (S x T x N fp32 for the forward's
+    contraction over K, at N = 64 so that dx's over N is never split)."""
+    expect = next((s for s in (4, 2) if L >= 1280 * s and L % (64 * s) == 0), 1)
+    f = lib.rlk_lora_linear_workspace_bytes
+    for T in (1, 33, 257):
+        uv = (2 * T * 4 + 255) // 256 * 256           # u and v at r = 1
+        part = (expect * T * 64 * 4 + 255) // 256 * 256 if expect > 1 else 0
+        assert f(T, L, 64, 1) == uv + part, (L, T)
+    # the same rule for dx's contraction over N (K = 64 is never split)
+    T = 33
+    uv = (2 * T * 4 + 255) // 256 * 256
+    part = (expect * T * 64 * 4 + 255) // 256 * 256 if expect > 1 else 0
+    assert f(T, 64, L, 1) == uv + part
+
+
 def test_workspace_sizes(lib):
     f = lib.rlk_linear_logp_fwd_workspace_bytes
     assert f(0, 4096, 151936) == 0
