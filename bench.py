@@ -41,10 +41,11 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 PUBLISHED_SCLK_GHZ = 2.4   # the clock the published peak assumes (256 CUs x 2.4 GHz x 4096 flop)
 METRIC = "linear-logp fwd+bwd tokens/s and % bf16 MFMA peak at H4096 V151936 T512"
 CSRC = os.path.join(ROOT, "rollout_rlk_linear_amd", "csrc")
+from rollout_rlk_linear_amd._build import SOURCE_FLAGS  # noqa: E402  (per-source build flags)
 
 
 # the sources that decide the linear-logp kernels' code and launches
-HASHED_SOURCES = ("rlk_abi.cpp", "rlk_device.h", "rlk_internal.h", "rlk_kernels.hip")
+HASHED_SOURCES = ("rlk_abi.cpp", "rlk_device.h", "rlk_internal.h", "rlk_kernels.hip", "rlk_dh.hip")
 
 
 def kernel_source_hash() -> str:
@@ -53,6 +54,7 @@ def kernel_source_hash() -> str:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
+            h.update(repr(SOURCE_FLAGS.get(name, [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -37,6 +37,13 @@ struct DwMap {
 };
 DwMap dw_map(int n_vtiles, int n_htiles);
 
+// The splits of the backward, as the kernels see them: P virtual slices of Vs
+// rows, padded to Vs_pad columns, each cut into n_sub splits of split_w
+// columns from the slice's first row (the last one shorter).
+struct SplitMap {
+  int Vs, Vs_pad, n_sub, split_w;
+};
+
 // Forward reduction layout. With P > 1 the call covers P of the 4 virtual
 // slices (vocab_total / 4 rows each) of the vocabulary: groups of 256
 // columns restart at each slice's first row (Gs groups per slice, the last

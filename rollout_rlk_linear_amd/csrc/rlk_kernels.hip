@@ -918,81 +918,14 @@ bwd_dw_kernel(const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __r
   dw_tile<PAD>(lds, gtv, ldg, hidden, T, Tp, H, u0, Vs, Vs_pad, vt, ht, dweight);
 }
 
-// The splits of the backward, as the kernels see them: P virtual slices of Vs
-// rows, padded to Vs_pad columns, each cut into n_sub splits of split_w
-// columns from the slice's first row (the last one shorter).
-struct SplitMap {
-  int Vs, Vs_pad, n_sub, split_w;
-};
-
-// dH partial of split s (of the call): rows t of the T-tile, columns h of the
-// H-tile, v over the split's columns in ascending order, one MFMA chain from
-// the split's first column (its G columns start at u_begin(s) - u0 in the
-// chunk buffer; its W rows at the slice's first row plus its offset). The
-// span is rounded up to whole MFMA steps: the G columns past the split's end
-// there are its slice's zero padding (or the next split's columns, at
-// multiples of 256 no step overruns) and the W rows past it read as zero.
-// Work items (t-tile fastest, then h-tile, then split) are dealt to the 8
-// XCDs in contiguous runs, so one split's G rows and W rows are fetched into
-// one XCD's L2 and reused there.
-// The MFMA is v_mfma_f32_32x32x16_bf16 (one wave per SIMD issues it at the
-// full matrix-core rate); every dH path uses it, so the split partials have
-// the same bits whatever the tile.
-template <int BM, int BN, int WM, int WN, int NSTG>
-using DhGemm = AsyncGemmKN<BM, BN, WM, WN, NSTG, true>;
-
-template <int BM, int BN, int WM, int WN, int NSTG>
-__device__ __forceinline__ void dh_item(unsigned char* lds, const uint16_t* __restrict__ gtv,
-                                        int64_t ldg, const uint16_t* __restrict__ weight, int T,
-                                        int H, int u0, SplitMap sm, int tt, int ht, int s,
-                                        float* __restrict__ part) {
-  using Gm = DhGemm<BM, BN, WM, WN, NSTG>;
-  const int row0 = tt * BM, h0 = ht * BN;
-  const int q = s / sm.n_sub, j = s - q * sm.n_sub;
-  const int a_col = q * sm.Vs_pad + j * sm.split_w - u0;  // chunk buffer column
-  const int w_row = q * sm.Vs + j * sm.split_w;            // call-local W row
-  const int len = min(sm.split_w, sm.Vs - j * sm.split_w);
-  Gm gm;
-  gm.zero();
-  gm.run(lds, gtv + (int64_t)row0 * ldg + a_col, ldg, T - row0, weight + (int64_t)w_row * H + h0,
-         H, len, min(BN, H - h0), 0, (len + 31) & ~31);
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int wm = wave % WM, wn = wave / WM;
-  // a 32-column block is whole or absent (H is a multiple of 64): wave-uniform test
-  const int hb = h0 + wn * Gm::WTN;
-  float* const out = part + (int64_t)s * T * H + hb + (lane & 31);
-  // accumulator element e of block (i, j): row 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
-  // column 32 j + lane % 32 (each store: 32 lanes x 4 bytes of one row)
-#pragma unroll
-  for (int i = 0; i < Gm::MI; ++i) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = row0 + wm * Gm::WTM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (t >= T) continue;
-      float* rowp = out + (int64_t)t * H;
-#pragma unroll
-      for (int j = 0; j < Gm::NJ; ++j)
-        if (hb + 32 * j < H) rowp[32 * j] = gm.acc[i][j][e];
-    }
-  }
-}
-
+// dH partials of split s (the kernel is compiled in rlk_dh.hip, on its own
+// so that its translation unit can take a machine-scheduler strategy of its
+// own).
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kThreads) void bwd_dh_kernel(
-    const uint16_t* __restrict__ gtv, int64_t ldg, const uint16_t* __restrict__ weight, int T,
-    int H, int u0, SplitMap sm, int n_splits, int split_base, int n_ttiles, int n_htiles,
-    int per_xcd, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[DhGemm<BM, BN, WM, WN, 4>::LDS_BYTES];
-  const int seq = blockIdx.x >> 3;
-  if (seq >= per_xcd) return;
-  const int w = (blockIdx.x & 7) * per_xcd + seq;
-  if (w >= n_ttiles * n_htiles * n_splits) return;
-  const int tt = w % n_ttiles;
-  const int ht = (w / n_ttiles) % n_htiles;
-  const int si = w / (n_ttiles * n_htiles);
-  dh_item<BM, BN, WM, WN, 4>(lds, gtv, ldg, weight, T, H, u0, sm, tt, ht, split_base + si, part);
-}
+__global__ void bwd_dh_kernel(const uint16_t* __restrict__ gtv, int64_t ldg,
+                              const uint16_t* __restrict__ weight, int T, int H, int u0,
+                              SplitMap sm, int n_splits, int split_base, int n_ttiles,
+                              int n_htiles, int per_xcd, float* __restrict__ part);
 
 __device__ __forceinline__ float4 add4(const float4& a, const float4& b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
@@ -1085,10 +1018,6 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
       const uint16_t* __restrict__, const uint16_t* __restrict__, int, int, int, int, int, int, \
       int, int, const float4* __restrict__, const float* __restrict__, const float* __restrict__, \
       const int32_t* __restrict__, int64_t, uint16_t* __restrict__, int64_t);
-#define RLK_DH(BM, BN, WM, WN)                                                                \
-  template __global__ void bwd_dh_kernel<BM, BN, WM, WN>(                                       \
-      const uint16_t* __restrict__, int64_t, const uint16_t* __restrict__, int, int, int, SplitMap, \
-      int, int, int, int, int, float* __restrict__);
 #define RLK_DW(PAD)                                                                            \
   template __global__ void bwd_dw_kernel<PAD>(const uint16_t* __restrict__, int64_t,           \
                                               const uint16_t* __restrict__, int, int, int, int, \
@@ -1100,8 +1029,6 @@ RLK_FWD_TILE(256, 2, 2, true)
 RLK_RECOMPUTE(32, 128, 2, 2, false)
 RLK_RECOMPUTE(256, 256, 2, 2, false)
 RLK_RECOMPUTE(256, 256, 2, 2, true)
-RLK_DH(32, 128, 1, 4)
-RLK_DH(256, 256, 2, 2)
 
 // ======================================================== launchers ======
 
