@@ -22,13 +22,16 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librlk_linear.so")
 ARCH = "gfx950"
 
-SOURCES = ["rlk_kernels.hip", "rlk_dh.hip", "rlk_microbench.hip", "rlk_lora.hip", "rlk_abi.cpp"]
-# Flags for one source only. The dH kernel's translation unit takes the
-# machine scheduler's iterative-ILP strategy: the same instructions, ordered
-# so that the kernel runs 1.0-1.6% faster; the forward's mainloop loses 3-6%
-# under it, so the rest keeps the default.
-SOURCE_FLAGS = {"rlk_dh.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
-HEADERS = ["rlk_device.h", "rlk_internal.h"]
+SOURCES = ["rlk_kernels.hip", "rlk_dh.hip", "rlk_microbench.hip", "rlk_lora.hip", "rlk_lora_fwd.hip",
+           "rlk_abi.cpp"]
+# Flags for one source only. The dH kernel's and the LoRA forward tile's
+# translation units take the machine scheduler's iterative-ILP strategy: the
+# same instructions, ordered so that dH runs 1-2% and the LoRA forward 3-7%
+# faster; the logits' mainloop loses 3-6% and the small LoRA backwards up to
+# 9% under it, so the rest keeps the default.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+SOURCE_FLAGS = {"rlk_dh.hip": _ILP, "rlk_lora_fwd.hip": _ILP}
+HEADERS = ["rlk_device.h", "rlk_internal.h", "rlk_lora_common.h"]
 
 
 def hipcc() -> str:
